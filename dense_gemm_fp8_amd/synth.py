@@ -1,0 +1,173 @@
+"""Seeded synthetic inputs for the tiled GEMM C = A·Bᵀ.
+
+This module is shared by the GPU tests, the bench and the oracle's tests.  It
+holds no GEMM arithmetic: it only draws seeded normal matrices and encodes them
+into the two input formats the path consumes.
+
+* bf16: float32 N(0, sigma^2) draws rounded to bfloat16 (round to nearest even).
+* fp8 (OCP e4m3): float32 N(0, 1) draws divided by a per-tensor scale
+  s = amax / 448 (448 is the largest finite e4m3 value) and rounded to the
+  nearest e4m3 code with ties to even; magnitudes above 448 saturate to +-448.
+
+The HipKittens pages (page 2, "Target operation" table) give the GEMM shapes and
+dtypes but no RNG, quantiser or rounding rule; the plainest readings are used
+here and listed in the design notes.
+
+Only numpy is imported, so loading this module never touches the GPU library.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+E4M3_MAX = 448.0
+
+
+def normal_f32(seed: int, rows: int, cols: int, sigma: float = 1.0) -> np.ndarray:
+    """rows x cols float32 draws from N(0, sigma^2), PCG64(seed), row-major."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = g.standard_normal(rows * cols, dtype=np.float32).reshape(rows, cols)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return x
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even.
+
+    Finite inputs only (the generators never produce NaN or Inf)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    u = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    return (u >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float32 -> OCP e4m3 codes (uint8), round to nearest even, saturating.
+
+    Layout S.EEEE.MMM with exponent bias 7; exponent field 0 is subnormal
+    (M/8 * 2^-6); S.1111.111 is NaN and never produced here."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    sign = (np.signbit(x)).astype(np.uint8) << np.uint8(7)
+    a_in = np.abs(x).astype(np.float32)
+    a = np.minimum(a_in, np.float32(E4M3_MAX))   # keeps the integer casts in range
+    # normal range [2^-6, 448): a = f * 2^E with f in [0.5, 1); unbiased exponent e = E - 1
+    f, E = np.frexp(a)
+    e = E.astype(np.int32) - 1
+    normal = a >= np.float32(2.0 ** -6)
+    # significand in [1, 2) scaled to 3 fraction bits; exact power-of-two scaling
+    mq = np.rint(np.ldexp(a, -e) * np.float32(8.0)).astype(np.int32) - 8  # 0..8
+    carry = mq == 8
+    e_n = np.where(carry, e + 1, e)
+    mq = np.where(carry, 0, mq)
+    code_n = ((e_n + 7) << 3) | mq
+    # subnormal range: multiples of 2^-9; a code of 8 is the smallest normal
+    code_s = np.rint(a * np.float32(2.0 ** 9)).astype(np.int32)
+    code = np.where(normal, code_n, code_s)
+    code = np.where(a_in >= np.float32(E4M3_MAX), 0x7E, code)
+    code = np.minimum(code, 0x7E)
+    return (code.astype(np.uint8) | sign)
+
+
+def e4m3_quantize(x: np.ndarray) -> tuple[np.ndarray, np.float32]:
+    """Per-tensor quantisation: s = amax/448 (s = 1 if amax == 0), codes = e4m3(x / s)."""
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
+    s = np.float32(amax / np.float32(E4M3_MAX)) if amax > 0 else np.float32(1.0)
+    q = e4m3_encode((x / s).astype(np.float32))
+    return q, s
+
+
+# --- workloads -------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One GEMM workload: C[M,N] = A[M,K] · B[N,K]ᵀ."""
+    name: str
+    dtype: str          # "bf16" or "fp8"
+    M: int
+    N: int
+    K: int
+    seed_a: int
+    seed_b: int
+    sigma_a: float = 1.0
+    sigma_b: float = 1.0
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def tol(self) -> float:
+        """Absolute fp32 tolerance 1e-3 * sqrt(K) on the pre-round result."""
+        return 1e-3 * float(np.sqrt(self.K))
+
+
+def workload(idx: int) -> Workload:
+    """The five seeded workloads (1-based index, seeds 1000*i + 1 / + 2)."""
+    table = {
+        1: ("bf16_256", "bf16", 256, 256, 256, 1.0, 1.0),
+        2: ("bf16_8192", "bf16", 8192, 8192, 8192, 1.0, 1.0),
+        3: ("bf16_mlp_16384x14336x4096", "bf16", 16384, 14336, 4096, 1.0, 0.02),
+        4: ("bf16_16384", "bf16", 16384, 16384, 16384, 1.0, 1.0),
+        5: ("fp8_e4m3_8192", "fp8", 8192, 8192, 8192, 1.0, 1.0),
+    }
+    name, dt, M, N, K, sa, sb = table[idx]
+    return Workload(name, dt, M, N, K, 1000 * idx + 1, 1000 * idx + 2, sa, sb)
+
+
+ALL_WORKLOADS = tuple(workload(i) for i in range(1, 6))
+
+
+def make_inputs(w: Workload):
+    """Host inputs for a workload.
+
+    bf16: (A_bits uint16 [M,K], B_bits uint16 [N,K], None, None)
+    fp8:  (A_codes uint8 [M,K], B_codes uint8 [N,K], scale_a, scale_b)"""
+    a = normal_f32(w.seed_a, w.M, w.K, w.sigma_a)
+    if w.dtype == "bf16":
+        A = f32_to_bf16_bits(a)
+        del a
+        B = f32_to_bf16_bits(normal_f32(w.seed_b, w.N, w.K, w.sigma_b))
+        return A, B, None, None
+    qa, sa = e4m3_quantize(a)
+    del a
+    qb, sb = e4m3_quantize(normal_f32(w.seed_b, w.N, w.K, w.sigma_b))
+    return qa, qb, sa, sb
+
+
+def small_int_bf16(seed: int, rows: int, cols: int, lo: int = -4, hi: int = 4) -> np.ndarray:
+    """Integer-valued bf16 bits with entries uniform in [lo, hi] (exact in bf16)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    v = g.integers(lo, hi + 1, size=(rows, cols)).astype(np.float32)
+    return f32_to_bf16_bits(v)
+
+
+def small_int_e4m3(seed: int, rows: int, cols: int, lo: int = -4, hi: int = 4) -> np.ndarray:
+    """Integer-valued e4m3 codes with entries uniform in [lo, hi] (exact in e4m3)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    v = g.integers(lo, hi + 1, size=(rows, cols)).astype(np.float32)
+    return e4m3_encode(v)
+
+
+def sample_pairs(seed: int, M: int, N: int, count: int, tile: int = 256) -> tuple[np.ndarray, np.ndarray]:
+    """Sampled output coordinates (m, n) that touch every output tile.
+
+    One row per tile row and one column per tile column are always included
+    (offset inside the tile varies per tile), then `count` further uniform pairs."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    gm, gn = -(-M // tile), -(-N // tile)
+    ms, ns = [], []
+    for tm in range(gm):
+        for tn in range(gn):
+            ms.append(min(M - 1, tm * tile + int(g.integers(0, tile))))
+            ns.append(min(N - 1, tn * tile + int(g.integers(0, tile))))
+    ms = np.array(ms, dtype=np.int64)
+    ns = np.array(ns, dtype=np.int64)
+    extra_m = g.integers(0, M, size=count, dtype=np.int64)
+    extra_n = g.integers(0, N, size=count, dtype=np.int64)
+    return np.concatenate([ms, extra_m]), np.concatenate([ns, extra_n])
