@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the tiled GEMM C = A·Bᵀ on one MI355X.
+
+One step = one GEMM launch over resident device inputs (the whole hot path:
+remap, HBM->LDS loads, ping-pong MFMA loop, epilogue).  Default workload: bf16
+M = N = K = 8192 with seeded N(0,1) inputs.  Prints one JSON line with the
+throughput (TFLOPS), the MFMA roofline of the kernel (live HIP-event timing),
+and the CPU oracle timed on a bounded sample as a baseline.
+
+  python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload 2]
+                  [--all] [--remap W,C | --row-major] [--schedule pingpong|lockstep]
+                  [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from dense_gemm_fp8_amd import synth  # noqa: E402
+
+METRIC = "GEMM TFLOPS at 8192³ bf16 (fraction of 2.5 PF peak); L2/LLC hit %"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}     # MI355X dense MFMA peaks
+# HipKittens 8-wave 0P/8C bf16 GEMM at 8192^3 on MI355X (page 2, Table 2 / Q3)
+PAGES_BF16_8192_TFLOPS = 1610.0
+KERNEL_SOURCES = ("dense_gemm_fp8_amd/csrc/gemm_kernels.hip", "dense_gemm_fp8_amd/csrc/remap.h",
+                  "dense_gemm_fp8_amd/csrc/kernels.h", "dense_gemm_fp8_amd/csrc/hkg_api.cpp")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w: synth.Workload) -> int:
+    """Bytes the GEMM must move at minimum: read A and B once, write C (bf16) once."""
+    e = 2 if w.dtype == "bf16" else 1
+    return e * (w.M * w.K + w.N * w.K) + 2 * w.M * w.N
+
+
+def kernel_name(dtype: str, schedule: str) -> str:
+    return "gemm_kernel<%s,%s>" % (dtype, schedule)
+
+
+def load_profile_facts(workload: str) -> dict:
+    """Counter-derived facts (HBM traffic, L2 hit rate) committed under
+    profiles/, valid only for the kernel source they were measured on."""
+    path = os.path.join(ROOT, "profiles", "counters_%s.json" % workload)
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        facts = json.load(f)
+    if facts.get("kernel_source_hash") != kernel_source_hash():
+        return {}
+    return facts
+
+
+def cpu_baseline(w: synth.Workload, A, B, sa, sb, target_s: float = 12.0) -> dict:
+    """The oracle as it stands, timed on this host on a sample of whole output rows."""
+    import oracle
+    threads = oracle.default_threads()
+    flops_per_row = 2.0 * w.N * w.K
+
+    def run(rows):
+        pm = np.repeat(np.arange(rows, dtype=np.int64) * max(1, w.M // rows), w.N)
+        pn = np.tile(np.arange(w.N, dtype=np.int64), rows)
+        t0 = time.perf_counter()
+        if w.dtype == "bf16":
+            oracle.gemm_bf16_pairs(A, B, pm, pn, threads=threads)
+        else:
+            oracle.gemm_fp8_pairs(A, B, sa, sb, pm, pn, threads=threads)
+        return time.perf_counter() - t0
+
+    probe_rows = max(1, threads // 2)
+    dt = run(probe_rows)
+    rate = probe_rows * flops_per_row / dt
+    rows = int(min(w.M, max(probe_rows, round(target_s * rate / flops_per_row))))
+    dt = run(rows)
+    return {"value": rows * flops_per_row / dt / 1e12, "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d full output rows (x %d columns, K=%d) of %s, fp64, %.1f s wall"
+                      % (rows, w.N, w.K, w.name, dt)}
+
+
+def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
+              with_cpu: bool) -> dict:
+    import torch
+    import dense_gemm_fp8_amd as hkg
+
+    dev = torch.device("cuda:0")
+    A, B, sa, sb = synth.make_inputs(w)
+    if w.dtype == "bf16":
+        dA = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).to(dev)
+        dB = torch.from_numpy(B.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        dA = torch.from_numpy(A).to(dev)
+        dB = torch.from_numpy(B).to(dev)
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        if w.dtype == "bf16":
+            hkg.gemm_bf16(dA, dB, C, opts=opts, stream=stream)
+        else:
+            hkg.gemm_fp8(dA, dB, sa, sb, C, opts=opts, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: every launch bracketed by HIP events on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    outer0 = torch.cuda.Event(enable_timing=True)
+    outer1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    outer0.record(stream)
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    outer1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = np.array([s.elapsed_time(e) for s, e in ev])
+    region_ms = outer0.elapsed_time(outer1)
+    ms_per_step = region_ms / steps
+    tflops = w.flops / (ms_per_step * 1e-3) / 1e12
+    kern_ms = float(per_launch_ms.mean())
+    achieved = w.flops / (kern_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+
+    facts = load_profile_facts(w.name)
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (round(tflops / PAGES_BF16_8192_TFLOPS, 4)
+                        if w.name == "bf16_8192" else None),
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+                   "inputs": "seeded N(0,1)%s" % ("" if w.dtype == "bf16" else
+                                                  " quantised to e4m3 with amax/448 scales"),
+                   "schedule": sched_name,
+                   "remap": ({"remap": opts.remap, "W": opts.W, "C": opts.C} if opts else "default")},
+        "fraction_of_peak": round(tflops / peak, 4),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": kernel_name(w.dtype, sched_name),
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": facts.get("hbm_bytes_per_launch"),
+            "algorithmic_flops_per_launch": w.flops,
+            "algorithmic_bytes_per_launch": algorithmic_bytes(w),
+            "kernel_ms_mean": round(kern_ms, 5),
+            "kernel_ms_min": round(float(per_launch_ms.min()), 5),
+            "kernel_ms_median": round(float(np.median(per_launch_ms)), 5),
+        },
+        "cache": {"l2_hit_pct": facts.get("l2_hit_pct"), "llc_hit_pct": facts.get("llc_hit_pct"),
+                  "source": facts.get("source")},
+        "wall_s_timed_region": round(wall, 4),
+        "kernel_source_hash": kernel_source_hash(),
+        "gpu": torch.cuda.get_device_name(dev),
+    }
+    del dA, dB, C
+    if with_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, A, B, sa, sb)
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--all", action="store_true", help="one line per workload 1..5")
+    ap.add_argument("--remap", type=str, default=None, help="W,C for the XCD remap")
+    ap.add_argument("--row-major", action="store_true")
+    ap.add_argument("--schedule", choices=["pingpong", "lockstep"], default="pingpong")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this GEMM path is single-GPU "
+              "(--gpus %d is not supported; run with --gpus 1)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import dense_gemm_fp8_amd as hkg
+    hkg.load()
+    sched = hkg.HKG_SCHED_PINGPONG if args.schedule == "pingpong" else hkg.HKG_SCHED_LOCKSTEP
+    opts = None
+    if args.row_major:
+        opts = hkg.make_opts(remap=hkg.HKG_REMAP_ROW_MAJOR, schedule=sched)
+    elif args.remap:
+        W, C = (int(v) for v in args.remap.split(","))
+        opts = hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=W, C=C, schedule=sched)
+    elif sched != hkg.HKG_SCHED_PINGPONG:
+        opts = hkg.make_opts(schedule=sched)
+
+    ids = [1, 2, 3, 4, 5] if args.all else [args.workload]
+    for i in ids:
+        w = synth.workload(i)
+        steps = args.steps
+        res = bench_one(w, steps, args.warmup, opts, args.schedule,
+                        with_cpu=(not args.no_cpu_baseline))
+        print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

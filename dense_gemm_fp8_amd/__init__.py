@@ -1,0 +1,227 @@
+"""dense_gemm_fp8_amd -- Python binding of libhkg, the MI355X (gfx950) tiled GEMM.
+
+    C[M,N] = A[M,K] · B[N,K]ᵀ     (bf16 or OCP e4m3 inputs, fp32 accumulate, bf16 out)
+
+The C ABI (include/hkg.h) is the product; this module only marshals
+arguments.  The functions with the C names (hkg_gemm_bf16, ...) take integers
+for device pointers and the stream, exactly like the C entry points.  The
+torch helpers (gemm_bf16, gemm_fp8, remap_tiles_device) take torch tensors that
+already live on the GPU; torch is used for device memory and streams only,
+every step of the GEMM runs in the library's own kernels.
+
+The shared library is built in-tree by dense_gemm_fp8_amd/build.py (or
+__graft_entry__.build()).  If it is missing, loading raises: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhkg.so")
+
+HKG_OK = 0
+HKG_ERR_NULL = -1
+HKG_ERR_SHAPE = -2
+HKG_ERR_ALIGN = -3
+HKG_ERR_SIZE = -4
+HKG_ERR_OPTS = -5
+HKG_ERR_DEVICE = -6
+HKG_ERR_LAUNCH = -7
+
+HKG_REMAP_DEFAULT = 0
+HKG_REMAP_ROW_MAJOR = 1
+HKG_REMAP_XCD = 2
+
+HKG_SCHED_DEFAULT = 0
+HKG_SCHED_PINGPONG = 1
+HKG_SCHED_LOCKSTEP = 2
+
+# exported symbols, in the order include/hkg.h declares them
+EXPORTS = (
+    "hkg_gemm_bf16",
+    "hkg_gemm_fp8",
+    "hkg_gemm_bf16_ex",
+    "hkg_gemm_fp8_ex",
+    "hkg_default_remap",
+    "hkg_remap_tile",
+    "hkg_remap_tiles_device",
+    "hkg_status_string",
+    "hkg_last_hip_error",
+)
+
+
+class hkg_gemm_opts(ctypes.Structure):
+    _fields_ = [("remap", ctypes.c_int32), ("W", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("schedule", ctypes.c_int32)]
+
+
+class HkgError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = "%s failed: %d (%s)" % (where, status, status_string(status))
+        if status == HKG_ERR_LAUNCH:
+            msg += ", hip error %d" % hkg_last_hip_error()
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libhkg.so from the package directory (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libhkg.so is not built (run python dense_gemm_fp8_amd/build.py "
+                           "or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, p, f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
+    popts = ctypes.POINTER(hkg_gemm_opts)
+    sig = {
+        "hkg_gemm_bf16": [i64, i64, i64, p, p, p, p, p],
+        "hkg_gemm_fp8": [i64, i64, i64, p, p, f32, f32, p, p, p],
+        "hkg_gemm_bf16_ex": [i64, i64, i64, p, p, p, p, p, popts],
+        "hkg_gemm_fp8_ex": [i64, i64, i64, p, p, f32, f32, p, p, p, popts],
+        "hkg_default_remap": [i64, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)],
+        "hkg_remap_tile": [i64, i64, i32, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)],
+        "hkg_remap_tiles_device": [i64, i64, i32, i32, p, p],
+        "hkg_status_string": [ctypes.c_int],
+        "hkg_last_hip_error": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "hkg_status_string" else ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# ---- the C entry points, same names and arguments ---------------------------------
+
+def hkg_gemm_bf16(M, N, K, A, B, C, C_f32, stream) -> int:
+    return load().hkg_gemm_bf16(M, N, K, A, B, C, C_f32, stream)
+
+
+def hkg_gemm_fp8(M, N, K, A, B, scale_a, scale_b, C, C_f32, stream) -> int:
+    return load().hkg_gemm_fp8(M, N, K, A, B, scale_a, scale_b, C, C_f32, stream)
+
+
+def hkg_gemm_bf16_ex(M, N, K, A, B, C, C_f32, stream, opts) -> int:
+    return load().hkg_gemm_bf16_ex(M, N, K, A, B, C, C_f32, stream,
+                                   ctypes.byref(opts) if opts is not None else None)
+
+
+def hkg_gemm_fp8_ex(M, N, K, A, B, scale_a, scale_b, C, C_f32, stream, opts) -> int:
+    return load().hkg_gemm_fp8_ex(M, N, K, A, B, scale_a, scale_b, C, C_f32, stream,
+                                  ctypes.byref(opts) if opts is not None else None)
+
+
+def hkg_default_remap(M, N, K, dtype):
+    """-> (status, W, C)."""
+    W, C = ctypes.c_int32(), ctypes.c_int32()
+    rc = load().hkg_default_remap(M, N, K, dtype, ctypes.byref(W), ctypes.byref(C))
+    return rc, W.value, C.value
+
+
+def hkg_remap_tile(Gm, Gn, W, C, b):
+    """-> (status, tile_m, tile_n)."""
+    tm, tn = ctypes.c_int64(), ctypes.c_int64()
+    rc = load().hkg_remap_tile(Gm, Gn, W, C, b, ctypes.byref(tm), ctypes.byref(tn))
+    return rc, tm.value, tn.value
+
+
+def hkg_remap_tiles_device(Gm, Gn, W, C, out, stream) -> int:
+    return load().hkg_remap_tiles_device(Gm, Gn, W, C, out, stream)
+
+
+def hkg_status_string(status: int) -> str:
+    return load().hkg_status_string(status).decode()
+
+
+def hkg_last_hip_error() -> int:
+    return load().hkg_last_hip_error()
+
+
+status_string = hkg_status_string
+
+
+# ---- torch marshalling helpers ------------------------------------------------------
+
+def make_opts(remap=HKG_REMAP_DEFAULT, W=0, C=0, schedule=HKG_SCHED_DEFAULT) -> hkg_gemm_opts:
+    return hkg_gemm_opts(remap, W, C, schedule)
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _dev_ptr(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def gemm_bf16(A, B, C=None, C_f32=None, opts=None, stream=None):
+    """C[M,N] (bf16) = A[M,K] · B[N,K]ᵀ for bf16 GPU tensors; returns C."""
+    import torch
+    if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
+        raise TypeError("A and B must be torch.bfloat16")
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("A is [M,K] and B is [N,K]")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if tuple(C.shape) != (M, N) or C.dtype != torch.bfloat16:
+        raise ValueError("C must be a [M,N] bfloat16 tensor")
+    if C_f32 is not None and (tuple(C_f32.shape) != (M, N) or C_f32.dtype != torch.float32):
+        raise ValueError("C_f32 must be a [M,N] float32 tensor")
+    rc = hkg_gemm_bf16_ex(M, N, K, _dev_ptr(A, "A"), _dev_ptr(B, "B"), _dev_ptr(C, "C"),
+                          _dev_ptr(C_f32, "C_f32"), _stream_handle(stream), opts)
+    if rc != HKG_OK:
+        raise HkgError(rc, "hkg_gemm_bf16_ex")
+    return C
+
+
+def gemm_fp8(A, B, scale_a, scale_b, C=None, C_f32=None, opts=None, stream=None):
+    """C[M,N] (bf16) = bf16(sa·sb · A[M,K] · B[N,K]ᵀ) for e4m3 code tensors
+    (torch.uint8 or torch.float8_e4m3fn) on the GPU; returns C."""
+    import torch
+    ok = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+    if A.dtype not in ok or B.dtype not in ok:
+        raise TypeError("A and B must hold e4m3 bytes (uint8 or float8_e4m3fn)")
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("A is [M,K] and B is [N,K]")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if tuple(C.shape) != (M, N) or C.dtype != torch.bfloat16:
+        raise ValueError("C must be a [M,N] bfloat16 tensor")
+    if C_f32 is not None and (tuple(C_f32.shape) != (M, N) or C_f32.dtype != torch.float32):
+        raise ValueError("C_f32 must be a [M,N] float32 tensor")
+    rc = hkg_gemm_fp8_ex(M, N, K, _dev_ptr(A, "A"), _dev_ptr(B, "B"), float(scale_a),
+                         float(scale_b), _dev_ptr(C, "C"), _dev_ptr(C_f32, "C_f32"),
+                         _stream_handle(stream), opts)
+    if rc != HKG_OK:
+        raise HkgError(rc, "hkg_gemm_fp8_ex")
+    return C
+
+
+def remap_tiles_device(Gm, Gn, W, C, stream=None):
+    """Device-evaluated grid remap -> int32 GPU tensor [Gm*Gn, 2] of (tile_m, tile_n)."""
+    import torch
+    out = torch.empty((Gm * Gn, 2), dtype=torch.int32, device="cuda")
+    rc = hkg_remap_tiles_device(Gm, Gn, W, C, out.data_ptr(), _stream_handle(stream))
+    if rc != HKG_OK:
+        raise HkgError(rc, "hkg_remap_tiles_device")
+    return out

@@ -1,0 +1,426 @@
+// gemm_kernels.hip -- gfx950 (MI355X) kernels for C = A * B^T.
+//
+// One 512-thread workgroup (8 waves of 64 lanes) computes one 256 x 256 output
+// tile (HipKittens, page 2, section 3 "Launch config": BLOCK 256 x 256,
+// K_STEP 64, WARPS_M = 2, WARPS_N = 4, DOT_SLICE 32, MFMA 16x16x32).
+//
+// Data path of one K step:
+//   HBM/L2 --buffer_load_dwordx4 ... lds--> LDS stage --ds_read_b128--> VGPR
+//   fragments --v_mfma--> fp32 accumulators (page 2, section 2 Pillar 1:
+//   direct HBM->LDS loads that bypass the register file, with the XOR swizzle
+//   applied to the HBM address).
+//
+// LDS (128 KiB, two stages; page 2 section 4 "Pipeline depth": 2-deep LDS
+// double buffer):
+//   stage s (64 KiB) = A panel [256 rows][128 B] then B panel [256 rows][128 B]
+//   one 128-byte row = one K step of one operand row (64 bf16 or 128 e4m3)
+//   row r stores its eight 16-byte chunks permuted: chunk c lives in slot
+//   c ^ slot_xor(r).
+//
+// A buffer load with the LDS bit writes lane l's 16 bytes to LDS address
+// M0 + 16*l, so one instruction fills 8 consecutive rows (1 KiB).  The lane
+// therefore cannot choose where its bytes land; instead each lane fetches the
+// global chunk that belongs in its fixed slot: lane l -> row 8u + l/8,
+// slot l%8, global chunk (l%8) ^ slot_xor(row).  This is the "swizzle applied
+// to the HBM address" of page 2, section 2 / page 1.
+//
+// Waves and the output tile (WARPS_M = 2 x WARPS_N = 4):
+//   wave w: group g = w / 4 owns tile rows [128 g, 128 g + 128),
+//           wn = w % 4 owns tile columns [64 wn, 64 wn + 64)
+//   -> a 128 x 64 fp32 sub-tile = 8 x 4 MFMA blocks of 16 x 16 = 128 fp32
+//      accumulator registers per lane (page 2 section 4 "Tile / launch
+//      optimality": the register budget at 2 waves per SIMD).
+//
+// MFMA operand order: the B fragment is the instruction's first (row) operand
+// and the A fragment its second (column) operand, so each 16 x 16 result block
+// is C^T and a lane holds 4 consecutive output COLUMNS of one output row.  The
+// B rows fed to the four column blocks j are interleaved (block j, operand row
+// 4a + b -> tile column 8a + b + 4 (j & 1) + 32 (j >> 1)) so that blocks j = 0,1
+// give a lane 8 consecutive bf16 (one 16-byte store) and j = 2,3 another 8.
+//
+// Schedules (page 2, section 2 Pillar 2; section 9.1 and 9.2):
+//   kPingPong  8-wave ping-pong.  Group 0 (waves 0-3, one per SIMD) and group
+//              1 (waves 4-7) run one barrier apart: while one group issues its
+//              MFMA cluster at s_setprio 3 the other issues the next K steps'
+//              HBM->LDS loads.  A conditional barrier staggers group 1 at the
+//              start (the "if (warpId < 4) barrier" of the listing
+//              description); s_barrier is the only synchronisation.
+//   kLockstep  all 8 waves compute the same K step and share the loads
+//              (no ping-pong; kept as an ablation).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "remap.h"
+
+namespace hkg {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kTile = 256;                        // output tile edge
+constexpr int kRowBytes = 128;                    // one K step of one row
+constexpr int kPanelBytes = kTile * kRowBytes;    // 32 KiB
+constexpr int kStageBytes = 2 * kPanelBytes;      // A panel + B panel
+constexpr int kLdsBytes = 2 * kStageBytes;        // 2 stages = 128 KiB
+constexpr int kDmaBytes = 64 * 16;                // one wave-wide 16 B/lane load
+constexpr int kDmaRows = kDmaBytes / kRowBytes;   // = 8 rows per load
+
+// Slot permutation of LDS row r (uses bits 0..4 of r).  A 16-lane group of a
+// ds_read_b128 reads one chunk from 16 rows; for conflict-free banking those
+// 16 reads must hit 16 different 16-byte slots of a 256-byte bank line
+// (64 banks x 4 B).  Two rows share a bank line (row bit 0), so for each
+// parity the 8 rows must get 8 different XOR values.  The A fragment reads
+// rows 16i + 0..15 (bits 1,2,3 vary), the interleaved B fragment reads rows
+// with bits 0,1,3,4 varying; (b1, b3, b2 ^ b4) is a bijection in both cases.
+__device__ __forceinline__ int slot_xor(int r)
+{
+    return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | ((((r >> 2) ^ (r >> 4)) & 1) << 2);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Workgroup barrier that is also a compiler barrier for memory accesses; it
+// deliberately does not wait for outstanding HBM->LDS loads (the schedules
+// wait for exactly the loads they need with wait_vmcnt).
+__device__ __forceinline__ void block_barrier()
+{
+    asm volatile("s_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    // dword3 0x00020000: raw (untyped) 32-bit buffer access on gfx9-family parts.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+
+// One wave-wide HBM->LDS load of 8 panel rows (u = row group, 0..31).
+__device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, char *panel, int u, int voff,
+                                         int soff_kstep, int ldk)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(panel + u * kDmaBytes), 16, voff,
+                                             soff_kstep + u * kDmaRows * ldk, 0, 0);
+}
+
+// Row groups u = base + (wave & 3) + 4 v, v < count: every lane of a wave
+// then shares the same row bits 3,4 ((u & 3) == (wave & 3)), so one per-lane
+// offset serves all its loads.
+template <int kCount>
+__device__ __forceinline__ void dma_panel_part(__amdgpu_buffer_rsrc_t rs, char *panel, int base,
+                                               int w4, int voff, int soff_kstep, int ldk)
+{
+#pragma unroll
+    for (int v = 0; v < kCount; ++v)
+        dma_rows(rs, panel, base + w4 + 4 * v, voff, soff_kstep, ldk);
+}
+
+template <int kDtype>
+struct Frag;
+template <>
+struct Frag<kBf16> {
+    using T = bf16x8;
+    static constexpr int kSlices = 2;   // DOT_SLICE 32 twice per K step of 64
+    __device__ __forceinline__ static T load(const char *p, int off0, int off1, int s)
+    {
+        return *reinterpret_cast<const bf16x8 *>(p + (s ? off1 : off0));
+    }
+    __device__ __forceinline__ static f32x4 mma(const T &x, const T &y, const f32x4 &c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
+    }
+};
+template <>
+struct Frag<kFp8> {
+    using T = i32x8;
+    static constexpr int kSlices = 1;   // one 16x16x128 step per K step of 128
+    __device__ __forceinline__ static T load(const char *p, int off0, int off1, int)
+    {
+        const i32x4 lo = *reinterpret_cast<const i32x4 *>(p + off0);
+        const i32x4 hi = *reinterpret_cast<const i32x4 *>(p + off1);
+        return T{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    __device__ __forceinline__ static f32x4 mma(const T &x, const T &y, const f32x4 &c)
+    {
+        // format selectors 0/0 = OCP e4m3 for both operands; the zero scale
+        // operands select the unscaled instruction.
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, 0, 0, 0, 0);
+    }
+};
+
+// Per-lane LDS byte offsets of the fragment reads (relative to a 32-row
+// group).  [parity][h]: h selects chunk q (h = 0) or chunk 4 + q (h = 1),
+// i.e. the two DOT_SLICEs of bf16 or the two halves of an e4m3 fragment.
+struct LaneOffsets {
+    int a[2][2];
+    int b[2][2];
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(int lane)
+{
+    const int x = lane & 15;      // operand row inside a 16-row block
+    const int q = lane >> 4;      // k chunk group
+    LaneOffsets o;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int ra = 16 * p + x;
+        const int rb = (x & 3) + 4 * p + 8 * (x >> 2);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            o.a[p][h] = ra * kRowBytes + (((4 * h + q) ^ slot_xor(ra)) << 4);
+            o.b[p][h] = rb * kRowBytes + (((4 * h + q) ^ slot_xor(rb)) << 4);
+        }
+    }
+    return o;
+}
+
+// The MFMA cluster of one K step for one wave: 8 x 4 blocks of 16 x 16.
+template <int kDtype>
+__device__ __forceinline__ void compute_kstep(const char *stage, const LaneOffsets &o, int g,
+                                              int wn, f32x4 (&acc)[8][4])
+{
+    using F = Frag<kDtype>;
+    const char *a_base = stage + (128 * g) * kRowBytes;
+    const char *b_base = stage + kPanelBytes + (64 * wn) * kRowBytes;
+#pragma unroll
+    for (int s = 0; s < F::kSlices; ++s) {
+        typename F::T bf[4], af[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            bf[j] = F::load(b_base + 32 * (j >> 1) * kRowBytes, o.b[j & 1][0], o.b[j & 1][1], s);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            af[i] = F::load(a_base + 16 * (i & ~1) * kRowBytes, o.a[i & 1][0], o.a[i & 1][1], s);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = F::mma(bf[j], af[i], acc[i][j]);
+    }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};   // v_cvt_pk_bf16_f32: round to nearest even
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Write the wave's 128 x 64 sub-tile: per 16-row block i a lane owns output
+// row m = 16 i + (lane % 16) and columns 8 q .. 8 q + 7 and 32 + 8 q .. + 7.
+__device__ __forceinline__ void store_tile(const GemmParams &p, int tm, int tn, int g, int wn,
+                                           int lane, f32x4 (&acc)[8][4])
+{
+    const int q = lane >> 4;
+    const int64_t row0 = (int64_t)tm * kTile + 128 * g + (lane & 15);
+    const int64_t col0 = (int64_t)tn * kTile + 64 * wn + 8 * q;
+    const float sc = p.scale;
+    uint16_t *C = static_cast<uint16_t *>(p.C);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t m = row0 + 16 * i;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const f32x4 lo = acc[i][2 * h] * sc;
+            const f32x4 hi = acc[i][2 * h + 1] * sc;
+            const int64_t off = m * p.N + col0 + 32 * h;
+            u32x4 packed = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                            pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
+            *reinterpret_cast<u32x4 *>(C + off) = packed;
+            if (p.C_f32) {
+                *reinterpret_cast<f32x4 *>(p.C_f32 + off) = lo;
+                *reinterpret_cast<f32x4 *>(p.C_f32 + off + 4) = hi;
+            }
+        }
+    }
+}
+
+template <int kDtype, int kSched>
+__global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = wave >> 2;     // ping-pong group, also the 128-row half of the tile
+    const int wn = wave & 3;     // 64-column quarter of the tile
+    const int w4 = wave & 3;
+
+    int tm, tn;
+    remap_tile(blockIdx.x, p.Gm, p.Gn, p.W, p.Cc, tm, tn);
+
+    constexpr int kElem = kDtype == kBf16 ? 2 : 1;
+    const int ldk = p.K * kElem;                          // bytes per operand row
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(static_cast<const char *>(p.A) + (int64_t)tm * kTile * ldk, kTile * ldk);
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(static_cast<const char *>(p.B) + (int64_t)tn * kTile * ldk, kTile * ldk);
+
+    // This lane's source offset inside a row group: row 8u + lane/8, slot
+    // lane%8; row bits 3,4 equal (u & 3) == w4 for every load this wave issues.
+    const int r8 = lane >> 3;
+    const int voff = r8 * ldk + (((lane & 7) ^ slot_xor(r8 | (w4 << 3))) << 4);
+
+    const LaneOffsets lo = lane_offsets(lane);
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = p.nk;
+    char *const stage0 = smem;
+    char *const stage1 = smem + kStageBytes;
+
+    if (kSched == kLockstep) {
+        // Each wave loads its 16 of the 64 row groups of a K step.
+        if (nk > 0) {
+            dma_panel_part<4>(ra, stage0, 16 * g, w4, voff, 0, ldk);
+            dma_panel_part<4>(rb, stage0 + kPanelBytes, 16 * g, w4, voff, 0, ldk);
+        }
+        if (nk > 1) {
+            dma_panel_part<4>(ra, stage1, 16 * g, w4, voff, kRowBytes, ldk);
+            dma_panel_part<4>(rb, stage1 + kPanelBytes, 16 * g, w4, voff, kRowBytes, ldk);
+            wait_vmcnt<8>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        block_barrier();
+        for (int t = 0; t < nk; ++t) {
+            char *st = (t & 1) ? stage1 : stage0;
+            compute_kstep<kDtype>(st, lo, g, wn, acc);
+            wait_lgkmcnt0();
+            block_barrier();                       // every wave is done with stage t&1
+            if (t + 2 < nk) {
+                dma_panel_part<4>(ra, st, 16 * g, w4, voff, (t + 2) * kRowBytes, ldk);
+                dma_panel_part<4>(rb, st + kPanelBytes, 16 * g, w4, voff, (t + 2) * kRowBytes, ldk);
+                wait_vmcnt<8>();                   // K step t+1 has landed
+            } else {
+                wait_vmcnt<0>();
+            }
+            block_barrier();                       // K step t+1 visible to all waves
+        }
+    } else {
+        // ---- 8-wave ping-pong ------------------------------------------------
+        // Who loads what (K step k into stage k & 1):
+        //   group 0: A rows   0..127 ("A0")      -- only group 0 reads them
+        //   group 1: A rows 128..255 ("A1") and all B rows
+        // Phases alternate between the groups; a phase ends at a barrier.
+        //   group 0: compute(t) | memory(t) | compute(t+1) | ...
+        //   group 1:   memory(t-1) | compute(t) | memory(t) | ...
+        // memory(t) issues the loads of K step t+2 into stage t & 1, which both
+        // groups have finished reading, and waits for the group's K step t+1.
+        // B(t+1) is awaited by group 1 at the end of its compute(t), one phase
+        // before group 0 needs it.
+        if (nk > 0) {   // K step 0: both groups share every panel
+            dma_panel_part<4>(ra, stage0, 16 * g, w4, voff, 0, ldk);
+            dma_panel_part<4>(rb, stage0 + kPanelBytes, 16 * g, w4, voff, 0, ldk);
+        }
+        if (nk > 1) {   // K step 1 in the steady-state split
+            if (g == 0) {
+                dma_panel_part<4>(ra, stage1, 0, w4, voff, kRowBytes, ldk);
+                wait_vmcnt<4>();
+            } else {
+                dma_panel_part<8>(rb, stage1 + kPanelBytes, 0, w4, voff, kRowBytes, ldk);
+                dma_panel_part<4>(ra, stage1, 16, w4, voff, kRowBytes, ldk);
+                wait_vmcnt<12>();
+            }
+        } else {
+            wait_vmcnt<0>();
+        }
+        block_barrier();
+        if (g == 1 && nk > 0)
+            block_barrier();                       // stagger group 1 by one phase
+
+        for (int t = 0; t < nk; ++t) {
+            char *st = (t & 1) ? stage1 : stage0;
+            // compute phase
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(3);
+            compute_kstep<kDtype>(st, lo, g, wn, acc);
+            __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_lgkmcnt0();
+            const bool last = t == nk - 1;
+            if (g == 1) {
+                if (!last)
+                    wait_vmcnt<4>();               // B(t+1) landed; A1(t+1) may fly
+                else
+                    continue;                      // group 1 ends after its last compute
+            }
+            block_barrier();
+            // memory phase
+            if (t + 2 < nk) {
+                const int soff = (t + 2) * kRowBytes;
+                if (g == 0) {
+                    dma_panel_part<4>(ra, st, 0, w4, voff, soff, ldk);
+                    wait_vmcnt<4>();               // A0(t+1) landed
+                } else {
+                    dma_panel_part<8>(rb, st + kPanelBytes, 0, w4, voff, soff, ldk);
+                    dma_panel_part<4>(ra, st, 16, w4, voff, soff, ldk);
+                    wait_vmcnt<12>();              // A1(t+1) landed
+                }
+            } else {
+                wait_vmcnt<0>();
+            }
+            if (!last)
+                block_barrier();
+        }
+    }
+    store_tile(p, tm, tn, g, wn, lane, acc);
+}
+
+__global__ void remap_tiles_kernel(int Gm, int Gn, int W, int C, int32_t *out)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < Gm * Gn) {
+        int tm, tn;
+        remap_tile(b, Gm, Gn, W, C, tm, tn);
+        out[2 * b] = tm;
+        out[2 * b + 1] = tn;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(Dtype dt, Schedule s, const GemmParams &p, hipStream_t stream)
+{
+    const dim3 grid(p.Gm * p.Gn), block(512);
+    if (dt == kBf16) {
+        if (s == kPingPong)
+            hipLaunchKernelGGL((gemm_kernel<kBf16, kPingPong>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((gemm_kernel<kBf16, kLockstep>), grid, block, 0, stream, p);
+    } else {
+        if (s == kPingPong)
+            hipLaunchKernelGGL((gemm_kernel<kFp8, kPingPong>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((gemm_kernel<kFp8, kLockstep>), grid, block, 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_remap_tiles(int Gm, int Gn, int W, int C, int32_t *out, hipStream_t stream)
+{
+    const int G = Gm * Gn;
+    hipLaunchKernelGGL(remap_tiles_kernel, dim3((G + 255) / 256), dim3(256), 0, stream, Gm, Gn,
+                       W, C, out);
+    return hipGetLastError();
+}
+
+}  // namespace hkg

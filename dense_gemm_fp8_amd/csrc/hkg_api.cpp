@@ -1,0 +1,258 @@
+// hkg_api.cpp -- the C ABI of libhkg: argument validation, launch plan
+// (tile grid, K steps, grid-remap parameters) and kernel launch.
+//
+// Every check runs before the first HIP call, so a rejected call launches
+// nothing and leaves C untouched.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/hkg.h"
+#include "kernels.h"
+#include "remap.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kTile = 256;
+constexpr int64_t kKStepBf16 = 64;
+constexpr int64_t kKStepFp8 = 128;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// W beyond the grid height, and any chunk with 8*C > G (no full cycle: the
+// whole grid is handled by the tail rule), give the same order; clamping keeps
+// the kernel's 32-bit products W*Gn and 8*C in range.
+void clamp_remap(int64_t Gm, int64_t Gn, int64_t *W, int64_t *C)
+{
+    const int64_t G = Gm * Gn;
+    if (*W > Gm)
+        *W = Gm;
+    if (*C > G / hkg::kNumXcd + 1)
+        *C = G / hkg::kNumXcd + 1;
+    if (*W < 1)
+        *W = 1;
+    if (*C < 1)
+        *C = 1;
+}
+
+// (W, C) used when the caller does not choose one.  A chunk of 32 tiles
+// gives each XCD one group of 32 consecutive remapped ids per round of the
+// 256-CU machine, and a window of 8 tile rows turns it into an 8 x 4 patch
+// of output tiles (8 A panels + 4 B panels shared in that XCD's L2).
+void default_remap(int64_t Gm, int64_t Gn, int32_t *W, int32_t *C)
+{
+    int64_t w = 8, c = 32;
+    clamp_remap(Gm, Gn, &w, &c);
+    *W = static_cast<int32_t>(w);
+    *C = static_cast<int32_t>(c);
+}
+
+int validate(int64_t M, int64_t N, int64_t K, int64_t kstep, int64_t elem, const void *A,
+             const void *B, const void *C, const float *C_f32)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return HKG_ERR_SHAPE;
+    if (M % kTile || N % kTile || K % kstep)
+        return HKG_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return HKG_OK;
+    if (!C || (K > 0 && (!A || !B)))
+        return HKG_ERR_NULL;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (C_f32 && !aligned16(C_f32)))
+        return HKG_ERR_ALIGN;
+    // One 256-row operand panel is addressed through a buffer resource with a
+    // 32-bit byte range, and tile counts / element offsets use 32-bit ints.
+    if (kTile * K * elem >= (int64_t(1) << 31))
+        return HKG_ERR_SIZE;
+    if ((M / kTile) * (N / kTile) >= (int64_t(1) << 30) || M >= (int64_t(1) << 31) ||
+        N >= (int64_t(1) << 31))
+        return HKG_ERR_SIZE;
+    return HKG_OK;
+}
+
+int resolve_opts(const hkg_gemm_opts *opts, int64_t Gm, int64_t Gn, int32_t *W, int32_t *C,
+                 hkg::Schedule *sched)
+{
+    default_remap(Gm, Gn, W, C);
+    *sched = hkg::kPingPong;
+    if (!opts)
+        return HKG_OK;
+    switch (opts->schedule) {
+    case HKG_SCHED_DEFAULT:
+    case HKG_SCHED_PINGPONG:
+        *sched = hkg::kPingPong;
+        break;
+    case HKG_SCHED_LOCKSTEP:
+        *sched = hkg::kLockstep;
+        break;
+    default:
+        return HKG_ERR_OPTS;
+    }
+    switch (opts->remap) {
+    case HKG_REMAP_DEFAULT:
+        break;
+    case HKG_REMAP_ROW_MAJOR:
+        *W = 1;
+        *C = 1;
+        break;
+    case HKG_REMAP_XCD:
+        if (opts->W < 1 || opts->C < 1)
+            return HKG_ERR_OPTS;
+        {
+            int64_t w = opts->W, c = opts->C;
+            clamp_remap(Gm, Gn, &w, &c);
+            *W = static_cast<int32_t>(w);
+            *C = static_cast<int32_t>(c);
+        }
+        break;
+    default:
+        return HKG_ERR_OPTS;
+    }
+    return HKG_OK;
+}
+
+int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const void *B, float sa,
+         float sb, void *C, float *C_f32, void *stream, const hkg_gemm_opts *opts)
+{
+    const int64_t kstep = dt == hkg::kBf16 ? kKStepBf16 : kKStepFp8;
+    const int64_t elem = dt == hkg::kBf16 ? 2 : 1;
+    int rc = validate(M, N, K, kstep, elem, A, B, C, C_f32);
+    if (rc != HKG_OK)
+        return rc;
+    const int64_t Gm = M / kTile, Gn = N / kTile;
+    int32_t W = 1, Cc = 1;
+    hkg::Schedule sched = hkg::kPingPong;
+    if (Gm > 0 && Gn > 0) {
+        rc = resolve_opts(opts, Gm, Gn, &W, &Cc, &sched);
+        if (rc != HKG_OK)
+            return rc;
+    } else if (opts && (opts->remap < 0 || opts->remap > 2 || opts->schedule < 0 ||
+                        opts->schedule > 2)) {
+        return HKG_ERR_OPTS;
+    }
+    if (M == 0 || N == 0)
+        return HKG_OK;
+
+    hkg::GemmParams p;
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.C_f32 = C_f32;
+    p.M = static_cast<int>(M);
+    p.N = static_cast<int>(N);
+    p.K = static_cast<int>(K);
+    p.Gm = static_cast<int>(Gm);
+    p.Gn = static_cast<int>(Gn);
+    p.W = W;
+    p.Cc = Cc;
+    p.nk = static_cast<int>(K / kstep);
+    // The product of the two per-tensor scales, rounded once to fp32.
+    p.scale = dt == hkg::kBf16 ? 1.0f : static_cast<float>(static_cast<double>(sa) * sb);
+
+    hipError_t e = hkg::launch_gemm(dt, sched, p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        g_last_hip_error = static_cast<int>(e);
+        return HKG_ERR_LAUNCH;
+    }
+    return HKG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hkg_gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
+                  float *C_f32, void *stream)
+{
+    return gemm(hkg::kBf16, M, N, K, A, B, 1.0f, 1.0f, C, C_f32, stream, nullptr);
+}
+
+int hkg_gemm_fp8(int64_t M, int64_t N, int64_t K, const void *A, const void *B, float scale_a,
+                 float scale_b, void *C, float *C_f32, void *stream)
+{
+    return gemm(hkg::kFp8, M, N, K, A, B, scale_a, scale_b, C, C_f32, stream, nullptr);
+}
+
+int hkg_gemm_bf16_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
+                     float *C_f32, void *stream, const hkg_gemm_opts *opts)
+{
+    return gemm(hkg::kBf16, M, N, K, A, B, 1.0f, 1.0f, C, C_f32, stream, opts);
+}
+
+int hkg_gemm_fp8_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                    float scale_a, float scale_b, void *C, float *C_f32, void *stream,
+                    const hkg_gemm_opts *opts)
+{
+    return gemm(hkg::kFp8, M, N, K, A, B, scale_a, scale_b, C, C_f32, stream, opts);
+}
+
+int hkg_default_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *W, int32_t *C)
+{
+    if (!W || !C)
+        return HKG_ERR_NULL;
+    const int64_t kstep = dtype == 0 ? kKStepBf16 : kKStepFp8;
+    if ((dtype != 0 && dtype != 1) || M <= 0 || N <= 0 || K < 0 || M % kTile || N % kTile ||
+        K % kstep)
+        return HKG_ERR_SHAPE;
+    default_remap(M / kTile, N / kTile, W, C);
+    return HKG_OK;
+}
+
+int hkg_remap_tile(int64_t Gm, int64_t Gn, int32_t W, int32_t C, int64_t b, int64_t *tile_m,
+                   int64_t *tile_n)
+{
+    if (!tile_m || !tile_n)
+        return HKG_ERR_NULL;
+    if (Gm < 1 || Gn < 1 || W < 1 || C < 1 || Gm * Gn >= (int64_t(1) << 30) || b < 0 ||
+        b >= Gm * Gn)
+        return HKG_ERR_SHAPE;
+    int64_t w = W, c = C;
+    clamp_remap(Gm, Gn, &w, &c);
+    int tm = 0, tn = 0;
+    hkg::remap_tile(static_cast<int>(b), static_cast<int>(Gm), static_cast<int>(Gn),
+                    static_cast<int>(w), static_cast<int>(c), tm, tn);
+    *tile_m = tm;
+    *tile_n = tn;
+    return HKG_OK;
+}
+
+int hkg_remap_tiles_device(int64_t Gm, int64_t Gn, int32_t W, int32_t C, int32_t *out,
+                           void *stream)
+{
+    if (!out)
+        return HKG_ERR_NULL;
+    if (Gm < 1 || Gn < 1 || W < 1 || C < 1 || Gm * Gn >= (int64_t(1) << 30))
+        return HKG_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(out) & 3u) != 0)
+        return HKG_ERR_ALIGN;
+    int64_t w = W, c = C;
+    clamp_remap(Gm, Gn, &w, &c);
+    hipError_t e = hkg::launch_remap_tiles(static_cast<int>(Gm), static_cast<int>(Gn),
+                                           static_cast<int>(w), static_cast<int>(c), out,
+                                           static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        g_last_hip_error = static_cast<int>(e);
+        return HKG_ERR_LAUNCH;
+    }
+    return HKG_OK;
+}
+
+const char *hkg_status_string(int status)
+{
+    switch (status) {
+    case HKG_OK: return "ok";
+    case HKG_ERR_NULL: return "a required pointer is NULL";
+    case HKG_ERR_SHAPE: return "unsupported shape (M, N multiples of 256; K of the K step)";
+    case HKG_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case HKG_ERR_SIZE: return "operand panel exceeds the 32-bit buffer range";
+    case HKG_ERR_OPTS: return "invalid hkg_gemm_opts";
+    case HKG_ERR_DEVICE: return "device query failed";
+    case HKG_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int hkg_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

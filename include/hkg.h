@@ -1,0 +1,139 @@
+/*
+ * hkg.h -- C ABI of libhkg, a tiled dense GEMM for AMD MI355X (gfx950).
+ *
+ *     C[M][N] = A[M][K] * B[N][K]^T        fp32 accumulation
+ *
+ * The operation is the BF16 GEMM / FP8 GEMM of HipKittens (page 2, section 3
+ * "Target operation" table: BF16 inputs, FP32 accumulator, BF16 output), with
+ * B used transposed as in the mma_ABt calls of the GEMM listing descriptions
+ * (page 2, sections 7 and 9.2).  Both operands are row-major with K contiguous
+ * ("K-major"); C is row-major.  The fp8 variant takes OCP e4m3 bytes with one
+ * fp32 scale per tensor and writes bf16  C = bf16(scale_a * scale_b * A*B^T).
+ *
+ * Launch shape (page 2, section 3 "Launch config" and section 8 "Launch
+ * shape"): one 512-thread workgroup (8 waves) per 256 x 256 output tile, a
+ * flat grid of ceil(M/256) * ceil(N/256) workgroups, K consumed 64 (bf16) or
+ * 128 (e4m3) at a time.  Workgroup ids are remapped to tiles by the
+ * chiplet-aware schedule of page 2, section 2 (Pillar 3) / section 7
+ * (Algorithm 1), with window height W and per-XCD chunk C.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named A, B, C, C_f32 are DEVICE pointers allocated, owned and
+ *    freed by the caller; the library never allocates, frees, copies to the
+ *    host or synchronises.  Work is enqueued on `stream` (a hipStream_t;
+ *    NULL = the default stream) and completes asynchronously; buffers must
+ *    stay alive until the stream has passed the kernel.
+ *  - All arguments are validated before any HIP call.  On any error nothing
+ *    is launched and C is untouched.
+ *  - Return value: HKG_OK (0) or a negative hkg_status.
+ *  - The library holds no mutable state apart from a thread-local copy of the
+ *    last HIP error; it is safe to call from several host threads.
+ */
+#ifndef HKG_H
+#define HKG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HKG_OK = 0,
+    HKG_ERR_NULL = -1,    /* a required pointer is NULL                              */
+    HKG_ERR_SHAPE = -2,   /* M, N, K negative or not a multiple of the tile/K step   */
+    HKG_ERR_ALIGN = -3,   /* a pointer is not 16-byte aligned                        */
+    HKG_ERR_SIZE = -4,    /* a per-tile operand panel exceeds the 32-bit buffer range */
+    HKG_ERR_OPTS = -5,    /* invalid hkg_gemm_opts                                   */
+    HKG_ERR_DEVICE = -6,  /* the current device is not gfx950 or cannot be queried   */
+    HKG_ERR_LAUNCH = -7   /* the kernel launch failed; see hkg_last_hip_error()      */
+} hkg_status;
+
+/* Grid order (the remap of page 2, section 2 Pillar 3 / section 7 Algorithm 1). */
+enum {
+    HKG_REMAP_DEFAULT = 0,  /* library's per-shape choice of (W, C)                */
+    HKG_REMAP_ROW_MAJOR = 1,/* identity order (W = 1, C = 1)                       */
+    HKG_REMAP_XCD = 2       /* explicit window height W >= 1 and chunk C >= 1       */
+};
+
+/* In-CU schedule (page 2, section 2 Pillar 2 and section 9.2). */
+enum {
+    HKG_SCHED_DEFAULT = 0,  /* 8-wave ping-pong                                     */
+    HKG_SCHED_PINGPONG = 1, /* 8-wave ping-pong: 2 groups of 4 waves alternate the
+                               MFMA and HBM->LDS roles via s_setprio + barriers      */
+    HKG_SCHED_LOCKSTEP = 2  /* all 8 waves compute the same K step (ablation only)   */
+};
+
+typedef struct {
+    int32_t remap;     /* HKG_REMAP_*                                  */
+    int32_t W;         /* window height in tile rows (HKG_REMAP_XCD)   */
+    int32_t C;         /* consecutive tiles per XCD (HKG_REMAP_XCD)    */
+    int32_t schedule;  /* HKG_SCHED_*                                  */
+} hkg_gemm_opts;
+
+/*
+ * bf16 GEMM.
+ *   A      [M][K] bfloat16, row-major (K contiguous), device, 16-byte aligned
+ *   B      [N][K] bfloat16, row-major (K contiguous), device, 16-byte aligned
+ *   C      [M][N] bfloat16, row-major, device, 16-byte aligned; written
+ *          with round-to-nearest-even from the fp32 accumulator
+ *   C_f32  NULL, or [M][N] fp32 row-major: the pre-rounding accumulator
+ *          (validation launches only; costs extra stores)
+ * Shapes: M % 256 == 0, N % 256 == 0, K % 64 == 0 (K == 0 writes zeros;
+ * M == 0 or N == 0 is a no-op).  C must not overlap A or B.
+ */
+int hkg_gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                  void *C, float *C_f32, void *stream);
+
+/*
+ * fp8 (OCP e4m3) GEMM with per-tensor scales.
+ *   A [M][K], B [N][K]: e4m3 bytes (S.EEEE.MMM, bias 7, max 448), row-major
+ *   scale_a, scale_b: host fp32 per-tensor dequantisation scales
+ *   C [M][N] bfloat16 = RNE(fp32(scale_a*scale_b) * fp32 accumulator)
+ *   C_f32: NULL or the scaled fp32 value before rounding
+ * Shapes: M % 256 == 0, N % 256 == 0, K % 128 == 0.  Otherwise as above.
+ */
+int hkg_gemm_fp8(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                 float scale_a, float scale_b, void *C, float *C_f32, void *stream);
+
+/* As above with an explicit grid order / schedule (opts may be NULL = defaults). */
+int hkg_gemm_bf16_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                     void *C, float *C_f32, void *stream, const hkg_gemm_opts *opts);
+int hkg_gemm_fp8_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                    float scale_a, float scale_b, void *C, float *C_f32, void *stream,
+                    const hkg_gemm_opts *opts);
+
+/*
+ * The (W, C) the library uses for HKG_REMAP_DEFAULT on a shape (host only, no
+ * HIP call).  dtype: 0 = bf16, 1 = fp8.  Returns HKG_ERR_NULL/SHAPE on bad input.
+ */
+int hkg_default_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *W, int32_t *C);
+
+/*
+ * The grid remap itself (page 2, section 7 Algorithm 1 reading): flat
+ * workgroup id b of a Gm x Gn tile grid -> output tile (tile_m, tile_n) for
+ * window height W and chunk C.  Host function, no HIP call.  Returns
+ * HKG_ERR_SHAPE if b is outside [0, Gm*Gn) or W, C < 1.
+ */
+int hkg_remap_tile(int64_t Gm, int64_t Gn, int32_t W, int32_t C, int64_t b,
+                   int64_t *tile_m, int64_t *tile_n);
+
+/*
+ * The same remap evaluated by the device code the GEMM kernels use: writes
+ * out[2*b] = tile_m, out[2*b+1] = tile_n for every b in [0, Gm*Gn).
+ *   out: device int32 array of 2*Gm*Gn elements, caller-owned.
+ */
+int hkg_remap_tiles_device(int64_t Gm, int64_t Gn, int32_t W, int32_t C, int32_t *out,
+                           void *stream);
+
+/* Static description of a status code. */
+const char *hkg_status_string(int status);
+
+/* hipError_t behind the last HKG_ERR_LAUNCH / HKG_ERR_DEVICE on this thread. */
+int hkg_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HKG_H */

@@ -1,0 +1,104 @@
+"""The C ABI library on the CPU: it loads, exports every declared symbol, and
+its host-side logic (validation before any HIP call, the grid remap, the
+default remap choice) behaves as documented.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_fp8_amd as hkg
+from oracle import remap as oracle_remap
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "hkg.h")).read()
+    return sorted(set(re.findall(r"\b(hkg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = hkg.load()
+    names = _declared()
+    assert len(names) == 9
+    assert sorted(hkg.EXPORTS) == names
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings():
+    for s in range(0, -8, -1):
+        assert hkg.hkg_status_string(s) != "unknown status"
+    assert hkg.hkg_status_string(5) == "unknown status"
+
+
+FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation
+
+
+@pytest.mark.parametrize("M,N,K", [(-256, 256, 64), (255, 256, 64), (256, 257, 64), (256, 256, 63)])
+def test_bad_shapes_rejected(M, N, K):
+    assert hkg.hkg_gemm_bf16(M, N, K, FAKE, FAKE, FAKE, None, None) == hkg.HKG_ERR_SHAPE
+
+
+def test_fp8_needs_k_multiple_of_128():
+    assert hkg.hkg_gemm_fp8(256, 256, 64, FAKE, FAKE, 1.0, 1.0, FAKE, None, None) == hkg.HKG_ERR_SHAPE
+
+
+def test_null_and_alignment_rejected():
+    assert hkg.hkg_gemm_bf16(256, 256, 64, None, FAKE, FAKE, None, None) == hkg.HKG_ERR_NULL
+    assert hkg.hkg_gemm_bf16(256, 256, 64, FAKE, FAKE, None, None, None) == hkg.HKG_ERR_NULL
+    assert hkg.hkg_gemm_bf16(256, 256, 64, FAKE + 8, FAKE, FAKE, None, None) == hkg.HKG_ERR_ALIGN
+    assert hkg.hkg_gemm_bf16(256, 256, 64, FAKE, FAKE, FAKE, FAKE + 4, None) == hkg.HKG_ERR_ALIGN
+    assert hkg.hkg_gemm_fp8(256, 256, 128, FAKE, FAKE + 2, 1.0, 1.0, FAKE, None, None) == hkg.HKG_ERR_ALIGN
+
+
+def test_size_limit_rejected():
+    # one 256-row bf16 panel of K = 2^22 is 2 GiB: beyond the 32-bit buffer range
+    assert hkg.hkg_gemm_bf16(256, 256, 1 << 22, FAKE, FAKE, FAKE, None, None) == hkg.HKG_ERR_SIZE
+
+
+def test_bad_opts_rejected():
+    bad = [hkg.make_opts(remap=7), hkg.make_opts(schedule=9), hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=0, C=4),
+           hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=4, C=0)]
+    for o in bad:
+        assert hkg.hkg_gemm_bf16_ex(256, 256, 64, FAKE, FAKE, FAKE, None, None, o) == hkg.HKG_ERR_OPTS
+
+
+def test_empty_output_is_a_noop():
+    # M == 0 or N == 0: nothing to compute, nothing launched, pointers unused
+    assert hkg.hkg_gemm_bf16(0, 256, 64, None, None, None, None, None) == hkg.HKG_OK
+    assert hkg.hkg_gemm_fp8(256, 0, 128, None, None, 1.0, 1.0, None, None, None) == hkg.HKG_OK
+
+
+@pytest.mark.parametrize("Gm,Gn", [(1, 1), (3, 5), (32, 32), (64, 56), (36, 36), (57, 57)])
+def test_host_remap_matches_oracle(Gm, Gn):
+    for W, C in [(1, 1), (8, 32), (5, 25), (7, 216), (8, 64), (8, 542), (3, 7)]:
+        want = oracle_remap.remap_table(Gm, Gn, min(W, Gm), min(C, Gm * Gn // 8 + 1))
+        got = []
+        for b in range(Gm * Gn):
+            rc, tm, tn = hkg.hkg_remap_tile(Gm, Gn, W, C, b)
+            assert rc == hkg.HKG_OK
+            got.append((tm, tn))
+        assert got == want
+
+
+def test_remap_clamping_does_not_change_order():
+    # W beyond the grid height and chunks with 8*C > G give the same order
+    Gm, Gn = 6, 10
+    assert oracle_remap.remap_table(Gm, Gn, 6, 8) == oracle_remap.remap_table(Gm, Gn, 6, 1000)
+    assert oracle_remap.remap_table(Gm, Gn, 6, 8) == oracle_remap.remap_table(Gm, Gn, 99, 8)
+
+
+def test_remap_rejects_bad_arguments():
+    assert hkg.hkg_remap_tile(4, 4, 1, 1, 16)[0] == hkg.HKG_ERR_SHAPE
+    assert hkg.hkg_remap_tile(4, 4, 0, 1, 0)[0] == hkg.HKG_ERR_SHAPE
+    assert hkg.hkg_remap_tiles_device(4, 4, 1, 1, None, None) == hkg.HKG_ERR_NULL
+
+
+def test_default_remap():
+    rc, W, C = hkg.hkg_default_remap(8192, 8192, 8192, 0)
+    assert rc == hkg.HKG_OK and 1 <= W <= 32 and C >= 1
+    assert hkg.hkg_default_remap(8192, 8192, 8192, 2)[0] == hkg.HKG_ERR_SHAPE
+    rc, W, C = hkg.hkg_default_remap(256, 256, 256, 1)
+    assert rc == hkg.HKG_OK and (W, C) == (1, 1)

@@ -1,0 +1,280 @@
+"""GPU parity of libhkg against the oracle, through the C ABI (needs a gfx950 GPU).
+
+Exactness cases (small integers, all-ones, identity, zeros) are compared bit for
+bit; random N(0,1) cases use the (i)-(iii) acceptance of tests/_parity.py;
+full-size workloads are compared on sampled outputs that touch every tile.
+Every launch goes through dense_gemm_fp8_amd's marshalling of the C entry
+points; nothing here falls back to a host computation."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from dense_gemm_fp8_amd import synth
+
+from _parity import bf16_to_f64, check
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU machines too
+    pytest.skip("no GPU", allow_module_level=True)
+
+import dense_gemm_fp8_amd as hkg  # noqa: E402
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _dev_u8(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).cuda()
+
+
+def _host_bits(c):
+    return c.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_bf16(A, B, opts=None, want_f32=True):
+    M, K = A.shape
+    N = B.shape[0]
+    dA, dB = _dev_bf16(A), _dev_bf16(B)
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    Cf = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda") if want_f32 else None
+    hkg.gemm_bf16(dA, dB, C, Cf, opts=opts)
+    torch.cuda.synchronize()
+    return _host_bits(C), (Cf.cpu().numpy() if want_f32 else None)
+
+
+def run_fp8(A, B, sa, sb, opts=None, want_f32=True):
+    M, K = A.shape
+    N = B.shape[0]
+    dA, dB = _dev_u8(A), _dev_u8(B)
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    Cf = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda") if want_f32 else None
+    hkg.gemm_fp8(dA, dB, sa, sb, C, Cf, opts=opts)
+    torch.cuda.synchronize()
+    return _host_bits(C), (Cf.cpu().numpy() if want_f32 else None)
+
+
+SCHEDULES = [hkg.HKG_SCHED_PINGPONG, hkg.HKG_SCHED_LOCKSTEP]
+
+
+# ---------------------------------------------------------------- remap ------------
+
+@pytest.mark.parametrize("Gm,Gn,W,C", [(32, 32, 8, 32), (32, 32, 1, 1), (36, 36, 7, 216),
+                                       (36, 36, 5, 25), (57, 57, 8, 64), (57, 57, 8, 542),
+                                       (64, 56, 6, 32), (3, 5, 2, 3)])
+def test_device_remap_matches_oracle(Gm, Gn, W, C):
+    from oracle import remap
+    _say("remap Gm=%d Gn=%d W=%d C=%d" % (Gm, Gn, W, C))
+    got = hkg.remap_tiles_device(Gm, Gn, W, C).cpu().numpy()
+    want = np.array(remap.remap_table(Gm, Gn, min(W, Gm), min(C, Gm * Gn // 8 + 1)))
+    np.testing.assert_array_equal(got, want)
+
+
+# ---------------------------------------------------------------- exactness --------
+
+@pytest.mark.parametrize("sched", SCHEDULES)
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (256, 256, 128), (256, 512, 192),
+                                   (512, 768, 320), (768, 256, 1024)])
+def test_bf16_small_integers_bit_exact(M, N, K, sched):
+    _say("bf16 ints %dx%dx%d sched=%d" % (M, N, K, sched))
+    A = synth.small_int_bf16(9100 + M + K, M, K)
+    B = synth.small_int_bf16(9200 + N + K, N, K)
+    cb, cf = run_bf16(A, B, opts=hkg.make_opts(schedule=sched))
+    want = (bf16_to_f64(A).astype(np.int64) @ bf16_to_f64(B).astype(np.int64).T).astype(np.float64)
+    np.testing.assert_array_equal(cf.astype(np.float64), want)
+    np.testing.assert_array_equal(cb, oracle.bf16_round(want))
+
+
+@pytest.mark.parametrize("sched", SCHEDULES)
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (256, 512, 256), (512, 768, 384),
+                                   (768, 256, 1024)])
+def test_fp8_small_integers_bit_exact(M, N, K, sched):
+    _say("fp8 ints %dx%dx%d sched=%d" % (M, N, K, sched))
+    A = synth.small_int_e4m3(9300 + M + K, M, K)
+    B = synth.small_int_e4m3(9400 + N + K, N, K)
+    cb, cf = run_fp8(A, B, 1.0, 1.0, opts=hkg.make_opts(schedule=sched))
+    tab = oracle.e4m3_table()
+    want = (tab[A].astype(np.int64) @ tab[B].astype(np.int64).T).astype(np.float64)
+    np.testing.assert_array_equal(cf.astype(np.float64), want)
+    np.testing.assert_array_equal(cb, oracle.bf16_round(want))
+
+
+def test_fp8_extreme_codes_exact():
+    # every finite e4m3 magnitude, both signs, against an all-ones partner: each
+    # output is a plain sum of decoded codes (exact in fp32 at these sizes)
+    _say("fp8 extreme codes")
+    M, N, K = 256, 256, 256
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    g = np.random.Generator(np.random.PCG64(9500))
+    A = codes[g.integers(0, codes.size, size=(M, K))]
+    B = np.full((N, K), 0x38, dtype=np.uint8)
+    cb, cf = run_fp8(A, B, 1.0, 1.0)
+    want = oracle.gemm_fp8(A, B, 1.0, 1.0)
+    np.testing.assert_array_equal(cf.astype(np.float64), want)
+
+
+@pytest.mark.parametrize("K", [64, 4096])
+def test_all_ones_gives_K(K):
+    _say("all ones K=%d" % K)
+    one = np.full((256, K), 0x3F80, dtype=np.uint16)
+    cb, cf = run_bf16(one, one[:256])
+    assert (cf == K).all()
+    np.testing.assert_array_equal(cb, oracle.bf16_round(np.full((256, 256), float(K))))
+    one8 = np.full((256, max(K, 128)), 0x38, dtype=np.uint8)
+    cb, cf = run_fp8(one8, one8, 1.0, 1.0)
+    assert (cf == max(K, 128)).all()
+
+
+def test_identity_operands_exact():
+    _say("identity")
+    K = 256
+    eye = synth.f32_to_bf16_bits(np.eye(K, dtype=np.float32))
+    B = synth.f32_to_bf16_bits(synth.normal_f32(9510, 512, K))
+    cb, cf = run_bf16(eye, B)                  # C = Bᵀ
+    np.testing.assert_array_equal(cf.astype(np.float64), bf16_to_f64(B).T)
+    np.testing.assert_array_equal(cb, B.T)
+    A = synth.f32_to_bf16_bits(synth.normal_f32(9511, 768, K))
+    cb, cf = run_bf16(A, eye)                  # C = A
+    np.testing.assert_array_equal(cb, A)
+
+
+def test_k_zero_writes_zeros():
+    _say("K=0")
+    M, N = 256, 512
+    C = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    Cf = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    rc = hkg.hkg_gemm_bf16(M, N, 0, None, None, C.data_ptr(), Cf.data_ptr(),
+                           torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == hkg.HKG_OK
+    assert (Cf == 0).all() and (C.float() == 0).all()
+
+
+# ---------------------------------------------------------------- random parity ----
+
+@pytest.mark.parametrize("sched", SCHEDULES)
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (512, 768, 448), (1024, 512, 1536)])
+def test_bf16_random_matches_oracle(M, N, K, sched):
+    _say("bf16 random %dx%dx%d sched=%d" % (M, N, K, sched))
+    A = synth.f32_to_bf16_bits(synth.normal_f32(9600 + K, M, K))
+    B = synth.f32_to_bf16_bits(synth.normal_f32(9700 + K, N, K))
+    cb, cf = run_bf16(A, B, opts=hkg.make_opts(schedule=sched))
+    ref = oracle.gemm_bf16(A, B)
+    check(ref, cf, cb, K, "bf16 %dx%dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("sched", SCHEDULES)
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (512, 768, 640), (1024, 512, 1536)])
+def test_fp8_random_matches_oracle(M, N, K, sched):
+    _say("fp8 random %dx%dx%d sched=%d" % (M, N, K, sched))
+    A, sa = synth.e4m3_quantize(synth.normal_f32(9800 + K, M, K))
+    B, sb = synth.e4m3_quantize(synth.normal_f32(9900 + K, N, K))
+    cb, cf = run_fp8(A, B, sa, sb, opts=hkg.make_opts(schedule=sched))
+    ref = oracle.gemm_fp8(A, B, sa, sb)
+    check(ref, cf, cb, K, "fp8 %dx%dx%d" % (M, N, K))
+
+
+def test_workload_256_full_parity():
+    w = synth.workload(1)
+    _say("workload %s" % w.name)
+    A, B, _, _ = synth.make_inputs(w)
+    cb, cf = run_bf16(A, B)
+    check(oracle.gemm_bf16(A, B), cf, cb, w.K, w.name)
+
+
+# ---------------------------------------------------------------- invariance -------
+
+def test_output_identical_across_grid_orders_and_schedules():
+    _say("invariance")
+    M, N, K = 2048, 1536, 1024
+    A = synth.f32_to_bf16_bits(synth.normal_f32(9960, M, K))
+    B = synth.f32_to_bf16_bits(synth.normal_f32(9961, N, K))
+    base, _ = run_bf16(A, B, want_f32=False)
+    variants = [hkg.make_opts(remap=hkg.HKG_REMAP_ROW_MAJOR),
+                hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=5, C=25),
+                hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=7, C=216),
+                hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=1, C=6),
+                hkg.make_opts(schedule=hkg.HKG_SCHED_LOCKSTEP)]
+    for o in variants:
+        got, _ = run_bf16(A, B, opts=o, want_f32=False)
+        np.testing.assert_array_equal(got, base)
+
+
+def test_repeated_launches_bit_identical_and_no_stray_writes():
+    _say("repeat + canary")
+    M, N, K = 1024, 1024, 512
+    A = _dev_bf16(synth.f32_to_bf16_bits(synth.normal_f32(9970, M, K)))
+    B = _dev_bf16(synth.f32_to_bf16_bits(synth.normal_f32(9971, N, K)))
+    pad = 4096
+    buf = torch.full((M * N + 2 * pad,), 12345, dtype=torch.int16, device="cuda")
+    C = buf[pad:pad + M * N].view(torch.bfloat16).view(M, N)
+    outs = []
+    for _ in range(10):
+        hkg.gemm_bf16(A, B, C)
+        torch.cuda.synchronize()
+        outs.append(C.view(torch.int16).clone())
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    assert (buf[:pad] == 12345).all() and (buf[pad + M * N:] == 12345).all()
+
+
+def test_rejected_call_leaves_output_untouched():
+    _say("rejected call")
+    C = torch.full((256, 256), 3.0, dtype=torch.bfloat16, device="cuda")
+    A = torch.zeros((256, 64), dtype=torch.bfloat16, device="cuda")
+    rc = hkg.hkg_gemm_bf16(256, 256, 64, A.data_ptr() + 2, A.data_ptr(), C.data_ptr(), None,
+                           torch.cuda.current_stream().cuda_stream)
+    assert rc == hkg.HKG_ERR_ALIGN
+    torch.cuda.synchronize()
+    assert (C.float() == 3.0).all()
+
+
+# ---------------------------------------------------------------- full sizes -------
+
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_full_size_workload_sampled_parity(idx):
+    """Every full-size workload, sampled outputs (one per tile + uniform extras),
+    in the launch configuration the bench times (default opts) and with the
+    fp32 copy; the two bf16 outputs must be identical."""
+    w = synth.workload(idx)
+    _say("full-size %s: inputs" % w.name)
+    A, B, sa, sb = synth.make_inputs(w)
+    if w.dtype == "bf16":
+        dA, dB = _dev_bf16(A), _dev_bf16(B)
+    else:
+        dA, dB = _dev_u8(A), _dev_u8(B)
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    C2 = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    Cf = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    _say("full-size %s: launch" % w.name)
+    if w.dtype == "bf16":
+        hkg.gemm_bf16(dA, dB, C)                 # bench configuration
+        hkg.gemm_bf16(dA, dB, C2, Cf)            # validation launch
+    else:
+        hkg.gemm_fp8(dA, dB, sa, sb, C)
+        hkg.gemm_fp8(dA, dB, sa, sb, C2, Cf)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), C2.view(torch.int16))
+    # (ii) on every entry, on the device: torch's float->bfloat16 cast is RNE
+    assert torch.equal(Cf.to(torch.bfloat16).view(torch.int16), C.view(torch.int16))
+    pm, pn = synth.sample_pairs(7000 + idx, w.M, w.N, 60000)
+    ipm, ipn = torch.from_numpy(pm).cuda(), torch.from_numpy(pn).cuda()
+    cf = Cf[ipm, ipn].cpu().numpy()
+    cb = C.view(torch.int16)[ipm, ipn].cpu().numpy().view(np.uint16)
+    del dA, dB, C, C2, Cf
+    _say("full-size %s: oracle on %d samples" % (w.name, pm.size))
+    if w.dtype == "bf16":
+        ref = oracle.gemm_bf16_pairs(A, B, pm, pn)
+    else:
+        ref = oracle.gemm_fp8_pairs(A, B, sa, sb, pm, pn)
+    info = check(ref, cf, cb, w.K, w.name)
+    _say("full-size %s: %s" % (w.name, info))
