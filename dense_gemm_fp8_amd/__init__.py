@@ -74,6 +74,14 @@ def load() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    # torch ships its own HIP runtime (same soname as ROCm's).  Loading torch
+    # first makes libhkg bind to that runtime, so kernels launch on the streams
+    # and device memory torch hands out; loading libhkg first would put two HIP
+    # runtimes in the process.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # plain C-ABI use without torch
+        pass
     if not os.path.exists(LIB_PATH):
         raise RuntimeError("libhkg.so is not built (run python dense_gemm_fp8_amd/build.py "
                            "or __graft_entry__.build()); there is no fallback path")
