@@ -10,12 +10,16 @@
 //   direct HBM->LDS loads that bypass the register file, with the XOR swizzle
 //   applied to the HBM address).
 //
-// LDS (128 KiB, two stages; page 2 section 4 "Pipeline depth": 2-deep LDS
-// double buffer):
-//   stage s (64 KiB) = A panel [256 rows][128 B] then B panel [256 rows][128 B]
+// LDS (the full 160 KiB of a gfx950 CU):
+//   A ring: 2 panels [256 rows][128 B] (K step k in panel k % 2)
+//   B ring: 3 panels [256 rows][128 B] (K step k in panel k % 3)
 //   one 128-byte row = one K step of one operand row (64 bf16 or 128 e4m3)
 //   row r stores its eight 16-byte chunks permuted: chunk c lives in slot
 //   c ^ slot_xor(r).
+// The pages keep a 2-deep LDS double buffer (page 2, section 4 "Pipeline
+// depth"); the third B panel here exists so that the ping-pong below can
+// prefetch register fragments one phase early while the shared B panel still
+// has three phases to arrive from HBM.
 //
 // A buffer load with the LDS bit writes lane l's 16 bytes to LDS address
 // M0 + 16*l, so one instruction fills 8 consecutive rows (1 KiB).  The lane
@@ -42,8 +46,11 @@
 //   kPingPong  8-wave ping-pong.  Group 0 (waves 0-3, one per SIMD) and group
 //              1 (waves 4-7) run one barrier apart: while one group issues its
 //              MFMA cluster at s_setprio 3 the other issues the next K steps'
-//              HBM->LDS loads.  A conditional barrier staggers group 1 at the
-//              start (the "if (warpId < 4) barrier" of the listing
+//              HBM->LDS loads and reads the first half of its own next
+//              cluster's fragments from LDS into registers, so a cluster
+//              starts with MFMAs instead of waiting for LDS.  Group 1 starts
+//              with a memory phase, which staggers it one phase behind group 0
+//              (the role of the "if (warpId < 4) barrier" of the listing
 //              description); s_barrier is the only synchronisation.
 //   kLockstep  all 8 waves compute the same K step and share the loads
 //              (no ping-pong; kept as an ablation).
@@ -67,8 +74,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int kTile = 256;                        // output tile edge
 constexpr int kRowBytes = 128;                    // one K step of one row
 constexpr int kPanelBytes = kTile * kRowBytes;    // 32 KiB
-constexpr int kStageBytes = 2 * kPanelBytes;      // A panel + B panel
-constexpr int kLdsBytes = 2 * kStageBytes;        // 2 stages = 128 KiB
+constexpr int kAPanels = 2;                       // A ring depth
+constexpr int kBPanels = 3;                       // B ring depth
+constexpr int kBRing = kAPanels * kPanelBytes;    // byte offset of the B ring
+constexpr int kLdsBytes = (kAPanels + kBPanels) * kPanelBytes;   // 160 KiB
 constexpr int kDmaBytes = 64 * 16;                // one wave-wide 16 B/lane load
 constexpr int kDmaRows = kDmaBytes / kRowBytes;   // = 8 rows per load
 
@@ -189,23 +198,35 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane)
     return o;
 }
 
-// The MFMA cluster of one K step for one wave: 8 x 4 blocks of 16 x 16.
+// Base addresses of a wave's fragments inside an A panel / B panel.
+__device__ __forceinline__ const char *a_frag_base(const char *a_panel, int g)
+{
+    return a_panel + (128 * g) * kRowBytes;
+}
+__device__ __forceinline__ const char *b_frag_base(const char *b_panel, int wn)
+{
+    return b_panel + (64 * wn) * kRowBytes;
+}
+// Offsets of fragment i of A (16-row block) and j of B (32-row half) from those bases.
+__device__ __forceinline__ constexpr int a_blk(int i) { return 16 * (i & ~1) * kRowBytes; }
+__device__ __forceinline__ constexpr int b_blk(int j) { return 32 * (j >> 1) * kRowBytes; }
+
+// The MFMA cluster of one K step for one wave, all fragments read inside the
+// cluster (used by the lockstep schedule): 8 x 4 blocks of 16 x 16.
 template <int kDtype>
-__device__ __forceinline__ void compute_kstep(const char *stage, const LaneOffsets &o, int g,
-                                              int wn, f32x4 (&acc)[8][4])
+__device__ __forceinline__ void compute_kstep(const char *a_base, const char *b_base,
+                                              const LaneOffsets &o, f32x4 (&acc)[8][4])
 {
     using F = Frag<kDtype>;
-    const char *a_base = stage + (128 * g) * kRowBytes;
-    const char *b_base = stage + kPanelBytes + (64 * wn) * kRowBytes;
 #pragma unroll
     for (int s = 0; s < F::kSlices; ++s) {
         typename F::T bf[4], af[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            bf[j] = F::load(b_base + 32 * (j >> 1) * kRowBytes, o.b[j & 1][0], o.b[j & 1][1], s);
+            bf[j] = F::load(b_base + b_blk(j), o.b[j & 1][0], o.b[j & 1][1], s);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            af[i] = F::load(a_base + 16 * (i & ~1) * kRowBytes, o.a[i & 1][0], o.a[i & 1][1], s);
+            af[i] = F::load(a_base + a_blk(i), o.a[i & 1][0], o.a[i & 1][1], s);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -213,6 +234,97 @@ __device__ __forceinline__ void compute_kstep(const char *stage, const LaneOffse
                 acc[i][j] = F::mma(bf[j], af[i], acc[i][j]);
     }
 }
+
+// Split of one K step's fragments for the ping-pong: the "head" (first half of
+// the MFMA cluster) is read from LDS during the wave's memory phase, the
+// "tail" at the start of the cluster while the head's MFMAs run.  Each part is
+// 12 ds_read_b128 (48 VGPRs per lane).
+//   bf16: head = DOT_SLICE 0 (4 B + 8 A fragments), tail = DOT_SLICE 1
+//   e4m3: head = the 4 B fragments + A fragments 0, 1; tail = A fragments 2..7
+template <int kDtype>
+struct Pipe;
+
+template <>
+struct Pipe<kBf16> {
+    using F = Frag<kBf16>;
+    struct Head {
+        bf16x8 a[8], b[4];
+    };
+    __device__ __forceinline__ static void read_head(Head &h, const char *a_base,
+                                                     const char *b_base, const LaneOffsets &o)
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            h.b[j] = F::load(b_base + b_blk(j), o.b[j & 1][0], o.b[j & 1][1], 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            h.a[i] = F::load(a_base + a_blk(i), o.a[i & 1][0], o.a[i & 1][1], 0);
+    }
+    __device__ __forceinline__ static void cluster(const Head &h, const char *a_base,
+                                                   const char *b_base, const LaneOffsets &o,
+                                                   f32x4 (&acc)[8][4])
+    {
+        bf16x8 a[8], b[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            b[j] = F::load(b_base + b_blk(j), o.b[j & 1][0], o.b[j & 1][1], 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            a[i] = F::load(a_base + a_blk(i), o.a[i & 1][0], o.a[i & 1][1], 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = F::mma(h.b[j], h.a[i], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = F::mma(b[j], a[i], acc[i][j]);
+    }
+};
+
+template <>
+struct Pipe<kFp8> {
+    using F = Frag<kFp8>;
+    struct Head {
+        i32x8 a[2], b[4];
+    };
+    __device__ __forceinline__ static void read_head(Head &h, const char *a_base,
+                                                     const char *b_base, const LaneOffsets &o)
+    {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            h.b[j] = F::load(b_base + b_blk(j), o.b[j & 1][0], o.b[j & 1][1], 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            h.a[i] = F::load(a_base + a_blk(i), o.a[i & 1][0], o.a[i & 1][1], 0);
+    }
+    __device__ __forceinline__ static void cluster(const Head &h, const char *a_base,
+                                                   const char *b_base, const LaneOffsets &o,
+                                                   f32x4 (&acc)[8][4])
+    {
+        (void)b_base;
+        i32x8 a[6];
+#pragma unroll
+        for (int i = 2; i < 8; ++i)
+            a[i - 2] = F::load(a_base + a_blk(i), o.a[i & 1][0], o.a[i & 1][1], 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = F::mma(h.b[j], h.a[i], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 2; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = F::mma(h.b[j], a[i - 2], acc[i][j]);
+    }
+};
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
@@ -284,31 +396,34 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = p.nk;
-    char *const stage0 = smem;
-    char *const stage1 = smem + kStageBytes;
+    // K step k lives in A panel k % 2 and B panel k % 3 (lockstep: k % 2).
+    auto a_panel = [&](int k) { return smem + (k & 1) * kPanelBytes; };
+    auto b_panel = [&](int k) { return smem + kBRing + (k % kBPanels) * kPanelBytes; };
+    auto b_panel2 = [&](int k) { return smem + kBRing + (k & 1) * kPanelBytes; };
 
     if (kSched == kLockstep) {
         // Each wave loads its 16 of the 64 row groups of a K step.
         if (nk > 0) {
-            dma_panel_part<4>(ra, stage0, 16 * g, w4, voff, 0, ldk);
-            dma_panel_part<4>(rb, stage0 + kPanelBytes, 16 * g, w4, voff, 0, ldk);
+            dma_panel_part<4>(ra, a_panel(0), 16 * g, w4, voff, 0, ldk);
+            dma_panel_part<4>(rb, b_panel2(0), 16 * g, w4, voff, 0, ldk);
         }
         if (nk > 1) {
-            dma_panel_part<4>(ra, stage1, 16 * g, w4, voff, kRowBytes, ldk);
-            dma_panel_part<4>(rb, stage1 + kPanelBytes, 16 * g, w4, voff, kRowBytes, ldk);
+            dma_panel_part<4>(ra, a_panel(1), 16 * g, w4, voff, kRowBytes, ldk);
+            dma_panel_part<4>(rb, b_panel2(1), 16 * g, w4, voff, kRowBytes, ldk);
             wait_vmcnt<8>();
         } else {
             wait_vmcnt<0>();
         }
         block_barrier();
         for (int t = 0; t < nk; ++t) {
-            char *st = (t & 1) ? stage1 : stage0;
-            compute_kstep<kDtype>(st, lo, g, wn, acc);
+            compute_kstep<kDtype>(a_frag_base(a_panel(t), g), b_frag_base(b_panel2(t), wn), lo,
+                                  acc);
             wait_lgkmcnt0();
-            block_barrier();                       // every wave is done with stage t&1
+            block_barrier();                       // every wave is done with K step t
             if (t + 2 < nk) {
-                dma_panel_part<4>(ra, st, 16 * g, w4, voff, (t + 2) * kRowBytes, ldk);
-                dma_panel_part<4>(rb, st + kPanelBytes, 16 * g, w4, voff, (t + 2) * kRowBytes, ldk);
+                const int soff = (t + 2) * kRowBytes;
+                dma_panel_part<4>(ra, a_panel(t), 16 * g, w4, voff, soff, ldk);
+                dma_panel_part<4>(rb, b_panel2(t), 16 * g, w4, voff, soff, ldk);
                 wait_vmcnt<8>();                   // K step t+1 has landed
             } else {
                 wait_vmcnt<0>();
@@ -317,69 +432,106 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
         }
     } else {
         // ---- 8-wave ping-pong ------------------------------------------------
-        // Who loads what (K step k into stage k & 1):
-        //   group 0: A rows   0..127 ("A0")      -- only group 0 reads them
-        //   group 1: A rows 128..255 ("A1") and all B rows
-        // Phases alternate between the groups; a phase ends at a barrier.
-        //   group 0: compute(t) | memory(t) | compute(t+1) | ...
-        //   group 1:   memory(t-1) | compute(t) | memory(t) | ...
-        // memory(t) issues the loads of K step t+2 into stage t & 1, which both
-        // groups have finished reading, and waits for the group's K step t+1.
-        // B(t+1) is awaited by group 1 at the end of its compute(t), one phase
-        // before group 0 needs it.
+        // Phases alternate between the groups and end at a barrier:
+        //   group 0:  c(0) | m(0) | c(1) | m(1) | ...
+        //   group 1:  m(-1)| c(0) | m(0) | c(1) | ...
+        // c(t) is the MFMA cluster of K step t (its head already in registers);
+        // m(t) issues HBM->LDS loads for later K steps and reads the head of
+        // c(t+1).  Loads (k = K step, into A panel k % 2 / B panel k % 3):
+        //   A rows   0..127 of k: group 0 in m(k-2), awaited at the end of c(k-1)
+        //   A rows 128..255 of k: group 1 in m(k-2), awaited at the end of c(k-1)
+        //   B rows   0..255 of k: group 1 in m(k-3), awaited at the end of m(k-2)
+        // so every panel is complete and published by a barrier before the
+        // memory phase that reads its head, and no load targets a panel that a
+        // phase in flight still reads.  Group 1 ends after c(nk-1); group 0
+        // skips the barriers after its last cluster, keeping the counts equal.
+        using P = Pipe<kDtype>;
+        typename P::Head head;
         if (nk > 0) {   // K step 0: both groups share every panel
-            dma_panel_part<4>(ra, stage0, 16 * g, w4, voff, 0, ldk);
-            dma_panel_part<4>(rb, stage0 + kPanelBytes, 16 * g, w4, voff, 0, ldk);
+            dma_panel_part<4>(ra, a_panel(0), 16 * g, w4, voff, 0, ldk);
+            dma_panel_part<4>(rb, b_panel(0), 16 * g, w4, voff, 0, ldk);
         }
-        if (nk > 1) {   // K step 1 in the steady-state split
-            if (g == 0) {
-                dma_panel_part<4>(ra, stage1, 0, w4, voff, kRowBytes, ldk);
-                wait_vmcnt<4>();
-            } else {
-                dma_panel_part<8>(rb, stage1 + kPanelBytes, 0, w4, voff, kRowBytes, ldk);
-                dma_panel_part<4>(ra, stage1, 16, w4, voff, kRowBytes, ldk);
-                wait_vmcnt<12>();
-            }
-        } else {
-            wait_vmcnt<0>();
-        }
-        block_barrier();
-        if (g == 1 && nk > 0)
-            block_barrier();                       // stagger group 1 by one phase
-
-        for (int t = 0; t < nk; ++t) {
-            char *st = (t & 1) ? stage1 : stage0;
-            // compute phase
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_setprio(3);
-            compute_kstep<kDtype>(st, lo, g, wn, acc);
-            __builtin_amdgcn_s_setprio(0);
-            __builtin_amdgcn_sched_barrier(0);
-            wait_lgkmcnt0();
-            const bool last = t == nk - 1;
-            if (g == 1) {
-                if (!last)
-                    wait_vmcnt<4>();               // B(t+1) landed; A1(t+1) may fly
-                else
-                    continue;                      // group 1 ends after its last compute
-            }
-            block_barrier();
-            // memory phase
-            if (t + 2 < nk) {
-                const int soff = (t + 2) * kRowBytes;
-                if (g == 0) {
-                    dma_panel_part<4>(ra, st, 0, w4, voff, soff, ldk);
-                    wait_vmcnt<4>();               // A0(t+1) landed
-                } else {
-                    dma_panel_part<8>(rb, st + kPanelBytes, 0, w4, voff, soff, ldk);
-                    dma_panel_part<4>(ra, st, 16, w4, voff, soff, ldk);
-                    wait_vmcnt<12>();              // A1(t+1) landed
-                }
+        if (g == 0) {
+            if (nk > 1) {
+                dma_panel_part<4>(ra, a_panel(1), 0, w4, voff, kRowBytes, ldk);
+                wait_vmcnt<4>();                   // K step 0 landed
             } else {
                 wait_vmcnt<0>();
             }
-            if (!last)
-                block_barrier();
+        } else {
+            if (nk > 1) {
+                dma_panel_part<8>(rb, b_panel(1), 0, w4, voff, kRowBytes, ldk);
+                wait_vmcnt<8>();                   // K step 0 landed
+            } else {
+                wait_vmcnt<0>();
+            }
+        }
+        block_barrier();
+
+        if (g == 0) {
+            if (nk > 0)
+                P::read_head(head, a_frag_base(a_panel(0), 0), b_frag_base(b_panel(0), wn), lo);
+            for (int t = 0; t < nk; ++t) {
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(3);
+                P::cluster(head, a_frag_base(a_panel(t), 0), b_frag_base(b_panel(t), wn), lo, acc);
+                __builtin_amdgcn_s_setprio(0);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_lgkmcnt0();
+                if (t == nk - 1)
+                    break;
+                wait_vmcnt<0>();                   // A rows 0..127 of t+1 landed
+                block_barrier();                   // end of c(t)
+                if (t + 2 < nk)
+                    dma_panel_part<4>(ra, a_panel(t + 2), 0, w4, voff, (t + 2) * kRowBytes, ldk);
+                P::read_head(head, a_frag_base(a_panel(t + 1), 0), b_frag_base(b_panel(t + 1), wn),
+                             lo);
+                block_barrier();                   // end of m(t)
+            }
+        } else if (nk > 0) {
+            // m(-1)
+            if (nk > 1)
+                dma_panel_part<4>(ra, a_panel(1), 16, w4, voff, kRowBytes, ldk);
+            if (nk > 2)
+                dma_panel_part<8>(rb, b_panel(2), 0, w4, voff, 2 * kRowBytes, ldk);
+            P::read_head(head, a_frag_base(a_panel(0), 1), b_frag_base(b_panel(0), wn), lo);
+            if (nk > 2)
+                wait_vmcnt<12>();                  // B of step 1 landed
+            else if (nk > 1)
+                wait_vmcnt<4>();
+            else
+                wait_vmcnt<0>();
+            if (nk > 1)
+                block_barrier();                   // end of m(-1)
+            for (int t = 0; t < nk; ++t) {
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(3);
+                P::cluster(head, a_frag_base(a_panel(t), 1), b_frag_base(b_panel(t), wn), lo, acc);
+                __builtin_amdgcn_s_setprio(0);
+                __builtin_amdgcn_sched_barrier(0);
+                wait_lgkmcnt0();
+                if (t == nk - 1)
+                    break;
+                if (t + 2 < nk)
+                    wait_vmcnt<8>();               // A rows 128..255 of t+1 landed
+                else
+                    wait_vmcnt<0>();
+                block_barrier();                   // end of c(t)
+                if (t + 2 < nk)
+                    dma_panel_part<4>(ra, a_panel(t + 2), 16, w4, voff, (t + 2) * kRowBytes, ldk);
+                if (t + 3 < nk)
+                    dma_panel_part<8>(rb, b_panel(t + 3), 0, w4, voff, (t + 3) * kRowBytes, ldk);
+                P::read_head(head, a_frag_base(a_panel(t + 1), 1), b_frag_base(b_panel(t + 1), wn),
+                             lo);
+                if (t + 3 < nk)
+                    wait_vmcnt<12>();              // B of step t+2 landed
+                else if (t + 2 < nk)
+                    wait_vmcnt<4>();
+                else
+                    wait_vmcnt<0>();
+                if (t != nk - 2)
+                    block_barrier();               // end of m(t)
+            }
         }
     }
     store_tile(p, tm, tn, g, wn, lane, acc);
