@@ -237,10 +237,16 @@ __device__ __forceinline__ void compute_kstep(const char *a_base, const char *b_
 
 // Split of one K step's fragments for the ping-pong: the "head" (first half of
 // the MFMA cluster) is read from LDS during the wave's memory phase, the
-// "tail" at the start of the cluster while the head's MFMAs run.  Each part is
+// "tail" during the cluster, while the head's MFMAs run.  Each part is
 // 12 ds_read_b128 (48 VGPRs per lane).
 //   bf16: head = DOT_SLICE 0 (4 B + 8 A fragments), tail = DOT_SLICE 1
 //   e4m3: head = the 4 B fragments + A fragments 0, 1; tail = A fragments 2..7
+// The tail reads are threaded between the MFMAs (sched_group_barrier) rather
+// than issued as one burst: a burst can fill the LDS command queue, and a
+// wave stalled on an LDS issue also stops issuing the MFMAs behind it.
+constexpr int kSchedMfma = 0x008;     // sched_group_barrier mask: MFMA
+constexpr int kSchedDsRead = 0x100;   // sched_group_barrier mask: LDS read
+
 template <int kDtype>
 struct Pipe;
 
@@ -271,18 +277,24 @@ struct Pipe<kBf16> {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             a[i] = F::load(a_base + a_blk(i), o.a[i & 1][0], o.a[i & 1][1], 1);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = F::mma(h.b[j], h.a[i], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = F::mma(b[j], a[i], acc[i][j]);
+        // order: (2 MFMA, 1 read) x 12 over the head, then the remaining 8 head
+        // MFMAs, then the 32 tail MFMAs
+#pragma unroll
+        for (int k = 0; k < 12; ++k) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 40, 0);
     }
 };
 
@@ -311,18 +323,29 @@ struct Pipe<kFp8> {
 #pragma unroll
         for (int i = 2; i < 8; ++i)
             a[i - 2] = F::load(a_base + a_blk(i), o.a[i & 1][0], o.a[i & 1][1], 0);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = F::mma(h.b[j], h.a[i], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 2; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = F::mma(h.b[j], a[i - 2], acc[i][j]);
+        // order: (1 MFMA, 1 read) x 8 over the head, then 4 MFMAs per A
+        // fragment, with the last 4 reads threaded between fragments 2 and 3
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16, 0);
     }
 };
 
@@ -437,10 +460,13 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
         //   group 1:  m(-1)| c(0) | m(0) | c(1) | ...
         // c(t) is the MFMA cluster of K step t (its head already in registers);
         // m(t) issues HBM->LDS loads for later K steps and reads the head of
-        // c(t+1).  Loads (k = K step, into A panel k % 2 / B panel k % 3):
+        // c(t+1).  Loads (k = K step, into A panel k % 2 / B panel k % 3), 32 KiB
+        // per memory phase for either group (the CU's HBM->LDS path, not HBM,
+        // limits how fast they issue, so the two phases carry equal shares):
         //   A rows   0..127 of k: group 0 in m(k-2), awaited at the end of c(k-1)
+        //   B rows   0..127 of k: group 0 in m(k-2), awaited at the end of c(k-1)
         //   A rows 128..255 of k: group 1 in m(k-2), awaited at the end of c(k-1)
-        //   B rows   0..255 of k: group 1 in m(k-3), awaited at the end of m(k-2)
+        //   B rows 128..255 of k: group 1 in m(k-3), awaited at the end of m(k-2)
         // so every panel is complete and published by a barrier before the
         // memory phase that reads its head, and no load targets a panel that a
         // phase in flight still reads.  Group 1 ends after c(nk-1); group 0
@@ -454,14 +480,15 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
         if (g == 0) {
             if (nk > 1) {
                 dma_panel_part<4>(ra, a_panel(1), 0, w4, voff, kRowBytes, ldk);
-                wait_vmcnt<4>();                   // K step 0 landed
+                dma_panel_part<4>(rb, b_panel(1), 0, w4, voff, kRowBytes, ldk);
+                wait_vmcnt<8>();                   // K step 0 landed
             } else {
                 wait_vmcnt<0>();
             }
         } else {
             if (nk > 1) {
-                dma_panel_part<8>(rb, b_panel(1), 0, w4, voff, kRowBytes, ldk);
-                wait_vmcnt<8>();                   // K step 0 landed
+                dma_panel_part<4>(rb, b_panel(1), 16, w4, voff, kRowBytes, ldk);
+                wait_vmcnt<4>();                   // K step 0 landed
             } else {
                 wait_vmcnt<0>();
             }
@@ -480,10 +507,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
                 wait_lgkmcnt0();
                 if (t == nk - 1)
                     break;
-                wait_vmcnt<0>();                   // A rows 0..127 of t+1 landed
+                wait_vmcnt<0>();                   // rows 0..127 of A and B of t+1 landed
                 block_barrier();                   // end of c(t)
-                if (t + 2 < nk)
+                if (t + 2 < nk) {
                     dma_panel_part<4>(ra, a_panel(t + 2), 0, w4, voff, (t + 2) * kRowBytes, ldk);
+                    dma_panel_part<4>(rb, b_panel(t + 2), 0, w4, voff, (t + 2) * kRowBytes, ldk);
+                }
                 P::read_head(head, a_frag_base(a_panel(t + 1), 0), b_frag_base(b_panel(t + 1), wn),
                              lo);
                 block_barrier();                   // end of m(t)
@@ -493,10 +522,10 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
             if (nk > 1)
                 dma_panel_part<4>(ra, a_panel(1), 16, w4, voff, kRowBytes, ldk);
             if (nk > 2)
-                dma_panel_part<8>(rb, b_panel(2), 0, w4, voff, 2 * kRowBytes, ldk);
+                dma_panel_part<4>(rb, b_panel(2), 16, w4, voff, 2 * kRowBytes, ldk);
             P::read_head(head, a_frag_base(a_panel(0), 1), b_frag_base(b_panel(0), wn), lo);
             if (nk > 2)
-                wait_vmcnt<12>();                  // B of step 1 landed
+                wait_vmcnt<8>();                   // B rows 128..255 of step 1 landed
             else if (nk > 1)
                 wait_vmcnt<4>();
             else
@@ -513,18 +542,18 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
                 if (t == nk - 1)
                     break;
                 if (t + 2 < nk)
-                    wait_vmcnt<8>();               // A rows 128..255 of t+1 landed
+                    wait_vmcnt<4>();               // A rows 128..255 of t+1 landed
                 else
                     wait_vmcnt<0>();
                 block_barrier();                   // end of c(t)
                 if (t + 2 < nk)
                     dma_panel_part<4>(ra, a_panel(t + 2), 16, w4, voff, (t + 2) * kRowBytes, ldk);
                 if (t + 3 < nk)
-                    dma_panel_part<8>(rb, b_panel(t + 3), 0, w4, voff, (t + 3) * kRowBytes, ldk);
+                    dma_panel_part<4>(rb, b_panel(t + 3), 16, w4, voff, (t + 3) * kRowBytes, ldk);
                 P::read_head(head, a_frag_base(a_panel(t + 1), 1), b_frag_base(b_panel(t + 1), wn),
                              lo);
                 if (t + 3 < nk)
-                    wait_vmcnt<12>();              // B of step t+2 landed
+                    wait_vmcnt<8>();               // B rows 128..255 of step t+2 landed
                 else if (t + 2 < nk)
                     wait_vmcnt<4>();
                 else
