@@ -30,17 +30,27 @@ from dense_gemm_fp8_amd import synth  # noqa: E402
 
 METRIC = "GEMM TFLOPS at 8192³ bf16 (fraction of 2.5 PF peak); L2/LLC hit %"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}     # MI355X dense MFMA peaks
-# HipKittens 8-wave 0P/8C bf16 GEMM at 8192^3 on MI355X (page 2, Table 2 / Q3)
+# HipKittens 8-wave 0P/8C bf16 GEMM at 8192^3 on MI355X (HipKittens L2 note, Table 2 / Q3)
 PAGES_BF16_8192_TFLOPS = 1610.0
 KERNEL_SOURCES = ("dense_gemm_fp8_amd/csrc/gemm_kernels.hip", "dense_gemm_fp8_amd/csrc/remap.h",
                   "dense_gemm_fp8_amd/csrc/kernels.h", "dense_gemm_fp8_amd/csrc/hkg_api.cpp")
 
 
+def _strip_comments(text: str) -> str:
+    """C/C++ source without comments and whitespace (a comment edit keeps the hash)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel and launch code, comments ignored: ties counter facts
+    committed under profiles/ to the code they were measured on."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            h.update(_strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

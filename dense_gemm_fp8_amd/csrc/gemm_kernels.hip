@@ -1,12 +1,12 @@
 // gemm_kernels.hip -- gfx950 (MI355X) kernels for C = A * B^T.
 //
 // One 512-thread workgroup (8 waves of 64 lanes) computes one 256 x 256 output
-// tile (HipKittens, page 2, section 3 "Launch config": BLOCK 256 x 256,
+// tile (HipKittens L2 note, section 3 "Launch config": BLOCK 256 x 256,
 // K_STEP 64, WARPS_M = 2, WARPS_N = 4, DOT_SLICE 32, MFMA 16x16x32).
 //
 // Data path of one K step:
 //   HBM/L2 --buffer_load_dwordx4 ... lds--> LDS stage --ds_read_b128--> VGPR
-//   fragments --v_mfma--> fp32 accumulators (page 2, section 2 Pillar 1:
+//   fragments --v_mfma--> fp32 accumulators (HipKittens L2 note, section 2 Pillar 1:
 //   direct HBM->LDS loads that bypass the register file, with the XOR swizzle
 //   applied to the HBM address).
 //
@@ -16,7 +16,7 @@
 //   one 128-byte row = one K step of one operand row (64 bf16 or 128 e4m3)
 //   row r stores its eight 16-byte chunks permuted: chunk c lives in slot
 //   c ^ slot_xor(r).
-// The pages keep a 2-deep LDS double buffer (page 2, section 4 "Pipeline
+// The pages keep a 2-deep LDS double buffer (HipKittens L2 note, section 4 "Pipeline
 // depth"); the third B panel here exists so that the ping-pong below can
 // prefetch register fragments one phase early while the shared B panel still
 // has three phases to arrive from HBM.
@@ -26,13 +26,13 @@
 // therefore cannot choose where its bytes land; instead each lane fetches the
 // global chunk that belongs in its fixed slot: lane l -> row 8u + l/8,
 // slot l%8, global chunk (l%8) ^ slot_xor(row).  This is the "swizzle applied
-// to the HBM address" of page 2, section 2 / page 1.
+// to the HBM address" of the HipKittens L2 note (section 2) and summary page.
 //
 // Waves and the output tile (WARPS_M = 2 x WARPS_N = 4):
 //   wave w: group g = w / 4 owns tile rows [128 g, 128 g + 128),
 //           wn = w % 4 owns tile columns [64 wn, 64 wn + 64)
 //   -> a 128 x 64 fp32 sub-tile = 8 x 4 MFMA blocks of 16 x 16 = 128 fp32
-//      accumulator registers per lane (page 2 section 4 "Tile / launch
+//      accumulator registers per lane (HipKittens L2 note, section 4 "Tile / launch
 //      optimality": the register budget at 2 waves per SIMD).
 //
 // MFMA operand order: the B fragment is the instruction's first (row) operand
@@ -42,7 +42,7 @@
 // 4a + b -> tile column 8a + b + 4 (j & 1) + 32 (j >> 1)) so that blocks j = 0,1
 // give a lane 8 consecutive bf16 (one 16-byte store) and j = 2,3 another 8.
 //
-// Schedules (page 2, section 2 Pillar 2; section 9.1 and 9.2):
+// Schedules (HipKittens L2 note, section 2 Pillar 2; sections 9.1 and 9.2):
 //   kPingPong  8-wave ping-pong.  Group 0 (waves 0-3, one per SIMD) and group
 //              1 (waves 4-7) run one barrier apart: while one group issues its
 //              MFMA cluster at s_setprio 3 the other issues the next K steps'

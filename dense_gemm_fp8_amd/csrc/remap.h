@@ -1,6 +1,6 @@
 // remap.h -- chiplet-aware workgroup -> output-tile remap for the GEMM kernels.
 //
-// HipKittens, page 2: section 2 (Pillar 3, non-programmable cache), section 7
+// HipKittens L2 note: section 2 (Pillar 3, non-programmable cache), section 7
 // (code citation 5, Algorithm 1 "XCD swizzle"), section 5 (Table 4: window W,
 // chunk C).  The hardware hands workgroup b of a launch to XCD b mod 8, so
 // neighbouring ids land on different L2 caches.  The remap

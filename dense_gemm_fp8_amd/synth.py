@@ -9,7 +9,7 @@ into the two input formats the path consumes.
   s = amax / 448 (448 is the largest finite e4m3 value) and rounded to the
   nearest e4m3 code with ties to even; magnitudes above 448 saturate to +-448.
 
-The HipKittens pages (page 2, "Target operation" table) give the GEMM shapes and
+The HipKittens L2 note (section 3, "Target operation" table) gives the GEMM shapes and
 dtypes but no RNG, quantiser or rounding rule; the plainest readings are used
 here and listed in the design notes.
 

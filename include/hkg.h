@@ -3,18 +3,18 @@
  *
  *     C[M][N] = A[M][K] * B[N][K]^T        fp32 accumulation
  *
- * The operation is the BF16 GEMM / FP8 GEMM of HipKittens (page 2, section 3
+ * The operation is the BF16 GEMM / FP8 GEMM of the HipKittens L2 note (section 3
  * "Target operation" table: BF16 inputs, FP32 accumulator, BF16 output), with
  * B used transposed as in the mma_ABt calls of the GEMM listing descriptions
- * (page 2, sections 7 and 9.2).  Both operands are row-major with K contiguous
+ * (same note, sections 7 and 9.2).  Both operands are row-major with K contiguous
  * ("K-major"); C is row-major.  The fp8 variant takes OCP e4m3 bytes with one
  * fp32 scale per tensor and writes bf16  C = bf16(scale_a * scale_b * A*B^T).
  *
- * Launch shape (page 2, section 3 "Launch config" and section 8 "Launch
+ * Launch shape (same note, section 3 "Launch config" and section 8 "Launch
  * shape"): one 512-thread workgroup (8 waves) per 256 x 256 output tile, a
  * flat grid of ceil(M/256) * ceil(N/256) workgroups, K consumed 64 (bf16) or
  * 128 (e4m3) at a time.  Workgroup ids are remapped to tiles by the
- * chiplet-aware schedule of page 2, section 2 (Pillar 3) / section 7
+ * chiplet-aware schedule of the same note, section 2 (Pillar 3) / section 7
  * (Algorithm 1), with window height W and per-XCD chunk C.
  *
  * Conventions for every entry point:
@@ -49,14 +49,14 @@ typedef enum {
     HKG_ERR_LAUNCH = -7   /* the kernel launch failed; see hkg_last_hip_error()      */
 } hkg_status;
 
-/* Grid order (the remap of page 2, section 2 Pillar 3 / section 7 Algorithm 1). */
+/* Grid order (the remap of the HipKittens L2 note, section 2 Pillar 3 / section 7 Algorithm 1). */
 enum {
     HKG_REMAP_DEFAULT = 0,  /* library's per-shape choice of (W, C)                */
     HKG_REMAP_ROW_MAJOR = 1,/* identity order (W = 1, C = 1)                       */
     HKG_REMAP_XCD = 2       /* explicit window height W >= 1 and chunk C >= 1       */
 };
 
-/* In-CU schedule (page 2, section 2 Pillar 2 and section 9.2). */
+/* In-CU schedule (HipKittens L2 note, section 2 Pillar 2 and section 9.2). */
 enum {
     HKG_SCHED_DEFAULT = 0,  /* 8-wave ping-pong                                     */
     HKG_SCHED_PINGPONG = 1, /* 8-wave ping-pong: 2 groups of 4 waves alternate the
@@ -110,7 +110,7 @@ int hkg_gemm_fp8_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *
 int hkg_default_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *W, int32_t *C);
 
 /*
- * The grid remap itself (page 2, section 7 Algorithm 1 reading): flat
+ * The grid remap itself (HipKittens L2 note, section 7 Algorithm 1 reading): flat
  * workgroup id b of a Gm x Gn tile grid -> output tile (tile_m, tile_n) for
  * window height W and chunk C.  Host function, no HIP call.  Returns
  * HKG_ERR_SHAPE if b is outside [0, Gm*Gn) or W, C < 1.

@@ -1,11 +1,11 @@
 """The chiplet cache bandwidth model -- TEST INFRASTRUCTURE ONLY.
 
-Source: HipKittens, page 2, section 4 ("方程物理意義", the paper's single explicit
+Source: HipKittens L2 note, section 4 ("方程物理意義", the paper's single explicit
 equation) and section 2 (Pillar 3):
 
     BW = LLC_BW * LLC_hit + L2_BW * L2_hit
 
-with hit rates as fractions.  Table 4 (page 2, section 5) prints, per grid
+with hit rates as fractions.  Table 4 (same note, section 5) prints, per grid
 order, the L2 and LLC hit rates and a "Mem BW" column.  Reading that column as
 this equation's output, the two constants are recovered by least squares over
 the six rows; the pages state L2 bandwidth is about 3x LLC bandwidth.

@@ -5,7 +5,7 @@
  * bench's CPU-baseline leg may load this library; the GPU library never does,
  * and the two share no source.
  *
- * What it computes (HipKittens, page 2, section 3 "Target operation" table:
+ * What it computes (HipKittens L2 note, section 3 "Target operation" table:
  * BF16 GEMM and FP8 GEMM, FP32 accumulate; B is used transposed, as the
  * mma_ABt calls in the section 7/9 listing descriptions show):
  *

@@ -1,6 +1,6 @@
 """Chiplet-aware grid remap, written from the pages -- TEST INFRASTRUCTURE ONLY.
 
-Source: HipKittens, page 2, section 2 (Q2, "Pillar 3 -- Non-programmable
+Source: HipKittens L2 note, section 2 (Q2, "Pillar 3 -- Non-programmable
 cache"), section 7 (code citation 5, "XCD swizzle (Algorithm 1, section 3.4)")
 and section 5 (Table 4 parameters W, C).  The pages describe the steps but do
 not print the pseudocode, so this is the plainest reading of their steps:
