@@ -10,6 +10,9 @@ and the CPU oracle timed on a bounded sample as a baseline.
   python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload 2]
                   [--all] [--remap W,C | --row-major] [--schedule pingpong|lockstep]
                   [--no-cpu-baseline]
+  python bench.py --sweep "1,1 8,32 5,25 ..." [--workload N | --shape M,N,K --dtype bf16|fp8]
+        grid-order sweep: one JSON line per (W, C) on the same resident inputs
+        ("1,1" is row-major order); used to choose the library's default (W, C)
 """
 from __future__ import annotations
 
@@ -202,6 +205,53 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
     return res
 
 
+def custom_workload(shape: str, dtype: str) -> synth.Workload:
+    M, N, K = (int(v) for v in shape.split(","))
+    return synth.Workload("%s_%dx%dx%d" % (dtype, M, N, K), dtype, M, N, K, 7101, 7102)
+
+
+def sweep(w: synth.Workload, pairs, steps: int, warmup: int) -> None:
+    """Time each grid order (W, C) on the same inputs; one JSON line each."""
+    import torch
+    import dense_gemm_fp8_amd as hkg
+
+    dev = torch.device("cuda:0")
+    A, B, sa, sb = synth.make_inputs(w)
+    if w.dtype == "bf16":
+        dA = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).to(dev)
+        dB = torch.from_numpy(B.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        dA = torch.from_numpy(A).to(dev)
+        dB = torch.from_numpy(B).to(dev)
+    del A, B
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    rc, dW, dC = hkg.hkg_default_remap(w.M, w.N, w.K, 0 if w.dtype == "bf16" else 1)
+    for (W, Cc) in pairs:
+        opts = hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=W, C=Cc)
+
+        def step():
+            if w.dtype == "bf16":
+                hkg.gemm_bf16(dA, dB, C, opts=opts, stream=stream)
+            else:
+                hkg.gemm_fp8(dA, dB, sa, sb, C, opts=opts, stream=stream)
+
+        for _ in range(warmup):
+            step()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        print(json.dumps({"sweep": w.name, "M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype,
+                          "W": W, "C": Cc, "default": [W, Cc] == [dW, dC], "ms": round(ms, 5),
+                          "TFLOPS": round(w.flops / (ms * 1e-3) / 1e12, 2)}), flush=True)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +263,9 @@ def main(argv=None) -> int:
     ap.add_argument("--row-major", action="store_true")
     ap.add_argument("--schedule", choices=["pingpong", "lockstep"], default="pingpong")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shape", type=str, default=None, help="M,N,K (custom size)")
+    ap.add_argument("--dtype", choices=["bf16", "fp8"], default="bf16")
+    ap.add_argument("--sweep", type=str, default=None, help='"W,C W,C ..." grid orders to time')
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -232,9 +285,14 @@ def main(argv=None) -> int:
     elif sched != hkg.HKG_SCHED_PINGPONG:
         opts = hkg.make_opts(schedule=sched)
 
+    if args.sweep:
+        w = custom_workload(args.shape, args.dtype) if args.shape else synth.workload(args.workload)
+        pairs = [tuple(int(v) for v in item.split(",")) for item in args.sweep.split()]
+        sweep(w, pairs, args.steps, args.warmup)
+        return 0
     ids = [1, 2, 3, 4, 5] if args.all else [args.workload]
     for i in ids:
-        w = synth.workload(i)
+        w = synth.workload(i) if not args.shape else custom_workload(args.shape, args.dtype)
         steps = args.steps
         res = bench_one(w, steps, args.warmup, opts, args.schedule,
                         with_cpu=(not args.no_cpu_baseline))

@@ -235,117 +235,69 @@ __device__ __forceinline__ void compute_kstep(const char *a_base, const char *b_
     }
 }
 
-// Split of one K step's fragments for the ping-pong: the "head" (first half of
-// the MFMA cluster) is read from LDS during the wave's memory phase, the
-// "tail" during the cluster, while the head's MFMAs run.  Each part is
-// 12 ds_read_b128 (48 VGPRs per lane).
-//   bf16: head = DOT_SLICE 0 (4 B + 8 A fragments), tail = DOT_SLICE 1
-//   e4m3: head = the 4 B fragments + A fragments 0, 1; tail = A fragments 2..7
-// The tail reads are threaded between the MFMAs (sched_group_barrier) rather
-// than issued as one burst: a burst can fill the LDS command queue, and a
-// wave stalled on an LDS issue also stops issuing the MFMAs behind it.
-constexpr int kSchedMfma = 0x008;     // sched_group_barrier mask: MFMA
-constexpr int kSchedDsRead = 0x100;   // sched_group_barrier mask: LDS read
-
+// Fragments of one K step for the ping-pong.  A wave reads all of them
+// (24 ds_read_b128, 96 VGPRs per lane) during its memory phase, while its
+// partner runs MFMAs, so the MFMA cluster itself contains no LDS instruction
+// and issues back to back.
+//   bf16: 2 DOT_SLICEs x (8 A + 4 B) fragments of 8 bf16
+//   e4m3: 8 A + 4 B fragments of 32 e4m3 (two 16-byte chunks each)
 template <int kDtype>
 struct Pipe;
 
 template <>
 struct Pipe<kBf16> {
     using F = Frag<kBf16>;
-    struct Head {
-        bf16x8 a[8], b[4];
+    struct Frags {
+        bf16x8 a[2][8], b[2][4];
     };
-    __device__ __forceinline__ static void read_head(Head &h, const char *a_base,
-                                                     const char *b_base, const LaneOffsets &o)
+    __device__ __forceinline__ static void read(Frags &f, const char *a_base, const char *b_base,
+                                                const LaneOffsets &o)
     {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            h.b[j] = F::load(b_base + b_blk(j), o.b[j & 1][0], o.b[j & 1][1], 0);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            h.a[i] = F::load(a_base + a_blk(i), o.a[i & 1][0], o.a[i & 1][1], 0);
-    }
-    __device__ __forceinline__ static void cluster(const Head &h, const char *a_base,
-                                                   const char *b_base, const LaneOffsets &o,
-                                                   f32x4 (&acc)[8][4])
-    {
-        bf16x8 a[8], b[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            b[j] = F::load(b_base + b_blk(j), o.b[j & 1][0], o.b[j & 1][1], 1);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            a[i] = F::load(a_base + a_blk(i), o.a[i & 1][0], o.a[i & 1][1], 1);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int s = 0; s < 2; ++s) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                acc[i][j] = F::mma(h.b[j], h.a[i], acc[i][j]);
+                f.b[s][j] = F::load(b_base + b_blk(j), o.b[j & 1][0], o.b[j & 1][1], s);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = F::mma(b[j], a[i], acc[i][j]);
-        // order: (2 MFMA, 1 read) x 12 over the head, then the remaining 8 head
-        // MFMAs, then the 32 tail MFMAs
-#pragma unroll
-        for (int k = 0; k < 12; ++k) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+            for (int i = 0; i < 8; ++i)
+                f.a[s][i] = F::load(a_base + a_blk(i), o.a[i & 1][0], o.a[i & 1][1], s);
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 40, 0);
+    }
+    __device__ __forceinline__ static void cluster(const Frags &f, f32x4 (&acc)[8][4])
+    {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = F::mma(f.b[s][j], f.a[s][i], acc[i][j]);
     }
 };
 
 template <>
 struct Pipe<kFp8> {
     using F = Frag<kFp8>;
-    struct Head {
-        i32x8 a[2], b[4];
+    struct Frags {
+        i32x8 a[8], b[4];
     };
-    __device__ __forceinline__ static void read_head(Head &h, const char *a_base,
-                                                     const char *b_base, const LaneOffsets &o)
+    __device__ __forceinline__ static void read(Frags &f, const char *a_base, const char *b_base,
+                                                const LaneOffsets &o)
     {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            h.b[j] = F::load(b_base + b_blk(j), o.b[j & 1][0], o.b[j & 1][1], 0);
+            f.b[j] = F::load(b_base + b_blk(j), o.b[j & 1][0], o.b[j & 1][1], 0);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            h.a[i] = F::load(a_base + a_blk(i), o.a[i & 1][0], o.a[i & 1][1], 0);
+        for (int i = 0; i < 8; ++i)
+            f.a[i] = F::load(a_base + a_blk(i), o.a[i & 1][0], o.a[i & 1][1], 0);
     }
-    __device__ __forceinline__ static void cluster(const Head &h, const char *a_base,
-                                                   const char *b_base, const LaneOffsets &o,
-                                                   f32x4 (&acc)[8][4])
+    __device__ __forceinline__ static void cluster(const Frags &f, f32x4 (&acc)[8][4])
     {
-        (void)b_base;
-        i32x8 a[6];
 #pragma unroll
-        for (int i = 2; i < 8; ++i)
-            a[i - 2] = F::load(a_base + a_blk(i), o.a[i & 1][0], o.a[i & 1][1], 0);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                acc[i][j] = F::mma(h.b[j], h.a[i], acc[i][j]);
-#pragma unroll
-        for (int i = 2; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = F::mma(h.b[j], a[i - 2], acc[i][j]);
-        // order: (1 MFMA, 1 read) x 8 over the head, then 4 MFMAs per A
-        // fragment, with the last 4 reads threaded between fragments 2 and 3
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-        }
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16, 0);
+                acc[i][j] = F::mma(f.b[j], f.a[i], acc[i][j]);
     }
 };
 
@@ -458,9 +410,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
         // Phases alternate between the groups and end at a barrier:
         //   group 0:  c(0) | m(0) | c(1) | m(1) | ...
         //   group 1:  m(-1)| c(0) | m(0) | c(1) | ...
-        // c(t) is the MFMA cluster of K step t (its head already in registers);
-        // m(t) issues HBM->LDS loads for later K steps and reads the head of
-        // c(t+1).  Loads (k = K step, into A panel k % 2 / B panel k % 3), 32 KiB
+        // c(t) is the MFMA cluster of K step t (its fragments already in
+        // registers); m(t) issues HBM->LDS loads for later K steps and reads
+        // all fragments of c(t+1) from LDS.  Loads (k = K step, into A panel k % 2 / B panel k % 3), 32 KiB
         // per memory phase for either group (the CU's HBM->LDS path, not HBM,
         // limits how fast they issue, so the two phases carry equal shares):
         //   A rows   0..127 of k: group 0 in m(k-2), awaited at the end of c(k-1)
@@ -468,11 +420,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
         //   A rows 128..255 of k: group 1 in m(k-2), awaited at the end of c(k-1)
         //   B rows 128..255 of k: group 1 in m(k-3), awaited at the end of m(k-2)
         // so every panel is complete and published by a barrier before the
-        // memory phase that reads its head, and no load targets a panel that a
+        // memory phase that reads its fragments, and no load targets a panel that a
         // phase in flight still reads.  Group 1 ends after c(nk-1); group 0
         // skips the barriers after its last cluster, keeping the counts equal.
         using P = Pipe<kDtype>;
-        typename P::Head head;
+        typename P::Frags frags;
         if (nk > 0) {   // K step 0: both groups share every panel
             dma_panel_part<4>(ra, a_panel(0), 16 * g, w4, voff, 0, ldk);
             dma_panel_part<4>(rb, b_panel(0), 16 * g, w4, voff, 0, ldk);
@@ -497,11 +449,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
 
         if (g == 0) {
             if (nk > 0)
-                P::read_head(head, a_frag_base(a_panel(0), 0), b_frag_base(b_panel(0), wn), lo);
+                P::read(frags, a_frag_base(a_panel(0), 0), b_frag_base(b_panel(0), wn), lo);
             for (int t = 0; t < nk; ++t) {
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_setprio(3);
-                P::cluster(head, a_frag_base(a_panel(t), 0), b_frag_base(b_panel(t), wn), lo, acc);
+                P::cluster(frags, acc);
                 __builtin_amdgcn_s_setprio(0);
                 __builtin_amdgcn_sched_barrier(0);
                 wait_lgkmcnt0();
@@ -513,8 +465,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
                     dma_panel_part<4>(ra, a_panel(t + 2), 0, w4, voff, (t + 2) * kRowBytes, ldk);
                     dma_panel_part<4>(rb, b_panel(t + 2), 0, w4, voff, (t + 2) * kRowBytes, ldk);
                 }
-                P::read_head(head, a_frag_base(a_panel(t + 1), 0), b_frag_base(b_panel(t + 1), wn),
-                             lo);
+                P::read(frags, a_frag_base(a_panel(t + 1), 0), b_frag_base(b_panel(t + 1), wn), lo);
                 block_barrier();                   // end of m(t)
             }
         } else if (nk > 0) {
@@ -523,7 +474,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
                 dma_panel_part<4>(ra, a_panel(1), 16, w4, voff, kRowBytes, ldk);
             if (nk > 2)
                 dma_panel_part<4>(rb, b_panel(2), 16, w4, voff, 2 * kRowBytes, ldk);
-            P::read_head(head, a_frag_base(a_panel(0), 1), b_frag_base(b_panel(0), wn), lo);
+            P::read(frags, a_frag_base(a_panel(0), 1), b_frag_base(b_panel(0), wn), lo);
             if (nk > 2)
                 wait_vmcnt<8>();                   // B rows 128..255 of step 1 landed
             else if (nk > 1)
@@ -535,7 +486,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
             for (int t = 0; t < nk; ++t) {
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_setprio(3);
-                P::cluster(head, a_frag_base(a_panel(t), 1), b_frag_base(b_panel(t), wn), lo, acc);
+                P::cluster(frags, acc);
                 __builtin_amdgcn_s_setprio(0);
                 __builtin_amdgcn_sched_barrier(0);
                 wait_lgkmcnt0();
@@ -550,8 +501,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
                     dma_panel_part<4>(ra, a_panel(t + 2), 16, w4, voff, (t + 2) * kRowBytes, ldk);
                 if (t + 3 < nk)
                     dma_panel_part<4>(rb, b_panel(t + 3), 16, w4, voff, (t + 3) * kRowBytes, ldk);
-                P::read_head(head, a_frag_base(a_panel(t + 1), 1), b_frag_base(b_panel(t + 1), wn),
-                             lo);
+                P::read(frags, a_frag_base(a_panel(t + 1), 1), b_frag_base(b_panel(t + 1), wn), lo);
                 if (t + 3 < nk)
                     wait_vmcnt<8>();               // B rows 128..255 of step t+2 landed
                 else if (t + 2 < nk)
