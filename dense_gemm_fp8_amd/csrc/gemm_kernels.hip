@@ -21,6 +21,13 @@
 // prefetch register fragments one phase early while the shared B panel still
 // has three phases to arrive from HBM.
 //
+// Edges: the buffer resource of a tile's panel spans exactly its valid rows,
+// and a buffer load whose offset (voffset + soffset) is out of range writes
+// zeros into LDS, so rows past M or N arrive as zeros.  In a last, partial K
+// step the lanes whose 16-byte chunk lies past K get an out-of-range voffset
+// (chunks never straddle K: K is a multiple of 8 bf16 / 16 e4m3).  Stores
+// skip rows >= M and columns >= N.
+//
 // A buffer load with the LDS bit writes lane l's 16 bytes to LDS address
 // M0 + 16*l, so one instruction fills 8 consecutive rows (1 KiB).  The lane
 // therefore cannot choose where its bytes land; instead each lane fetches the
@@ -117,6 +124,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 {
     // dword3 0x00020000: raw (untyped) 32-bit buffer access on gfx9-family parts.
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+
+constexpr int kOutOfRange = int(0x80000000u);   // voffset past any panel's range
+
+// voffset for K step k: the lane's own offset, or out of range if its chunk
+// (at byte cbytes of the K step) lies past the row's ldk bytes.
+__device__ __forceinline__ int kstep_voff(int voff, int cbytes, int k, int ldk)
+{
+    return k * kRowBytes + cbytes < ldk ? voff : kOutOfRange;
 }
 
 // One wave-wide HBM->LDS load of 8 panel rows (u = row group, 0..31).
@@ -309,6 +325,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 
 // Write the wave's 128 x 64 sub-tile: per 16-row block i a lane owns output
 // row m = 16 i + (lane % 16) and columns 8 q .. 8 q + 7 and 32 + 8 q .. + 7.
+// Tiles inside M x N with N % 8 == 0 use 16-byte stores; edge tiles store
+// only rows < M and columns < N (element by element when N % 8 != 0).
 __device__ __forceinline__ void store_tile(const GemmParams &p, int tm, int tn, int g, int wn,
                                            int lane, f32x4 (&acc)[8][4])
 {
@@ -317,20 +335,37 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, int tm, int tn, 
     const int64_t col0 = (int64_t)tn * kTile + 64 * wn + 8 * q;
     const float sc = p.scale;
     uint16_t *C = static_cast<uint16_t *>(p.C);
+    const bool vec = (p.N & 7) == 0;
+    const bool inside = (tm + 1) * kTile <= p.M && (tn + 1) * kTile <= p.N && vec;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int64_t m = row0 + 16 * i;
+        if (!inside && m >= p.M)
+            continue;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const f32x4 lo = acc[i][2 * h] * sc;
             const f32x4 hi = acc[i][2 * h + 1] * sc;
-            const int64_t off = m * p.N + col0 + 32 * h;
+            const int64_t n0 = col0 + 32 * h;
+            const int64_t off = m * p.N + n0;
             u32x4 packed = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
                             pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
-            *reinterpret_cast<u32x4 *>(C + off) = packed;
-            if (p.C_f32) {
-                *reinterpret_cast<f32x4 *>(p.C_f32 + off) = lo;
-                *reinterpret_cast<f32x4 *>(p.C_f32 + off + 4) = hi;
+            if (inside || (vec && n0 < p.N)) {
+                *reinterpret_cast<u32x4 *>(C + off) = packed;
+                if (p.C_f32) {
+                    *reinterpret_cast<f32x4 *>(p.C_f32 + off) = lo;
+                    *reinterpret_cast<f32x4 *>(p.C_f32 + off + 4) = hi;
+                }
+            } else if (!vec) {
+                const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    if (n0 + e < p.N) {
+                        C[off + e] = (uint16_t)(packed[e >> 1] >> (16 * (e & 1)));
+                        if (p.C_f32)
+                            p.C_f32[off + e] = v[e];
+                    }
+                }
             }
         }
     }
@@ -352,15 +387,19 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
 
     constexpr int kElem = kDtype == kBf16 ? 2 : 1;
     const int ldk = p.K * kElem;                          // bytes per operand row
+    const int rows_a = min(kTile, p.M - tm * kTile);      // valid rows of this tile's panels
+    const int rows_b = min(kTile, p.N - tn * kTile);
     const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(static_cast<const char *>(p.A) + (int64_t)tm * kTile * ldk, kTile * ldk);
+        make_rsrc(static_cast<const char *>(p.A) + (int64_t)tm * kTile * ldk, rows_a * ldk);
     const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(static_cast<const char *>(p.B) + (int64_t)tn * kTile * ldk, kTile * ldk);
+        make_rsrc(static_cast<const char *>(p.B) + (int64_t)tn * kTile * ldk, rows_b * ldk);
 
     // This lane's source offset inside a row group: row 8u + lane/8, slot
     // lane%8; row bits 3,4 equal (u & 3) == w4 for every load this wave issues.
     const int r8 = lane >> 3;
-    const int voff = r8 * ldk + (((lane & 7) ^ slot_xor(r8 | (w4 << 3))) << 4);
+    const int cbytes = ((lane & 7) ^ slot_xor(r8 | (w4 << 3))) << 4;
+    const int voff0 = r8 * ldk + cbytes;
+    auto voff = [&](int k) { return kstep_voff(voff0, cbytes, k, ldk); };
 
     const LaneOffsets lo = lane_offsets(lane);
     f32x4 acc[8][4];
@@ -379,12 +418,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
     if (kSched == kLockstep) {
         // Each wave loads its 16 of the 64 row groups of a K step.
         if (nk > 0) {
-            dma_panel_part<4>(ra, a_panel(0), 16 * g, w4, voff, 0, ldk);
-            dma_panel_part<4>(rb, b_panel2(0), 16 * g, w4, voff, 0, ldk);
+            dma_panel_part<4>(ra, a_panel(0), 16 * g, w4, voff(0), 0, ldk);
+            dma_panel_part<4>(rb, b_panel2(0), 16 * g, w4, voff(0), 0, ldk);
         }
         if (nk > 1) {
-            dma_panel_part<4>(ra, a_panel(1), 16 * g, w4, voff, kRowBytes, ldk);
-            dma_panel_part<4>(rb, b_panel2(1), 16 * g, w4, voff, kRowBytes, ldk);
+            dma_panel_part<4>(ra, a_panel(1), 16 * g, w4, voff(1), kRowBytes, ldk);
+            dma_panel_part<4>(rb, b_panel2(1), 16 * g, w4, voff(1), kRowBytes, ldk);
             wait_vmcnt<8>();
         } else {
             wait_vmcnt<0>();
@@ -397,8 +436,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
             block_barrier();                       // every wave is done with K step t
             if (t + 2 < nk) {
                 const int soff = (t + 2) * kRowBytes;
-                dma_panel_part<4>(ra, a_panel(t), 16 * g, w4, voff, soff, ldk);
-                dma_panel_part<4>(rb, b_panel2(t), 16 * g, w4, voff, soff, ldk);
+                dma_panel_part<4>(ra, a_panel(t), 16 * g, w4, voff(t + 2), soff, ldk);
+                dma_panel_part<4>(rb, b_panel2(t), 16 * g, w4, voff(t + 2), soff, ldk);
                 wait_vmcnt<8>();                   // K step t+1 has landed
             } else {
                 wait_vmcnt<0>();
@@ -426,20 +465,20 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
         using P = Pipe<kDtype>;
         typename P::Frags frags;
         if (nk > 0) {   // K step 0: both groups share every panel
-            dma_panel_part<4>(ra, a_panel(0), 16 * g, w4, voff, 0, ldk);
-            dma_panel_part<4>(rb, b_panel(0), 16 * g, w4, voff, 0, ldk);
+            dma_panel_part<4>(ra, a_panel(0), 16 * g, w4, voff(0), 0, ldk);
+            dma_panel_part<4>(rb, b_panel(0), 16 * g, w4, voff(0), 0, ldk);
         }
         if (g == 0) {
             if (nk > 1) {
-                dma_panel_part<4>(ra, a_panel(1), 0, w4, voff, kRowBytes, ldk);
-                dma_panel_part<4>(rb, b_panel(1), 0, w4, voff, kRowBytes, ldk);
+                dma_panel_part<4>(ra, a_panel(1), 0, w4, voff(1), kRowBytes, ldk);
+                dma_panel_part<4>(rb, b_panel(1), 0, w4, voff(1), kRowBytes, ldk);
                 wait_vmcnt<8>();                   // K step 0 landed
             } else {
                 wait_vmcnt<0>();
             }
         } else {
             if (nk > 1) {
-                dma_panel_part<4>(rb, b_panel(1), 16, w4, voff, kRowBytes, ldk);
+                dma_panel_part<4>(rb, b_panel(1), 16, w4, voff(1), kRowBytes, ldk);
                 wait_vmcnt<4>();                   // K step 0 landed
             } else {
                 wait_vmcnt<0>();
@@ -462,8 +501,10 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
                 wait_vmcnt<0>();                   // rows 0..127 of A and B of t+1 landed
                 block_barrier();                   // end of c(t)
                 if (t + 2 < nk) {
-                    dma_panel_part<4>(ra, a_panel(t + 2), 0, w4, voff, (t + 2) * kRowBytes, ldk);
-                    dma_panel_part<4>(rb, b_panel(t + 2), 0, w4, voff, (t + 2) * kRowBytes, ldk);
+                    dma_panel_part<4>(ra, a_panel(t + 2), 0, w4, voff(t + 2),
+                                      (t + 2) * kRowBytes, ldk);
+                    dma_panel_part<4>(rb, b_panel(t + 2), 0, w4, voff(t + 2),
+                                      (t + 2) * kRowBytes, ldk);
                 }
                 P::read(frags, a_frag_base(a_panel(t + 1), 0), b_frag_base(b_panel(t + 1), wn), lo);
                 block_barrier();                   // end of m(t)
@@ -471,9 +512,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
         } else if (nk > 0) {
             // m(-1)
             if (nk > 1)
-                dma_panel_part<4>(ra, a_panel(1), 16, w4, voff, kRowBytes, ldk);
+                dma_panel_part<4>(ra, a_panel(1), 16, w4, voff(1), kRowBytes, ldk);
             if (nk > 2)
-                dma_panel_part<4>(rb, b_panel(2), 16, w4, voff, 2 * kRowBytes, ldk);
+                dma_panel_part<4>(rb, b_panel(2), 16, w4, voff(2), 2 * kRowBytes, ldk);
             P::read(frags, a_frag_base(a_panel(0), 1), b_frag_base(b_panel(0), wn), lo);
             if (nk > 2)
                 wait_vmcnt<8>();                   // B rows 128..255 of step 1 landed
@@ -498,9 +539,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
                     wait_vmcnt<0>();
                 block_barrier();                   // end of c(t)
                 if (t + 2 < nk)
-                    dma_panel_part<4>(ra, a_panel(t + 2), 16, w4, voff, (t + 2) * kRowBytes, ldk);
+                    dma_panel_part<4>(ra, a_panel(t + 2), 16, w4, voff(t + 2),
+                                      (t + 2) * kRowBytes, ldk);
                 if (t + 3 < nk)
-                    dma_panel_part<4>(rb, b_panel(t + 3), 16, w4, voff, (t + 3) * kRowBytes, ldk);
+                    dma_panel_part<4>(rb, b_panel(t + 3), 16, w4, voff(t + 3),
+                                      (t + 3) * kRowBytes, ldk);
                 P::read(frags, a_frag_base(a_panel(t + 1), 1), b_frag_base(b_panel(t + 1), wn), lo);
                 if (t + 3 < nk)
                     wait_vmcnt<8>();               // B rows 128..255 of step t+2 landed

@@ -15,8 +15,12 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr int64_t kTile = 256;
-constexpr int64_t kKStepBf16 = 64;
+constexpr int64_t kKStepBf16 = 64;     // K elements per step (one 128-byte LDS row)
 constexpr int64_t kKStepFp8 = 128;
+constexpr int64_t kKAlignBf16 = 8;     // K granule: operand rows stay 16-byte aligned
+constexpr int64_t kKAlignFp8 = 16;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -48,12 +52,12 @@ void default_remap(int64_t Gm, int64_t Gn, int32_t *W, int32_t *C)
     *C = static_cast<int32_t>(c);
 }
 
-int validate(int64_t M, int64_t N, int64_t K, int64_t kstep, int64_t elem, const void *A,
+int validate(int64_t M, int64_t N, int64_t K, int64_t kalign, int64_t elem, const void *A,
              const void *B, const void *C, const float *C_f32)
 {
     if (M < 0 || N < 0 || K < 0)
         return HKG_ERR_SHAPE;
-    if (M % kTile || N % kTile || K % kstep)
+    if (K % kalign)
         return HKG_ERR_SHAPE;
     if (M == 0 || N == 0)
         return HKG_OK;
@@ -65,8 +69,8 @@ int validate(int64_t M, int64_t N, int64_t K, int64_t kstep, int64_t elem, const
     // 32-bit byte range, and tile counts / element offsets use 32-bit ints.
     if (kTile * K * elem >= (int64_t(1) << 31))
         return HKG_ERR_SIZE;
-    if ((M / kTile) * (N / kTile) >= (int64_t(1) << 30) || M >= (int64_t(1) << 31) ||
-        N >= (int64_t(1) << 31))
+    if (ceil_div(M, kTile) * ceil_div(N, kTile) >= (int64_t(1) << 30) ||
+        M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31))
         return HKG_ERR_SIZE;
     return HKG_OK;
 }
@@ -116,11 +120,12 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
          float sb, void *C, float *C_f32, void *stream, const hkg_gemm_opts *opts)
 {
     const int64_t kstep = dt == hkg::kBf16 ? kKStepBf16 : kKStepFp8;
+    const int64_t kalign = dt == hkg::kBf16 ? kKAlignBf16 : kKAlignFp8;
     const int64_t elem = dt == hkg::kBf16 ? 2 : 1;
-    int rc = validate(M, N, K, kstep, elem, A, B, C, C_f32);
+    int rc = validate(M, N, K, kalign, elem, A, B, C, C_f32);
     if (rc != HKG_OK)
         return rc;
-    const int64_t Gm = M / kTile, Gn = N / kTile;
+    const int64_t Gm = ceil_div(M, kTile), Gn = ceil_div(N, kTile);
     int32_t W = 1, Cc = 1;
     hkg::Schedule sched = hkg::kPingPong;
     if (Gm > 0 && Gn > 0) {
@@ -146,7 +151,7 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
     p.Gn = static_cast<int>(Gn);
     p.W = W;
     p.Cc = Cc;
-    p.nk = static_cast<int>(K / kstep);
+    p.nk = static_cast<int>(ceil_div(K, kstep));
     // The product of the two per-tensor scales, rounded once to fp32.
     p.scale = dt == hkg::kBf16 ? 1.0f : static_cast<float>(static_cast<double>(sa) * sb);
 
@@ -191,11 +196,10 @@ int hkg_default_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *W
 {
     if (!W || !C)
         return HKG_ERR_NULL;
-    const int64_t kstep = dtype == 0 ? kKStepBf16 : kKStepFp8;
-    if ((dtype != 0 && dtype != 1) || M <= 0 || N <= 0 || K < 0 || M % kTile || N % kTile ||
-        K % kstep)
+    const int64_t kalign = dtype == 0 ? kKAlignBf16 : kKAlignFp8;
+    if ((dtype != 0 && dtype != 1) || M <= 0 || N <= 0 || K < 0 || K % kalign)
         return HKG_ERR_SHAPE;
-    default_remap(M / kTile, N / kTile, W, C);
+    default_remap(ceil_div(M, kTile), ceil_div(N, kTile), W, C);
     return HKG_OK;
 }
 
@@ -243,7 +247,7 @@ const char *hkg_status_string(int status)
     switch (status) {
     case HKG_OK: return "ok";
     case HKG_ERR_NULL: return "a required pointer is NULL";
-    case HKG_ERR_SHAPE: return "unsupported shape (M, N multiples of 256; K of the K step)";
+    case HKG_ERR_SHAPE: return "unsupported shape (negative, or K not a multiple of 8 bf16 / 16 e4m3)";
     case HKG_ERR_ALIGN: return "pointer not 16-byte aligned";
     case HKG_ERR_SIZE: return "operand panel exceeds the 32-bit buffer range";
     case HKG_ERR_OPTS: return "invalid hkg_gemm_opts";

@@ -13,7 +13,7 @@
  * Launch shape (same note, section 3 "Launch config" and section 8 "Launch
  * shape"): one 512-thread workgroup (8 waves) per 256 x 256 output tile, a
  * flat grid of ceil(M/256) * ceil(N/256) workgroups, K consumed 64 (bf16) or
- * 128 (e4m3) at a time.  Workgroup ids are remapped to tiles by the
+ * 128 (e4m3) at a time; rows past M or N and K past the end read as zeros.  Workgroup ids are remapped to tiles by the
  * chiplet-aware schedule of the same note, section 2 (Pillar 3) / section 7
  * (Algorithm 1), with window height W and per-XCD chunk C.
  *
@@ -41,7 +41,7 @@ extern "C" {
 typedef enum {
     HKG_OK = 0,
     HKG_ERR_NULL = -1,    /* a required pointer is NULL                              */
-    HKG_ERR_SHAPE = -2,   /* M, N, K negative or not a multiple of the tile/K step   */
+    HKG_ERR_SHAPE = -2,   /* M, N, K negative, or K not a multiple of 8 (bf16) / 16 (e4m3) */
     HKG_ERR_ALIGN = -3,   /* a pointer is not 16-byte aligned                        */
     HKG_ERR_SIZE = -4,    /* a per-tile operand panel exceeds the 32-bit buffer range */
     HKG_ERR_OPTS = -5,    /* invalid hkg_gemm_opts                                   */
@@ -79,8 +79,10 @@ typedef struct {
  *          with round-to-nearest-even from the fp32 accumulator
  *   C_f32  NULL, or [M][N] fp32 row-major: the pre-rounding accumulator
  *          (validation launches only; costs extra stores)
- * Shapes: M % 256 == 0, N % 256 == 0, K % 64 == 0 (K == 0 writes zeros;
- * M == 0 or N == 0 is a no-op).  C must not overlap A or B.
+ * Shapes: any M, N >= 0; K >= 0 with K % 8 == 0 so operand rows stay 16-byte
+ * aligned (K == 0 writes zeros; M == 0 or N == 0 is a no-op).  Edge tiles
+ * (M or N not multiples of 256, K not a multiple of 64) are handled inside the
+ * kernels.  C must not overlap A or B.
  */
 int hkg_gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                   void *C, float *C_f32, void *stream);
@@ -91,7 +93,7 @@ int hkg_gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
  *   scale_a, scale_b: host fp32 per-tensor dequantisation scales
  *   C [M][N] bfloat16 = RNE(fp32(scale_a*scale_b) * fp32 accumulator)
  *   C_f32: NULL or the scaled fp32 value before rounding
- * Shapes: M % 256 == 0, N % 256 == 0, K % 128 == 0.  Otherwise as above.
+ * Shapes: any M, N >= 0; K >= 0 with K % 16 == 0.  Otherwise as above.
  */
 int hkg_gemm_fp8(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                  float scale_a, float scale_b, void *C, float *C_f32, void *stream);

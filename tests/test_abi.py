@@ -36,13 +36,16 @@ def test_status_strings():
 FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation
 
 
-@pytest.mark.parametrize("M,N,K", [(-256, 256, 64), (255, 256, 64), (256, 257, 64), (256, 256, 63)])
+@pytest.mark.parametrize("M,N,K", [(-256, 256, 64), (256, -1, 64), (256, 256, -8), (256, 256, 63),
+                                   (300, 100, 4), (1, 1, 12)])
 def test_bad_shapes_rejected(M, N, K):
+    # any M, N >= 0 is accepted; K must be a multiple of 8 (16-byte operand rows)
     assert hkg.hkg_gemm_bf16(M, N, K, FAKE, FAKE, FAKE, None, None) == hkg.HKG_ERR_SHAPE
 
 
-def test_fp8_needs_k_multiple_of_128():
-    assert hkg.hkg_gemm_fp8(256, 256, 64, FAKE, FAKE, 1.0, 1.0, FAKE, None, None) == hkg.HKG_ERR_SHAPE
+def test_fp8_needs_k_multiple_of_16():
+    for K in (8, 72, 100):
+        assert hkg.hkg_gemm_fp8(256, 256, K, FAKE, FAKE, 1.0, 1.0, FAKE, None, None) == hkg.HKG_ERR_SHAPE
 
 
 def test_null_and_alignment_rejected():
@@ -98,7 +101,10 @@ def test_remap_rejects_bad_arguments():
 
 def test_default_remap():
     rc, W, C = hkg.hkg_default_remap(8192, 8192, 8192, 0)
-    assert rc == hkg.HKG_OK and 1 <= W <= 32 and C >= 1
+    assert rc == hkg.HKG_OK and (W, C) == (8, 32)
     assert hkg.hkg_default_remap(8192, 8192, 8192, 2)[0] == hkg.HKG_ERR_SHAPE
+    assert hkg.hkg_default_remap(8192, 8192, 8190, 0)[0] == hkg.HKG_ERR_SHAPE
     rc, W, C = hkg.hkg_default_remap(256, 256, 256, 1)
     assert rc == hkg.HKG_OK and (W, C) == (1, 1)
+    rc, W, C = hkg.hkg_default_remap(300, 9000, 64, 0)     # ragged: 2 x 36 tiles
+    assert rc == hkg.HKG_OK and (W, C) == (2, 10)

@@ -309,3 +309,86 @@ def test_full_size_workload_sampled_parity(idx):
         ref = oracle.gemm_fp8_pairs(A, B, sa, sb, pm, pn)
     info = check(ref, cf, cb, w.K, w.name)
     _say("full-size %s: %s" % (w.name, info))
+
+
+# ---------------------------------------------------------------- ragged shapes ----
+
+RAGGED_BF16 = [(1, 1, 8), (17, 33, 72), (255, 257, 200), (300, 520, 136), (513, 777, 1000)]
+RAGGED_FP8 = [(1, 1, 16), (130, 250, 144), (513, 300, 272), (257, 1000, 1040)]
+
+
+@pytest.mark.parametrize("sched", SCHEDULES)
+@pytest.mark.parametrize("M,N,K", RAGGED_BF16)
+def test_bf16_ragged_integers_bit_exact(M, N, K, sched):
+    _say("bf16 ragged ints %dx%dx%d sched=%d" % (M, N, K, sched))
+    A = synth.small_int_bf16(9600 + M + K, M, K)
+    B = synth.small_int_bf16(9700 + N + K, N, K)
+    cb, cf = run_bf16(A, B, opts=hkg.make_opts(schedule=sched))
+    want = (bf16_to_f64(A).astype(np.int64) @ bf16_to_f64(B).astype(np.int64).T).astype(np.float64)
+    np.testing.assert_array_equal(cf.astype(np.float64), want)
+    np.testing.assert_array_equal(cb, oracle.bf16_round(want))
+
+
+@pytest.mark.parametrize("sched", SCHEDULES)
+@pytest.mark.parametrize("M,N,K", RAGGED_FP8)
+def test_fp8_ragged_integers_bit_exact(M, N, K, sched):
+    _say("fp8 ragged ints %dx%dx%d sched=%d" % (M, N, K, sched))
+    A = synth.small_int_e4m3(9800 + M + K, M, K)
+    B = synth.small_int_e4m3(9900 + N + K, N, K)
+    cb, cf = run_fp8(A, B, 1.0, 1.0, opts=hkg.make_opts(schedule=sched))
+    tab = oracle.e4m3_table()
+    want = (tab[A].astype(np.int64) @ tab[B].astype(np.int64).T).astype(np.float64)
+    np.testing.assert_array_equal(cf.astype(np.float64), want)
+    np.testing.assert_array_equal(cb, oracle.bf16_round(want))
+
+
+@pytest.mark.parametrize("M,N,K", [(700, 900, 1000), (1000, 777, 520)])
+def test_bf16_ragged_random_matches_oracle(M, N, K):
+    _say("bf16 ragged random %dx%dx%d" % (M, N, K))
+    A = synth.f32_to_bf16_bits(synth.normal_f32(9610 + K, M, K))
+    B = synth.f32_to_bf16_bits(synth.normal_f32(9710 + K, N, K))
+    cb, cf = run_bf16(A, B)
+    check(oracle.gemm_bf16(A, B), cf, cb, K, "bf16 ragged %dx%dx%d" % (M, N, K))
+
+
+def test_fp8_ragged_random_matches_oracle():
+    M, N, K = 700, 900, 1040
+    _say("fp8 ragged random %dx%dx%d" % (M, N, K))
+    A, sa = synth.e4m3_quantize(synth.normal_f32(9810, M, K))
+    B, sb = synth.e4m3_quantize(synth.normal_f32(9910, N, K))
+    cb, cf = run_fp8(A, B, sa, sb)
+    check(oracle.gemm_fp8(A, B, sa, sb), cf, cb, K, "fp8 ragged")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 260, 72), (257, 1, 8), (1, 513, 1000)])
+def test_ragged_no_stray_writes(M, N, K):
+    _say("ragged canary %dx%dx%d" % (M, N, K))
+    A = _dev_bf16(synth.f32_to_bf16_bits(synth.normal_f32(9980, M, K)))
+    B = _dev_bf16(synth.f32_to_bf16_bits(synth.normal_f32(9981, N, K)))
+    pad = 4096
+    buf = torch.full((M * N + 2 * pad,), 12345, dtype=torch.int16, device="cuda")
+    C = buf[pad:pad + M * N].view(torch.bfloat16).view(M, N)
+    fbuf = torch.full((M * N + 2 * pad,), -7.0, dtype=torch.float32, device="cuda")
+    Cf = fbuf[pad:pad + M * N].view(M, N)
+    hkg.gemm_bf16(A, B, C, Cf)
+    torch.cuda.synchronize()
+    assert (buf[:pad] == 12345).all() and (buf[pad + M * N:] == 12345).all()
+    assert (fbuf[:pad] == -7.0).all() and (fbuf[pad + M * N:] == -7.0).all()
+    assert torch.equal(Cf.to(torch.bfloat16).view(torch.int16), C.view(torch.int16))
+
+
+def test_large_ragged_sampled_parity():
+    M, N, K = 5000, 3000, 2056
+    _say("large ragged %dx%dx%d" % (M, N, K))
+    A = synth.f32_to_bf16_bits(synth.normal_f32(9990, M, K))
+    B = synth.f32_to_bf16_bits(synth.normal_f32(9991, N, K))
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    Cf = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    hkg.gemm_bf16(_dev_bf16(A), _dev_bf16(B), C, Cf)
+    torch.cuda.synchronize()
+    assert torch.equal(Cf.to(torch.bfloat16).view(torch.int16), C.view(torch.int16))
+    pm, pn = synth.sample_pairs(9992, M, N, 30000)
+    ipm, ipn = torch.from_numpy(pm).cuda(), torch.from_numpy(pn).cuda()
+    cf = Cf[ipm, ipn].cpu().numpy()
+    cb = C.view(torch.int16)[ipm, ipn].cpu().numpy().view(np.uint16)
+    check(oracle.gemm_bf16_pairs(A, B, pm, pn), cf, cb, K, "large ragged")
