@@ -8,7 +8,7 @@ throughput (TFLOPS), the MFMA roofline of the kernel (live HIP-event timing),
 and the CPU oracle timed on a bounded sample as a baseline.
 
   python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload 2]
-                  [--all] [--remap W,C | --row-major] [--schedule pingpong|lockstep]
+                  [--all] [--remap W,C | --row-major] [--schedule interleave|pingpong|lockstep]
                   [--no-cpu-baseline]
   python bench.py --sweep "1,1 8,32 5,25 ..." [--workload N | --shape M,N,K --dtype bf16|fp8]
         grid-order sweep: one JSON line per (W, C) on the same resident inputs
@@ -64,6 +64,8 @@ def algorithmic_bytes(w: synth.Workload) -> int:
 
 
 def kernel_name(dtype: str, schedule: str) -> str:
+    if schedule == "interleave":
+        return "gemm4_kernel<%s>" % dtype
     return "gemm_kernel<%s,%s>" % (dtype, schedule)
 
 
@@ -228,8 +230,11 @@ def sweep(w: synth.Workload, pairs, steps: int, warmup: int) -> None:
     stream = torch.cuda.current_stream(dev)
     rc, dW, dC = hkg.hkg_default_remap(w.M, w.N, w.K, 0 if w.dtype == "bf16" else 1)
 
-    def run(W, Cc, n):
-        opts = hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=W, C=Cc)
+    scheds = {"p": hkg.HKG_SCHED_PINGPONG, "l": hkg.HKG_SCHED_LOCKSTEP,
+              "i": hkg.HKG_SCHED_INTERLEAVE}
+
+    def run(W, Cc, n, sc="i"):
+        opts = hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=W, C=Cc, schedule=scheds[sc])
         for _ in range(n):
             if w.dtype == "bf16":
                 hkg.gemm_bf16(dA, dB, C, opts=opts, stream=stream)
@@ -248,18 +253,20 @@ def sweep(w: synth.Workload, pairs, steps: int, warmup: int) -> None:
     torch.cuda.synchronize()
     times = {p: [] for p in pairs}
     for order in (list(pairs), list(reversed(pairs))):   # forward then reverse
-        for (W, Cc) in order:
-            run(W, Cc, warmup)
+        for key in order:
+            run(*key[:2], warmup, *key[2:])
             e0.record(stream)
-            run(W, Cc, steps)
+            run(*key[:2], steps, *key[2:])
             e1.record(stream)
             torch.cuda.synchronize()
-            times[(W, Cc)].append(e0.elapsed_time(e1) / steps)
-    for (W, Cc) in pairs:
-        ms = float(np.mean(times[(W, Cc)]))
+            times[key].append(e0.elapsed_time(e1) / steps)
+    for key in pairs:
+        W, Cc = key[:2]
+        ms = float(np.mean(times[key]))
         print(json.dumps({"sweep": w.name, "M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype,
-                          "W": W, "C": Cc, "default": [W, Cc] == [dW, dC],
-                          "ms": round(ms, 5), "ms_runs": [round(t, 5) for t in times[(W, Cc)]],
+                          "W": W, "C": Cc, "schedule": key[2] if len(key) > 2 else "i",
+                          "default": [W, Cc] == [dW, dC],
+                          "ms": round(ms, 5), "ms_runs": [round(t, 5) for t in times[key]],
                           "TFLOPS": round(w.flops / (ms * 1e-3) / 1e12, 2)}), flush=True)
 
 
@@ -272,7 +279,8 @@ def main(argv=None) -> int:
     ap.add_argument("--all", action="store_true", help="one line per workload 1..5")
     ap.add_argument("--remap", type=str, default=None, help="W,C for the XCD remap")
     ap.add_argument("--row-major", action="store_true")
-    ap.add_argument("--schedule", choices=["pingpong", "lockstep"], default="pingpong")
+    ap.add_argument("--schedule", choices=["interleave", "pingpong", "lockstep"],
+                    default="interleave", help="in-CU schedule (default: the library's, interleave)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shape", type=str, default=None, help="M,N,K (custom size)")
     ap.add_argument("--dtype", choices=["bf16", "fp8"], default="bf16")
@@ -286,19 +294,21 @@ def main(argv=None) -> int:
 
     import dense_gemm_fp8_amd as hkg
     hkg.load()
-    sched = hkg.HKG_SCHED_PINGPONG if args.schedule == "pingpong" else hkg.HKG_SCHED_LOCKSTEP
+    sched = {"pingpong": hkg.HKG_SCHED_PINGPONG, "lockstep": hkg.HKG_SCHED_LOCKSTEP,
+             "interleave": hkg.HKG_SCHED_INTERLEAVE}[args.schedule]
     opts = None
     if args.row_major:
         opts = hkg.make_opts(remap=hkg.HKG_REMAP_ROW_MAJOR, schedule=sched)
     elif args.remap:
         W, C = (int(v) for v in args.remap.split(","))
         opts = hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=W, C=C, schedule=sched)
-    elif sched != hkg.HKG_SCHED_PINGPONG:
+    elif sched != hkg.HKG_SCHED_INTERLEAVE:
         opts = hkg.make_opts(schedule=sched)
 
     if args.sweep:
         w = custom_workload(args.shape, args.dtype) if args.shape else synth.workload(args.workload)
-        pairs = [tuple(int(v) for v in item.split(",")) for item in args.sweep.split()]
+        pairs = [tuple(int(v) if v.isdigit() else v for v in item.split(","))
+                 for item in args.sweep.split()]
         sweep(w, pairs, args.steps, args.warmup)
         return 0
     ids = [1, 2, 3, 4, 5] if args.all else [args.workload]

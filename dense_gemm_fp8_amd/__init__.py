@@ -37,6 +37,7 @@ HKG_REMAP_XCD = 2
 HKG_SCHED_DEFAULT = 0
 HKG_SCHED_PINGPONG = 1
 HKG_SCHED_LOCKSTEP = 2
+HKG_SCHED_INTERLEAVE = 3
 
 # exported symbols, in the order include/hkg.h declares them
 EXPORTS = (

@@ -2,6 +2,7 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 
@@ -28,14 +29,47 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
+# The compiler's per-kernel resource report (registers, scratch, spills).
+RESOURCE_REMARKS = "-Rpass-analysis=kernel-resource-usage"
+
+
+def scratch_users(report: str) -> list[tuple[str, str, int]]:
+    """(kernel, item, value) for every kernel that the report shows using
+    scratch memory or spilling registers.  The GEMM kernels keep their whole
+    accumulator tile in registers; if the compiler ever demotes it to scratch
+    the kernel still computes the right answer, only 10-60x slower, so the
+    build treats that as an error."""
+    bad, fn = [], None
+    for line in report.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            fn = m.group(1)
+            continue
+        m = re.search(r"remark:\s+(ScratchSize \[bytes/lane\]|VGPRs Spill|SGPRs Spill): (\d+)", line)
+        if m and fn and int(m.group(2)) > 0:
+            bad.append((fn, m.group(1), int(m.group(2))))
+    return bad
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
-    """Compile every source into dense_gemm_fp8_amd/libhkg.so (always rebuilds)."""
+    """Compile every source into dense_gemm_fp8_amd/libhkg.so (always rebuilds);
+    fails if a kernel uses scratch memory or spills registers."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), "-shared", "-x", "hip", *SOURCES,
-           "-I", os.path.join(ROOT, "include"), "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, RESOURCE_REMARKS, *(extra or []), "-shared", "-x", "hip",
+           *SOURCES, "-I", os.path.join(ROOT, "include"), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    other = [ln for ln in res.stderr.splitlines()
+             if "kernel-resource-usage" not in ln and "packed-fp32-ops" not in ln]
+    if other and (verbose or res.returncode != 0):
+        print("\n".join(other), file=sys.stderr, flush=True)
+    if res.returncode != 0:
+        raise subprocess.CalledProcessError(res.returncode, cmd)
+    bad = scratch_users(res.stderr)
+    if bad:
+        os.unlink(tmp)
+        raise RuntimeError("kernels using scratch memory: %s" % bad)
     os.replace(tmp, LIB)
     return LIB
 

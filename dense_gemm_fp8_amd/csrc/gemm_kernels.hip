@@ -1,8 +1,12 @@
 // gemm_kernels.hip -- gfx950 (MI355X) kernels for C = A * B^T.
 //
-// One 512-thread workgroup (8 waves of 64 lanes) computes one 256 x 256 output
-// tile (HipKittens L2 note, section 3 "Launch config": BLOCK 256 x 256,
-// K_STEP 64, WARPS_M = 2, WARPS_N = 4, DOT_SLICE 32, MFMA 16x16x32).
+// One workgroup computes one 256 x 256 output tile (HipKittens L2 note,
+// section 3 "Launch config": BLOCK 256 x 256, K_STEP 64, DOT_SLICE 32, MFMA
+// 16x16x32).  Two kernels share the data path and the LDS ring below:
+//   gemm_kernel   512 threads, 8 waves as WARPS_M = 2 x WARPS_N = 4 (the
+//                 ping-pong and lockstep schedules)
+//   gemm4_kernel  256 threads, 4 waves of 128 x 128 each (the 4-wave
+//                 interleave, the library's default; see its section below)
 //
 // Data path of one K step:
 //   HBM/L2 --buffer_load_dwordx4 ... lds--> LDS stage --ds_read_b128--> VGPR
@@ -323,16 +327,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Write the wave's 128 x 64 sub-tile: per 16-row block i a lane owns output
-// row m = 16 i + (lane % 16) and columns 8 q .. 8 q + 7 and 32 + 8 q .. + 7.
+// Write a wave's 128-row sub-tile of kCols / 16 column blocks, whose top-left
+// corner is (row_off, col_off) inside the tile: per 16-row block i a lane owns
+// output row m = 16 i + (lane % 16) and, per 32-column group h, columns
+// 32 h + 8 q .. 32 h + 8 q + 7 (blocks 2 h and 2 h + 1, interleaved as above).
 // Tiles inside M x N with N % 8 == 0 use 16-byte stores; edge tiles store
 // only rows < M and columns < N (element by element when N % 8 != 0).
-__device__ __forceinline__ void store_tile(const GemmParams &p, int tm, int tn, int g, int wn,
-                                           int lane, f32x4 (&acc)[8][4])
+template <int kBlocks>
+__device__ __forceinline__ void store_tile(const GemmParams &p, int tm, int tn, int row_off,
+                                           int col_off, int lane, f32x4 (&acc)[8][kBlocks])
 {
     const int q = lane >> 4;
-    const int64_t row0 = (int64_t)tm * kTile + 128 * g + (lane & 15);
-    const int64_t col0 = (int64_t)tn * kTile + 64 * wn + 8 * q;
+    const int64_t row0 = (int64_t)tm * kTile + row_off + (lane & 15);
+    const int64_t col0 = (int64_t)tn * kTile + col_off + 8 * q;
     const float sc = p.scale;
     uint16_t *C = static_cast<uint16_t *>(p.C);
     const bool vec = (p.N & 7) == 0;
@@ -343,7 +350,7 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, int tm, int tn, 
         if (!inside && m >= p.M)
             continue;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < kBlocks / 2; ++h) {
             const f32x4 lo = acc[i][2 * h] * sc;
             const f32x4 hi = acc[i][2 * h + 1] * sc;
             const int64_t n0 = col0 + 32 * h;
@@ -556,7 +563,311 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
             }
         }
     }
-    store_tile(p, tm, tn, g, wn, lane, acc);
+    store_tile<4>(p, tm, tn, 128 * g, 64 * wn, lane, acc);
+}
+
+// ---- 4-wave interleave (one wave per SIMD) --------------------------------
+// HipKittens L2 note, section 9.1 / summary page "4-wave interleave": each
+// wave issues its own loads and LDS reads between its MFMAs.  Wave w owns the
+// 128 x 128 quarter (wm, wn) = (w >> 1, w & 1) of the tile: 8 x 8 blocks of
+// 16 x 16, i.e. 256 fp32 accumulators per lane, which fit next to the
+// fragments only because a single wave per SIMD has the whole register file.
+// Per K step a wave reads 16 fragments of 128 rows of A and B each, a third
+// fewer LDS bytes per CU than the 8-wave split (8 x 4 blocks per wave).
+//
+// A K step is two halves of MFMAs with one barrier between them; all four
+// waves run the same program:
+//   half 0 of step t: the first half of the MFMAs; the loads of B(t+2) into
+//                     B panel (t+2) % 3; fragment reads that complete step t
+//   barrier:          every wave waited for its own loads of step t+1 and
+//                     has its reads of A panel t % 2 back in registers
+//   half 1 of step t: the second half of the MFMAs; the loads of A(t+2) into
+//                     A panel t % 2; fragment reads that begin step t+1
+// Each memory instruction is slotted after a given MFMA (sched_barrier after
+// every slot), so the matrix core is fed by one MFMA after another while the
+// loads and reads issue in its shadow.  The loop body is the same for every
+// t: loads of K steps >= nk are out of range and write zeros into panels no
+// one reads any more, and the reads of "step nk" in the last half are unused.
+// ---- 4-wave layout ----------------------------------------------------------
+// The A and B panels of the 4-wave kernel use one XOR swizzle each instead of
+// the shared slot_xor: the A fragment reads vary row bits 1,2,3 within a
+// 16-lane group and B's interleaved reads bits 1,3,4 (plus the row parity
+// bit 0, which selects the bank half), so
+//   A: slot = chunk ^ (b1 | b3 << 1 | b2 << 2)   (independent of row bit 4)
+//   B: slot = chunk ^ (b1 | b3 << 1 | b4 << 2)   (independent of row bit 2)
+// are bank-conflict free, and the two row parities of a fragment pair (A
+// rows 16 apart, B rows 4 apart) lie a constant 2048 / 512 bytes apart, so
+// one lane base per operand and chunk half serves every block.
+__device__ __forceinline__ int slot_xor_a(int r)
+{
+    return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2);
+}
+__device__ __forceinline__ int slot_xor_b(int r)
+{
+    return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 4) & 1) << 2);
+}
+
+// Lane part of a fragment read, chunk half h (q or 4 + q): A row x, B row
+// (x & 3) + 8 (x >> 2) of a block pair, x = lane % 16, q = lane / 16.
+struct QuadLane {
+    int a[2], b[2];
+};
+__device__ __forceinline__ QuadLane quad_lane(int lane)
+{
+    const int x = lane & 15, q = lane >> 4;
+    const int rb = (x & 3) + 8 * (x >> 2);
+    QuadLane l;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        l.a[h] = x * kRowBytes + (((4 * h + q) ^ slot_xor_a(x)) << 4);
+        l.b[h] = rb * kRowBytes + (((4 * h + q) ^ slot_xor_b(rb)) << 4);
+    }
+    return l;
+}
+// Offsets of A fragment i (rows 16 i ..) and B fragment j (rows 32 (j >> 1)
+// + 4 (j & 1) + interleave) from the lane's base.
+__device__ __forceinline__ constexpr int qa_blk(int i) { return 16 * i * kRowBytes; }
+__device__ __forceinline__ constexpr int qb_blk(int j) { return (32 * (j >> 1) + 4 * (j & 1)) * kRowBytes; }
+
+// An empty asm that claims to change x.  Applied to the lane base address of
+// a half, it stops the optimiser from folding a panel's offset into a
+// separate precomputed address per fragment read (one register each, and one
+// vector add each per K step): every read stays one ds_read of
+// (base + constant block offset).
+__device__ __forceinline__ int opaque(int x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+template <int kDtype>
+struct Quad;
+
+template <>
+struct Quad<kBf16> {
+    // half h runs DOT_SLICE h of all 64 blocks (i-major); half 0 reads slice 1
+    // of step t, half 1 reads slice 0 of step t+1 (B fragments 0..7 first,
+    // then A fragments 0..7: the order the next half's MFMAs need them).
+    using F = Frag<kBf16>;
+    struct Frags {
+        bf16x8 a[2][8], b[2][8];   // [slice][block]
+    };
+    static constexpr int kMfmas = 64;   // per half
+    // the MFMA after which load v (0..7) / fragment read r (0..15) issues
+    __device__ static constexpr int dma_slot(int v) { return 8 * v + 4; }
+    __device__ static constexpr int read_slot(int r) { return 3 * r; }
+
+    __device__ __forceinline__ static void read_first(Frags &f, const char *smem,
+                                                      const QuadLane &l, int a_off, int b_off)
+    {
+        const int ba = opaque(l.a[0] + a_off), bb = opaque(l.b[0] + b_off);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            f.b[0][j] = *reinterpret_cast<const bf16x8 *>(smem + qb_blk(j) + bb);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            f.a[0][i] = *reinterpret_cast<const bf16x8 *>(smem + qa_blk(i) + ba);
+    }
+    // a_off / b_off: LDS bytes of the wave's rows of the panels this half
+    // reads from; dma(v) issues the half's load v.
+    template <int kH, class Dma>
+    __device__ __forceinline__ static void half(Frags &f, f32x4 (&acc)[8][8], const char *smem,
+                                                const QuadLane &l, int a_off, int b_off, Dma &&dma)
+    {
+        constexpr int s = 1 - kH;
+        const int ba = opaque(l.a[s] + a_off), bb = opaque(l.b[s] + b_off);
+#pragma unroll
+        for (int n = 0; n < kMfmas; ++n) {
+            const int i = n >> 3, j = n & 7;
+            acc[i][j] = F::mma(f.b[kH][j], f.a[kH][i], acc[i][j]);
+#pragma unroll
+            for (int v = 0; v < 8; ++v)
+                if (dma_slot(v) == n)
+                    dma(v);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (read_slot(r) != n)
+                    continue;
+                if (r < 8)
+                    f.b[s][r] = *reinterpret_cast<const bf16x8 *>(smem + qb_blk(r) + bb);
+                else
+                    f.a[s][r - 8] = *reinterpret_cast<const bf16x8 *>(smem + qa_blk(r - 8) + ba);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+};
+
+template <>
+struct Quad<kFp8> {
+    // half 0 runs blocks (i, j < 4), half 1 blocks (i, j >= 4), both i-major.
+    // Half 0 reads B fragments 4..7 of step t; half 1 reads B fragments 0..3
+    // of step t+1 and A fragment i of step t+1 right after the last MFMA
+    // that uses A fragment i of step t, so one K step of fragments (128
+    // registers) is all a wave holds.  A fragment is two 16-byte chunks
+    // (halves h = 0, 1).
+    using F = Frag<kFp8>;
+    struct Frags {
+        i32x8 a[8], b[8];
+    };
+    static constexpr int kMfmas = 32;   // per half
+    __device__ static constexpr int dma_slot(int v) { return 4 * v + 1; }
+    // B fragment 4 + r (half 0) or r (half 1)
+    __device__ static constexpr int b_read_slot(int h, int r) { return h == 0 ? 4 * r + 2 : r; }
+
+    __device__ __forceinline__ static i32x8 frag(const char *smem, int blk, int base0, int base1)
+    {
+        const i32x4 lo = *reinterpret_cast<const i32x4 *>(smem + blk + base0);
+        const i32x4 hi = *reinterpret_cast<const i32x4 *>(smem + blk + base1);
+        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    __device__ __forceinline__ static void read_first(Frags &f, const char *smem,
+                                                      const QuadLane &l, int a_off, int b_off)
+    {
+        const int ba0 = opaque(l.a[0] + a_off), ba1 = opaque(l.a[1] + a_off);
+        const int bb0 = opaque(l.b[0] + b_off), bb1 = opaque(l.b[1] + b_off);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            f.b[j] = frag(smem, qb_blk(j), bb0, bb1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            f.a[i] = frag(smem, qa_blk(i), ba0, ba1);
+    }
+    template <int kH, class Dma>
+    __device__ __forceinline__ static void half(Frags &f, f32x4 (&acc)[8][8], const char *smem,
+                                                const QuadLane &l, int a_off, int b_off, Dma &&dma)
+    {
+        int ba0 = 0, ba1 = 0;
+        if (kH == 1)
+            ba0 = opaque(l.a[0] + a_off), ba1 = opaque(l.a[1] + a_off);
+        const int bb0 = opaque(l.b[0] + b_off), bb1 = opaque(l.b[1] + b_off);
+#pragma unroll
+        for (int n = 0; n < kMfmas; ++n) {
+            const int i = n >> 2, j = 4 * kH + (n & 3);
+            acc[i][j] = F::mma(f.b[j], f.a[i], acc[i][j]);
+#pragma unroll
+            for (int v = 0; v < 8; ++v)
+                if (dma_slot(v) == n)
+                    dma(v);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (b_read_slot(kH, r) != n)
+                    continue;
+                const int jb = 4 * (1 - kH) + r;
+                f.b[jb] = frag(smem, qb_blk(jb), bb0, bb1);
+            }
+            if (kH == 1 && (n & 3) == 3)
+                f.a[i] = frag(smem, qa_blk(i), ba0, ba1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+};
+
+// every memory instruction of a half has an MFMA to follow
+static_assert(Quad<kBf16>::dma_slot(7) < Quad<kBf16>::kMfmas &&
+                  Quad<kBf16>::read_slot(15) < Quad<kBf16>::kMfmas, "bf16 slot plan");
+static_assert(Quad<kFp8>::dma_slot(7) < Quad<kFp8>::kMfmas &&
+                  Quad<kFp8>::b_read_slot(0, 3) < Quad<kFp8>::kMfmas, "e4m3 slot plan");
+
+// What the 4-wave loop of one workgroup works on.
+struct QuadCtx {
+    __amdgpu_buffer_rsrc_t ra, rb;   // this tile's A and B rows
+    char *smem;
+    int wave;                        // 0..3, also the row group phase of its loads
+    int a_rows, b_rows;              // LDS bytes of the wave's rows in an A / B panel 0
+    int voff_a, voff_b;              // lane's load offsets (swizzled chunk of its row)
+    int cb_a, cb_b;                  // byte of that chunk inside a K step
+    QuadLane l;
+};
+
+// K step t: the loads it issues are of step t+2; kMasked: that step may be a
+// partial or absent one (lanes whose chunk lies past K load zeros).
+template <int kDtype, bool kMasked>
+__device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4 (&acc)[8][8],
+                                          const QuadCtx &c, int ldk, int t)
+{
+    using Q = Quad<kDtype>;
+    const int k2 = t + 2;
+    const int va = kMasked ? kstep_voff(c.voff_a, c.cb_a, k2, ldk) : c.voff_a;
+    const int vb = kMasked ? kstep_voff(c.voff_b, c.cb_b, k2, ldk) : c.voff_b;
+    // (readfirstlane keeps loop strength reduction from deriving this scalar
+    // offset from the lane's k2 * 128 + chunk byte)
+    const int so = __builtin_amdgcn_readfirstlane(k2 * kRowBytes);
+    const int pa = (t & 1) * kPanelBytes, pa1 = kPanelBytes - pa;
+    const int m3 = t % kBPanels;
+    const int pb = m3 * kPanelBytes;
+    const int pb1 = (m3 == 2 ? 0 : m3 + 1) * kPanelBytes;
+    const int pb2 = (m3 == 0 ? 2 : m3 - 1) * kPanelBytes;
+    char *const a_dst = c.smem + pa;
+    char *const b_dst = c.smem + kBRing + pb2;
+    __builtin_amdgcn_sched_barrier(0);
+    Q::template half<0>(f, acc, c.smem, c.l, c.a_rows + pa, c.b_rows + pb,
+                        [&](int v) { dma_rows(c.rb, b_dst, c.wave + 4 * v, vb, so, ldk); });
+    wait_lgkmcnt0();
+    wait_vmcnt<8>();                               // step t+1 landed (B(t+2) in flight)
+    block_barrier();
+    Q::template half<1>(f, acc, c.smem, c.l, c.a_rows + pa1, c.b_rows + pb1,
+                        [&](int v) { dma_rows(c.ra, a_dst, c.wave + 4 * v, va, so, ldk); });
+}
+
+template <int kDtype>
+__global__ __launch_bounds__(256, 1) void gemm4_kernel(const GemmParams p)
+{
+    __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+
+    const int lane = threadIdx.x & 63;
+    QuadCtx c;
+    c.smem = smem;
+    c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    c.a_rows = 128 * (c.wave >> 1) * kRowBytes;            // tile rows 128 (w >> 1) ..
+    c.b_rows = kBRing + 128 * (c.wave & 1) * kRowBytes;    // tile columns 128 (w & 1) ..
+
+    int tm, tn;
+    remap_tile(blockIdx.x, p.Gm, p.Gn, p.W, p.Cc, tm, tn);
+
+    constexpr int kElem = kDtype == kBf16 ? 2 : 1;
+    const int ldk = p.K * kElem;
+    const int rows_a = min(kTile, p.M - tm * kTile);
+    const int rows_b = min(kTile, p.N - tn * kTile);
+    c.ra = make_rsrc(static_cast<const char *>(p.A) + (int64_t)tm * kTile * ldk, rows_a * ldk);
+    c.rb = make_rsrc(static_cast<const char *>(p.B) + (int64_t)tn * kTile * ldk, rows_b * ldk);
+
+    // Each wave loads row groups u = wave + 4 v (v < 8) of every panel, so
+    // row bits 3,4 equal the wave index for all its loads.
+    const int r8 = lane >> 3;
+    c.cb_a = ((lane & 7) ^ slot_xor_a(r8 | (c.wave << 3))) << 4;
+    c.cb_b = ((lane & 7) ^ slot_xor_b(r8 | (c.wave << 3))) << 4;
+    c.voff_a = r8 * ldk + c.cb_a;
+    c.voff_b = r8 * ldk + c.cb_b;
+    c.l = quad_lane(lane);
+
+    f32x4 acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    using Q = Quad<kDtype>;
+    const int nk = p.nk;
+    if (nk > 0) {
+        // K steps 0 and 1 (for nk == 1 the loads of step 1 write zeros).
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            dma_panel_part<8>(c.ra, smem + k * kPanelBytes, 0, c.wave,
+                              kstep_voff(c.voff_a, c.cb_a, k, ldk), k * kRowBytes, ldk);
+            dma_panel_part<8>(c.rb, smem + kBRing + k * kPanelBytes, 0, c.wave,
+                              kstep_voff(c.voff_b, c.cb_b, k, ldk), k * kRowBytes, ldk);
+        }
+        wait_vmcnt<16>();                          // step 0 landed
+        block_barrier();
+        typename Q::Frags f;
+        Q::read_first(f, smem, c.l, c.a_rows, c.b_rows);
+        for (int t = 0; t < nk; ++t)
+            quad_step<kDtype, true>(f, acc, c, ldk, t);
+        wait_vmcnt<0>();
+    }
+    store_tile<8>(p, tm, tn, c.a_rows / kRowBytes, (c.b_rows - kBRing) / kRowBytes, lane, acc);
 }
 
 __global__ void remap_tiles_kernel(int Gm, int Gn, int W, int C, int32_t *out)
@@ -575,7 +886,12 @@ __global__ void remap_tiles_kernel(int Gm, int Gn, int W, int C, int32_t *out)
 hipError_t launch_gemm(Dtype dt, Schedule s, const GemmParams &p, hipStream_t stream)
 {
     const dim3 grid(p.Gm * p.Gn), block(512);
-    if (dt == kBf16) {
+    if (s == kInterleave) {
+        if (dt == kBf16)
+            hipLaunchKernelGGL(gemm4_kernel<kBf16>, grid, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL(gemm4_kernel<kFp8>, grid, dim3(256), 0, stream, p);
+    } else if (dt == kBf16) {
         if (s == kPingPong)
             hipLaunchKernelGGL((gemm_kernel<kBf16, kPingPong>), grid, block, 0, stream, p);
         else

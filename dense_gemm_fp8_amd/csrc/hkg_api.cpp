@@ -79,16 +79,20 @@ int resolve_opts(const hkg_gemm_opts *opts, int64_t Gm, int64_t Gn, int32_t *W, 
                  hkg::Schedule *sched)
 {
     default_remap(Gm, Gn, W, C);
-    *sched = hkg::kPingPong;
+    *sched = hkg::kInterleave;
     if (!opts)
         return HKG_OK;
     switch (opts->schedule) {
     case HKG_SCHED_DEFAULT:
+        break;
     case HKG_SCHED_PINGPONG:
         *sched = hkg::kPingPong;
         break;
     case HKG_SCHED_LOCKSTEP:
         *sched = hkg::kLockstep;
+        break;
+    case HKG_SCHED_INTERLEAVE:
+        *sched = hkg::kInterleave;
         break;
     default:
         return HKG_ERR_OPTS;
@@ -127,13 +131,13 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
         return rc;
     const int64_t Gm = ceil_div(M, kTile), Gn = ceil_div(N, kTile);
     int32_t W = 1, Cc = 1;
-    hkg::Schedule sched = hkg::kPingPong;
+    hkg::Schedule sched = hkg::kInterleave;
     if (Gm > 0 && Gn > 0) {
         rc = resolve_opts(opts, Gm, Gn, &W, &Cc, &sched);
         if (rc != HKG_OK)
             return rc;
     } else if (opts && (opts->remap < 0 || opts->remap > 2 || opts->schedule < 0 ||
-                        opts->schedule > 2)) {
+                        opts->schedule > 3)) {
         return HKG_ERR_OPTS;
     }
     if (M == 0 || N == 0)

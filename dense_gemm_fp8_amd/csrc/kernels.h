@@ -21,7 +21,7 @@ struct GemmParams {
 };
 
 enum Dtype { kBf16 = 0, kFp8 = 1 };
-enum Schedule { kPingPong = 0, kLockstep = 1 };
+enum Schedule { kPingPong = 0, kLockstep = 1, kInterleave = 2 };
 
 hipError_t launch_gemm(Dtype dt, Schedule s, const GemmParams &p, hipStream_t stream);
 hipError_t launch_remap_tiles(int Gm, int Gn, int W, int C, int32_t *out, hipStream_t stream);

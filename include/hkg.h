@@ -11,9 +11,11 @@
  * fp32 scale per tensor and writes bf16  C = bf16(scale_a * scale_b * A*B^T).
  *
  * Launch shape (same note, section 3 "Launch config" and section 8 "Launch
- * shape"): one 512-thread workgroup (8 waves) per 256 x 256 output tile, a
- * flat grid of ceil(M/256) * ceil(N/256) workgroups, K consumed 64 (bf16) or
- * 128 (e4m3) at a time; rows past M or N and K past the end read as zeros.  Workgroup ids are remapped to tiles by the
+ * shape"): one workgroup per 256 x 256 output tile -- 256 threads (4 waves,
+ * the default 4-wave interleave) or 512 threads (8 waves, the ping-pong and
+ * lockstep schedules) -- on a flat grid of ceil(M/256) * ceil(N/256)
+ * workgroups, K consumed 64 (bf16) or 128 (e4m3) at a time; rows past M or N
+ * and K past the end read as zeros.  Workgroup ids are remapped to tiles by the
  * chiplet-aware schedule of the same note, section 2 (Pillar 3) / section 7
  * (Algorithm 1), with window height W and per-XCD chunk C.
  *
@@ -58,10 +60,13 @@ enum {
 
 /* In-CU schedule (HipKittens L2 note, section 2 Pillar 2 and section 9.2). */
 enum {
-    HKG_SCHED_DEFAULT = 0,  /* 8-wave ping-pong                                     */
+    HKG_SCHED_DEFAULT = 0,  /* 4-wave interleave (HKG_SCHED_INTERLEAVE)             */
     HKG_SCHED_PINGPONG = 1, /* 8-wave ping-pong: 2 groups of 4 waves alternate the
                                MFMA and HBM->LDS roles via s_setprio + barriers      */
-    HKG_SCHED_LOCKSTEP = 2  /* all 8 waves compute the same K step (ablation only)   */
+    HKG_SCHED_LOCKSTEP = 2, /* all 8 waves compute the same K step (ablation only)   */
+    HKG_SCHED_INTERLEAVE = 3/* 4 waves (one per SIMD), each 128 x 128 of the tile,
+                               loads and LDS reads slotted between its own MFMAs
+                               (the note's section 9.1 4-wave interleave)            */
 };
 
 typedef struct {

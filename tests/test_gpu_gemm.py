@@ -63,7 +63,8 @@ def run_fp8(A, B, sa, sb, opts=None, want_f32=True):
     return _host_bits(C), (Cf.cpu().numpy() if want_f32 else None)
 
 
-SCHEDULES = [hkg.HKG_SCHED_PINGPONG, hkg.HKG_SCHED_LOCKSTEP]
+SCHEDULES = [hkg.HKG_SCHED_PINGPONG, hkg.HKG_SCHED_LOCKSTEP, hkg.HKG_SCHED_INTERLEAVE]
+SCHED_IDS = ["pingpong", "lockstep", "interleave"]
 
 
 # ---------------------------------------------------------------- remap ------------
@@ -81,7 +82,7 @@ def test_device_remap_matches_oracle(Gm, Gn, W, C):
 
 # ---------------------------------------------------------------- exactness --------
 
-@pytest.mark.parametrize("sched", SCHEDULES)
+@pytest.mark.parametrize("sched", SCHEDULES, ids=SCHED_IDS)
 @pytest.mark.parametrize("M,N,K", [(256, 256, 64), (256, 256, 128), (256, 512, 192),
                                    (512, 768, 320), (768, 256, 1024)])
 def test_bf16_small_integers_bit_exact(M, N, K, sched):
@@ -94,7 +95,7 @@ def test_bf16_small_integers_bit_exact(M, N, K, sched):
     np.testing.assert_array_equal(cb, oracle.bf16_round(want))
 
 
-@pytest.mark.parametrize("sched", SCHEDULES)
+@pytest.mark.parametrize("sched", SCHEDULES, ids=SCHED_IDS)
 @pytest.mark.parametrize("M,N,K", [(256, 256, 128), (256, 512, 256), (512, 768, 384),
                                    (768, 256, 1024)])
 def test_fp8_small_integers_bit_exact(M, N, K, sched):
@@ -192,7 +193,7 @@ def test_k_zero_writes_zeros():
 
 # ---------------------------------------------------------------- random parity ----
 
-@pytest.mark.parametrize("sched", SCHEDULES)
+@pytest.mark.parametrize("sched", SCHEDULES, ids=SCHED_IDS)
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (512, 768, 448), (1024, 512, 1536)])
 def test_bf16_random_matches_oracle(M, N, K, sched):
     _say("bf16 random %dx%dx%d sched=%d" % (M, N, K, sched))
@@ -203,7 +204,7 @@ def test_bf16_random_matches_oracle(M, N, K, sched):
     check(ref, cf, cb, K, "bf16 %dx%dx%d" % (M, N, K))
 
 
-@pytest.mark.parametrize("sched", SCHEDULES)
+@pytest.mark.parametrize("sched", SCHEDULES, ids=SCHED_IDS)
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (512, 768, 640), (1024, 512, 1536)])
 def test_fp8_random_matches_oracle(M, N, K, sched):
     _say("fp8 random %dx%dx%d sched=%d" % (M, N, K, sched))
@@ -230,11 +231,14 @@ def test_output_identical_across_grid_orders_and_schedules():
     A = synth.f32_to_bf16_bits(synth.normal_f32(9960, M, K))
     B = synth.f32_to_bf16_bits(synth.normal_f32(9961, N, K))
     base, _ = run_bf16(A, B, want_f32=False)
-    variants = [hkg.make_opts(remap=hkg.HKG_REMAP_ROW_MAJOR),
+    variants = [hkg.make_opts(schedule=hkg.HKG_SCHED_PINGPONG),
+                hkg.make_opts(remap=hkg.HKG_REMAP_ROW_MAJOR),
                 hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=5, C=25),
                 hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=7, C=216),
                 hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=1, C=6),
-                hkg.make_opts(schedule=hkg.HKG_SCHED_LOCKSTEP)]
+                hkg.make_opts(schedule=hkg.HKG_SCHED_LOCKSTEP),
+                hkg.make_opts(schedule=hkg.HKG_SCHED_INTERLEAVE),
+                hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=3, C=9, schedule=hkg.HKG_SCHED_INTERLEAVE)]
     for o in variants:
         got, _ = run_bf16(A, B, opts=o, want_f32=False)
         np.testing.assert_array_equal(got, base)
@@ -317,7 +321,7 @@ RAGGED_BF16 = [(1, 1, 8), (17, 33, 72), (255, 257, 200), (300, 520, 136), (513, 
 RAGGED_FP8 = [(1, 1, 16), (130, 250, 144), (513, 300, 272), (257, 1000, 1040)]
 
 
-@pytest.mark.parametrize("sched", SCHEDULES)
+@pytest.mark.parametrize("sched", SCHEDULES, ids=SCHED_IDS)
 @pytest.mark.parametrize("M,N,K", RAGGED_BF16)
 def test_bf16_ragged_integers_bit_exact(M, N, K, sched):
     _say("bf16 ragged ints %dx%dx%d sched=%d" % (M, N, K, sched))
@@ -329,7 +333,7 @@ def test_bf16_ragged_integers_bit_exact(M, N, K, sched):
     np.testing.assert_array_equal(cb, oracle.bf16_round(want))
 
 
-@pytest.mark.parametrize("sched", SCHEDULES)
+@pytest.mark.parametrize("sched", SCHEDULES, ids=SCHED_IDS)
 @pytest.mark.parametrize("M,N,K", RAGGED_FP8)
 def test_fp8_ragged_integers_bit_exact(M, N, K, sched):
     _say("fp8 ragged ints %dx%dx%d sched=%d" % (M, N, K, sched))
