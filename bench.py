@@ -2,7 +2,8 @@
 """Benchmark of the tiled GEMM C = A·Bᵀ on one MI355X.
 
 One step = one GEMM launch over resident device inputs (the whole hot path:
-remap, HBM->LDS loads, ping-pong MFMA loop, epilogue).  Default workload: bf16
+remap, HBM->LDS loads, the in-CU MFMA loop -- the 4-wave interleave unless
+--schedule says otherwise -- and the epilogue).  Default workload: bf16
 M = N = K = 8192 with seeded N(0,1) inputs.  Prints one JSON line with the
 throughput (TFLOPS), the MFMA roofline of the kernel (live HIP-event timing),
 and the CPU oracle timed on a bounded sample as a baseline.
@@ -10,6 +11,8 @@ and the CPU oracle timed on a bounded sample as a baseline.
   python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload 2]
                   [--all] [--remap W,C | --row-major] [--schedule interleave|pingpong|lockstep]
                   [--no-cpu-baseline]
+  python bench.py --sizes "1024 2048 ..." [--dtype bf16|fp8]
+        square-size sweep: both schedules per size, one JSON line each
   python bench.py --sweep "1,1 8,32 5,25 ..." [--workload N | --shape M,N,K --dtype bf16|fp8]
         grid-order sweep: one JSON line per (W, C) on the same resident inputs
         ("1,1" is row-major order); used to choose the library's default (W, C)
@@ -270,6 +273,63 @@ def sweep(w: synth.Workload, pairs, steps: int, warmup: int) -> None:
                           "TFLOPS": round(w.flops / (ms * 1e-3) / 1e12, 2)}), flush=True)
 
 
+def size_sweep(sizes, dtype: str, warmup: int) -> None:
+    """Square sizes n x n x n (any n: edge tiles are masked): both in-CU
+    schedules on the same inputs, each timed for ~0.2 s twice (forward and
+    reverse order); one JSON line per (size, schedule)."""
+    import torch
+    import dense_gemm_fp8_amd as hkg
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    scheds = [("interleave", hkg.HKG_SCHED_INTERLEAVE), ("pingpong", hkg.HKG_SCHED_PINGPONG)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    for n in sizes:
+        w = custom_workload("%d,%d,%d" % (n, n, n), dtype)
+        A, B, sa, sb = synth.make_inputs(w)
+        if dtype == "bf16":
+            dA = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).to(dev)
+            dB = torch.from_numpy(B.view(np.int16)).view(torch.bfloat16).to(dev)
+        else:
+            dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+        del A, B
+        C = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+
+        def run(sc, k):
+            opts = hkg.make_opts(schedule=sc)
+            for _ in range(k):
+                if dtype == "bf16":
+                    hkg.gemm_bf16(dA, dB, C, opts=opts, stream=stream)
+                else:
+                    hkg.gemm_fp8(dA, dB, sa, sb, C, opts=opts, stream=stream)
+
+        def timed(sc, k):
+            e0.record(stream)
+            run(sc, k)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / k
+
+        run(scheds[0][1], warmup)
+        est = timed(scheds[0][1], 3)
+        steps = int(min(500, max(5, 200.0 / max(est, 1e-3))))
+        times = {name: [] for name, _ in scheds}
+        for order in (scheds, scheds[::-1]):
+            for name, sc in order:
+                run(sc, 2)
+                times[name].append(timed(sc, steps))
+        peak = 2500.0 if dtype == "bf16" else 5000.0
+        for name, _ in scheds:
+            ms = float(np.mean(times[name]))
+            tf = w.flops / (ms * 1e-3) / 1e12
+            print(json.dumps({"size_sweep": dtype, "n": n, "schedule": name, "steps": steps,
+                              "ms": round(ms, 5), "TFLOPS": round(tf, 1),
+                              "frac_of_peak": round(tf / peak, 4)}), flush=True)
+        del dA, dB, C
+        torch.cuda.empty_cache()
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +345,8 @@ def main(argv=None) -> int:
     ap.add_argument("--shape", type=str, default=None, help="M,N,K (custom size)")
     ap.add_argument("--dtype", choices=["bf16", "fp8"], default="bf16")
     ap.add_argument("--sweep", type=str, default=None, help='"W,C W,C ..." grid orders to time')
+    ap.add_argument("--sizes", type=str, default=None,
+                    help='"n n ..." square sizes: both schedules per size (with --dtype)')
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -305,6 +367,9 @@ def main(argv=None) -> int:
     elif sched != hkg.HKG_SCHED_INTERLEAVE:
         opts = hkg.make_opts(schedule=sched)
 
+    if args.sizes:
+        size_sweep([int(v) for v in args.sizes.split()], args.dtype, args.warmup)
+        return 0
     if args.sweep:
         w = custom_workload(args.shape, args.dtype) if args.shape else synth.workload(args.workload)
         pairs = [tuple(int(v) if v.isdigit() else v for v in item.split(","))
