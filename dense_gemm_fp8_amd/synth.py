@@ -9,6 +9,12 @@ into the two input formats the path consumes.
   s = amax / 448 (448 is the largest finite e4m3 value) and rounded to the
   nearest e4m3 code with ties to even; magnitudes above 448 saturate to +-448.
 
+* MXFP8 (OCP Microscaling Formats specification v1.0): e4m3 elements with one
+  E8M0 scale (2^(E-127)) per block of 32 consecutive elements along K; the
+  block's shared exponent is floor(log2(amax)) - 8 (8 = exponent of the
+  largest power of two in e4m3) as in the specification's conversion, and the
+  elements are x / 2^shared rounded to e4m3 (nearest even, saturating).
+
 The HipKittens L2 note (section 3, "Target operation" table) gives the GEMM shapes and
 dtypes but no RNG, quantiser or rounding rule; the plainest readings are used
 here and listed in the design notes.
@@ -82,13 +88,49 @@ def e4m3_quantize(x: np.ndarray) -> tuple[np.ndarray, np.float32]:
     return q, s
 
 
+MX_BLOCK = 32          # elements per E8M0 scale (along K)
+E8M0_BIAS = 127
+E4M3_EMAX = 8          # exponent of the largest power of two that e4m3 holds (256)
+
+
+def mx_quantize(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """MXFP8 quantisation of a float32 [R, K] matrix (K % 32 == 0).
+
+    Returns (codes uint8 [R, K], scales uint8 [R, K/32]).  Per block of 32:
+    shared = floor(log2(amax)) - 8, clamped to the E8M0 range [-127, 127];
+    codes = e4m3(x / 2^shared).  An all-zero block gets scale byte 127 (1.0)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    R, K = x.shape
+    if K % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    blocks = x.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(blocks), axis=2)
+    _, E = np.frexp(amax)                       # amax = f * 2^E, f in [0.5, 1)
+    shared = np.where(amax > 0, E.astype(np.int32) - 1 - E4M3_EMAX, 0)
+    shared = np.clip(shared, -E8M0_BIAS, E8M0_BIAS)
+    scaled = np.ldexp(blocks, -shared[:, :, None]).astype(np.float32)   # exact power-of-two scaling
+    codes = e4m3_encode(scaled).reshape(R, K)
+    return codes, (shared + E8M0_BIAS).astype(np.uint8)
+
+
+def small_int_mx(seed: int, rows: int, cols: int, lo: int = -2, hi: int = 2,
+                 elo: int = -2, ehi: int = 2) -> tuple[np.ndarray, np.ndarray]:
+    """Integer-valued e4m3 codes in [lo, hi] with E8M0 block scales 2^e,
+    e uniform in [elo, ehi] (every product and partial sum exact in fp32 for
+    small K)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    codes = e4m3_encode(g.integers(lo, hi + 1, size=(rows, cols)).astype(np.float32))
+    scales = (g.integers(elo, ehi + 1, size=(rows, cols // MX_BLOCK)) + E8M0_BIAS).astype(np.uint8)
+    return codes, scales
+
+
 # --- workloads -------------------------------------------------------------------
 
 @dataclasses.dataclass(frozen=True)
 class Workload:
     """One GEMM workload: C[M,N] = A[M,K] · B[N,K]ᵀ."""
     name: str
-    dtype: str          # "bf16" or "fp8"
+    dtype: str          # "bf16", "fp8" (per-tensor scales) or "mxfp8" (block scales)
     M: int
     N: int
     K: int
@@ -115,28 +157,32 @@ def workload(idx: int) -> Workload:
         3: ("bf16_mlp_16384x14336x4096", "bf16", 16384, 14336, 4096, 1.0, 0.02),
         4: ("bf16_16384", "bf16", 16384, 16384, 16384, 1.0, 1.0),
         5: ("fp8_e4m3_8192", "fp8", 8192, 8192, 8192, 1.0, 1.0),
+        6: ("mxfp8_8192", "mxfp8", 8192, 8192, 8192, 1.0, 1.0),
     }
     name, dt, M, N, K, sa, sb = table[idx]
     return Workload(name, dt, M, N, K, 1000 * idx + 1, 1000 * idx + 2, sa, sb)
 
 
-ALL_WORKLOADS = tuple(workload(i) for i in range(1, 6))
+ALL_WORKLOADS = tuple(workload(i) for i in range(1, 6))   # the five configurations
+MX_WORKLOAD = workload(6)                                  # block-scaled e4m3 at 8192^3
 
 
 def make_inputs(w: Workload):
     """Host inputs for a workload.
 
-    bf16: (A_bits uint16 [M,K], B_bits uint16 [N,K], None, None)
-    fp8:  (A_codes uint8 [M,K], B_codes uint8 [N,K], scale_a, scale_b)"""
+    bf16:  (A_bits uint16 [M,K], B_bits uint16 [N,K], None, None)
+    fp8:   (A_codes uint8 [M,K], B_codes uint8 [N,K], scale_a, scale_b)
+    mxfp8: (A_codes uint8 [M,K], B_codes uint8 [N,K], SA uint8 [M,K/32], SB uint8 [N,K/32])"""
     a = normal_f32(w.seed_a, w.M, w.K, w.sigma_a)
     if w.dtype == "bf16":
         A = f32_to_bf16_bits(a)
         del a
         B = f32_to_bf16_bits(normal_f32(w.seed_b, w.N, w.K, w.sigma_b))
         return A, B, None, None
-    qa, sa = e4m3_quantize(a)
+    quant = mx_quantize if w.dtype == "mxfp8" else e4m3_quantize
+    qa, sa = quant(a)
     del a
-    qb, sb = e4m3_quantize(normal_f32(w.seed_b, w.N, w.K, w.sigma_b))
+    qb, sb = quant(normal_f32(w.seed_b, w.N, w.K, w.sigma_b))
     return qa, qb, sa, sb
 
 

@@ -57,6 +57,13 @@ def _load():
                                         p, ctypes.c_int]
         lib.oracle_gemm_bf16_pairs.restype = ctypes.c_int
         lib.oracle_gemm_bf16_pairs.argtypes = [i64, i64, i64, p, p, p, p, i64, p, ctypes.c_int]
+        lib.oracle_e8m0_value.restype = ctypes.c_double
+        lib.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_gemm_mxfp8.restype = ctypes.c_int
+        lib.oracle_gemm_mxfp8.argtypes = [i64, i64, i64, p, p, p, p, p, ctypes.c_int]
+        lib.oracle_gemm_mxfp8_pairs.restype = ctypes.c_int
+        lib.oracle_gemm_mxfp8_pairs.argtypes = [i64, i64, i64, p, p, p, p, p, p, i64, p,
+                                                ctypes.c_int]
         lib.oracle_gemm_fp8_pairs.restype = ctypes.c_int
         lib.oracle_gemm_fp8_pairs.argtypes = [i64, i64, i64, p, p, ctypes.c_float,
                                               ctypes.c_float, p, p, i64, p, ctypes.c_int]
@@ -156,4 +163,47 @@ def gemm_fp8_pairs(A, B, scale_a, scale_b, pm, pn, threads: int | None = None) -
                                        threads or default_threads())
     if rc:
         raise RuntimeError("oracle_gemm_fp8_pairs failed: %d" % rc)
+    return out
+
+
+def e8m0_value(e: int) -> float:
+    return _load().oracle_e8m0_value(e)
+
+
+def _check_mx(A, B, SA, SB, K):
+    _check(A, B, K, np.uint8)
+    if K % 32:
+        raise ValueError("MXFP8 needs K % 32 == 0")
+    if SA.dtype != np.uint8 or SB.dtype != np.uint8:
+        raise TypeError("expected uint8 E8M0 scales")
+    if SA.shape != (A.shape[0], K // 32) or SB.shape != (B.shape[0], K // 32):
+        raise ValueError("SA must be [M,K/32] and SB [N,K/32]")
+
+
+def gemm_mxfp8(A, B, SA, SB, threads: int | None = None) -> np.ndarray:
+    """fp64 reference of the MXFP8 product: e4m3 codes A [M,K], B [N,K] with
+    E8M0 block scales SA [M,K/32], SB [N,K/32] (one per 32 consecutive k)."""
+    A, B = np.ascontiguousarray(A), np.ascontiguousarray(B)
+    SA, SB = np.ascontiguousarray(SA), np.ascontiguousarray(SB)
+    M, K = A.shape; N = B.shape[0]
+    _check_mx(A, B, SA, SB, K)
+    out = np.empty((M, N), dtype=np.float64)
+    rc = _load().oracle_gemm_mxfp8(M, N, K, _ptr(A), _ptr(B), _ptr(SA), _ptr(SB), _ptr(out),
+                                   threads or default_threads())
+    if rc:
+        raise RuntimeError("oracle_gemm_mxfp8 failed: %d" % rc)
+    return out
+
+
+def gemm_mxfp8_pairs(A, B, SA, SB, pm, pn, threads: int | None = None) -> np.ndarray:
+    A, B = np.ascontiguousarray(A), np.ascontiguousarray(B)
+    SA, SB = np.ascontiguousarray(SA), np.ascontiguousarray(SB)
+    M, K = A.shape; N = B.shape[0]
+    _check_mx(A, B, SA, SB, K)
+    pm = np.ascontiguousarray(pm, dtype=np.int64); pn = np.ascontiguousarray(pn, dtype=np.int64)
+    out = np.empty(pm.shape, dtype=np.float64)
+    rc = _load().oracle_gemm_mxfp8_pairs(M, N, K, _ptr(A), _ptr(B), _ptr(SA), _ptr(SB), _ptr(pm),
+                                         _ptr(pn), pm.size, _ptr(out), threads or default_threads())
+    if rc:
+        raise RuntimeError("oracle_gemm_mxfp8_pairs failed: %d" % rc)
     return out

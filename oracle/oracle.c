@@ -25,6 +25,16 @@
  *   OCP e4m3 (FN): S.EEEE.MMM, bias 7, no infinities; E == 0 is subnormal
  *   (M/8 * 2^-6), otherwise (1 + M/8) * 2^(E-7); S.1111.111 is NaN; max 448.
  *
+ * MXFP8 (the fp8 input type that the HipKittens L2 note's section 3 table
+ * names; the format itself is the OCP Microscaling (MX) Formats
+ * specification v1.0): e4m3 elements, and one E8M0 scale per 32 consecutive
+ * elements along K of each row.  An E8M0 byte E is the value 2^(E-127), and
+ * E == 0xFF is NaN.  Element k of row r stands for
+ *     e4m3(a[r][k]) * 2^(SA[r][k/32] - 127),
+ * so the reference is the same k-ascending fp64 sum of those products, with
+ * SA stored [M][K/32] and SB [N][K/32] row-major.  Each product is an
+ * exact fp64 value (8-bit significand, exponent within +-300).
+ *
  * Rounding to bf16 is one round-to-nearest-even step from the fp64 value
  * (not via binary32).
  *
@@ -93,14 +103,23 @@ void oracle_bf16_round_array(const double *x, uint16_t *out, int64_t n)
         out[i] = oracle_bf16_round(x[i]);
 }
 
+/* OCP MX E8M0 scale: 2^(E - 127); 0xFF is NaN. */
+double oracle_e8m0_value(uint8_t e)
+{
+    if (e == 0xFF)
+        return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
 /* ---------------------------------------------------------------- GEMM ---- */
 
-enum { ORACLE_BF16 = 0, ORACLE_E4M3 = 1 };
+enum { ORACLE_BF16 = 0, ORACLE_E4M3 = 1, ORACLE_MXFP8 = 2 };
 
 typedef struct {
     int kind;
     int64_t M, N, K;
     const void *A, *B;
+    const uint8_t *SA, *SB;     /* MXFP8 block scales [rows][K/32], else NULL */
     double scale;               /* multiplies the sum (1 for bf16) */
     const int64_t *pm, *pn;     /* pairs, or NULL for the full M x N grid */
     int64_t count;              /* number of outputs */
@@ -116,11 +135,20 @@ static double dot_row_row(const job_t *j, int64_t m, int64_t n)
         const uint16_t *b = (const uint16_t *)j->B + n * j->K;
         for (int64_t k = 0; k < j->K; ++k)
             s += oracle_bf16_value(a[k]) * oracle_bf16_value(b[k]);
-    } else {
+    } else if (j->kind == ORACLE_E4M3) {
         const uint8_t *a = (const uint8_t *)j->A + m * j->K;
         const uint8_t *b = (const uint8_t *)j->B + n * j->K;
         for (int64_t k = 0; k < j->K; ++k)
             s += oracle_e4m3_value(a[k]) * oracle_e4m3_value(b[k]);
+    } else {
+        const int64_t nb = j->K / 32;
+        const uint8_t *a = (const uint8_t *)j->A + m * j->K;
+        const uint8_t *b = (const uint8_t *)j->B + n * j->K;
+        const uint8_t *sa = j->SA + m * nb;
+        const uint8_t *sb = j->SB + n * nb;
+        for (int64_t k = 0; k < j->K; ++k)
+            s += (oracle_e4m3_value(a[k]) * oracle_e8m0_value(sa[k / 32])) *
+                 (oracle_e4m3_value(b[k]) * oracle_e8m0_value(sb[k / 32]));
     }
     return s * j->scale;
 }
@@ -143,10 +171,12 @@ static void *worker(void *arg)
 }
 
 static int run(int kind, int64_t M, int64_t N, int64_t K, const void *A, const void *B,
-               double scale, const int64_t *pm, const int64_t *pn, int64_t count,
-               double *out, int nthreads)
+               const uint8_t *SA, const uint8_t *SB, double scale, const int64_t *pm,
+               const int64_t *pn, int64_t count, double *out, int nthreads)
 {
     if (M < 0 || N < 0 || K < 0 || count < 0 || !out)
+        return -1;
+    if (kind == ORACLE_MXFP8 && (K % 32 != 0 || (M > 0 && N > 0 && K > 0 && (!SA || !SB))))
         return -1;
     if (count == 0)
         return 0;
@@ -169,6 +199,7 @@ static int run(int kind, int64_t M, int64_t N, int64_t K, const void *A, const v
     for (int t = 0; t < nthreads; ++t) {
         job_t *j = &jobs[t];
         j->kind = kind; j->M = M; j->N = N; j->K = K; j->A = A; j->B = B;
+        j->SA = SA; j->SB = SB;
         j->scale = scale; j->pm = pm; j->pn = pn; j->count = count; j->out = out;
         j->begin = t * per;
         j->end = (t + 1) * per < count ? (t + 1) * per : count;
@@ -193,14 +224,14 @@ static int run(int kind, int64_t M, int64_t N, int64_t K, const void *A, const v
 int oracle_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, const uint16_t *B,
                      double *out, int nthreads)
 {
-    return run(ORACLE_BF16, M, N, K, A, B, 1.0, NULL, NULL, M * N, out, nthreads);
+    return run(ORACLE_BF16, M, N, K, A, B, NULL, NULL, 1.0, NULL, NULL, M * N, out, nthreads);
 }
 
 int oracle_gemm_fp8(int64_t M, int64_t N, int64_t K, const uint8_t *A, const uint8_t *B,
                     float scale_a, float scale_b, double *out, int nthreads)
 {
-    return run(ORACLE_E4M3, M, N, K, A, B, (double)scale_a * (double)scale_b, NULL, NULL,
-               M * N, out, nthreads);
+    return run(ORACLE_E4M3, M, N, K, A, B, NULL, NULL, (double)scale_a * (double)scale_b, NULL,
+               NULL, M * N, out, nthreads);
 }
 
 /* Sampled outputs: out[i] = ref[pm[i]][pn[i]]. */
@@ -210,7 +241,7 @@ int oracle_gemm_bf16_pairs(int64_t M, int64_t N, int64_t K, const uint16_t *A,
 {
     if (count > 0 && (!pm || !pn))
         return -1;
-    return run(ORACLE_BF16, M, N, K, A, B, 1.0, pm, pn, count, out, nthreads);
+    return run(ORACLE_BF16, M, N, K, A, B, NULL, NULL, 1.0, pm, pn, count, out, nthreads);
 }
 
 int oracle_gemm_fp8_pairs(int64_t M, int64_t N, int64_t K, const uint8_t *A, const uint8_t *B,
@@ -219,6 +250,24 @@ int oracle_gemm_fp8_pairs(int64_t M, int64_t N, int64_t K, const uint8_t *A, con
 {
     if (count > 0 && (!pm || !pn))
         return -1;
-    return run(ORACLE_E4M3, M, N, K, A, B, (double)scale_a * (double)scale_b, pm, pn, count,
-               out, nthreads);
+    return run(ORACLE_E4M3, M, N, K, A, B, NULL, NULL, (double)scale_a * (double)scale_b, pm, pn,
+               count, out, nthreads);
+}
+
+/* MXFP8: A, B e4m3 codes [rows][K]; SA [M][K/32], SB [N][K/32] E8M0 bytes;
+ * K must be a multiple of 32. */
+int oracle_gemm_mxfp8(int64_t M, int64_t N, int64_t K, const uint8_t *A, const uint8_t *B,
+                      const uint8_t *SA, const uint8_t *SB, double *out, int nthreads)
+{
+    return run(ORACLE_MXFP8, M, N, K, A, B, SA, SB, 1.0, NULL, NULL, M * N, out, nthreads);
+}
+
+int oracle_gemm_mxfp8_pairs(int64_t M, int64_t N, int64_t K, const uint8_t *A,
+                            const uint8_t *B, const uint8_t *SA, const uint8_t *SB,
+                            const int64_t *pm, const int64_t *pn, int64_t count, double *out,
+                            int nthreads)
+{
+    if (count > 0 && (!pm || !pn))
+        return -1;
+    return run(ORACLE_MXFP8, M, N, K, A, B, SA, SB, 1.0, pm, pn, count, out, nthreads);
 }
