@@ -35,7 +35,7 @@ if ROOT not in sys.path:
 from dense_gemm_fp8_amd import synth  # noqa: E402
 
 METRIC = "GEMM TFLOPS at 8192³ bf16 (fraction of 2.5 PF peak); L2/LLC hit %"
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}     # MI355X dense MFMA peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0}   # MI355X dense MFMA peaks
 # HipKittens 8-wave 0P/8C bf16 GEMM at 8192^3 on MI355X (HipKittens L2 note, Table 2 / Q3)
 PAGES_BF16_8192_TFLOPS = 1610.0
 KERNEL_SOURCES = ("dense_gemm_fp8_amd/csrc/gemm_kernels.hip", "dense_gemm_fp8_amd/csrc/remap.h",
@@ -61,9 +61,11 @@ def kernel_source_hash() -> str:
 
 
 def algorithmic_bytes(w: synth.Workload) -> int:
-    """Bytes the GEMM must move at minimum: read A and B once, write C (bf16) once."""
+    """Bytes the GEMM must move at minimum: read A and B once (MXFP8: and their
+    one-byte scales per 32 elements), write C (bf16) once."""
     e = 2 if w.dtype == "bf16" else 1
-    return e * (w.M * w.K + w.N * w.K) + 2 * w.M * w.N
+    scales = (w.M + w.N) * w.K // 32 if w.dtype == "mxfp8" else 0
+    return e * (w.M * w.K + w.N * w.K) + scales + 2 * w.M * w.N
 
 
 def kernel_name(dtype: str, schedule: str) -> str:
@@ -97,6 +99,8 @@ def cpu_baseline(w: synth.Workload, A, B, sa, sb, target_s: float = 12.0) -> dic
         t0 = time.perf_counter()
         if w.dtype == "bf16":
             oracle.gemm_bf16_pairs(A, B, pm, pn, threads=threads)
+        elif w.dtype == "mxfp8":
+            oracle.gemm_mxfp8_pairs(A, B, sa, sb, pm, pn, threads=threads)
         else:
             oracle.gemm_fp8_pairs(A, B, sa, sb, pm, pn, threads=threads)
         return time.perf_counter() - t0
@@ -127,18 +131,35 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
         dB = torch.from_numpy(B).to(dev)
     C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if w.dtype == "mxfp8":
+        # one MXFP8 step packs both operands' scales from their natural
+        # [rows][K/32] layout, then runs the GEMM kernel
+        dSA = torch.from_numpy(sa).to(dev)
+        dSB = torch.from_numpy(sb).to(dev)
+        pSA = hkg.mx_pack_scales(dSA, hkg.HKG_MX_OPERAND_A, stream=stream)
+        pSB = hkg.mx_pack_scales(dSB, hkg.HKG_MX_OPERAND_B, stream=stream)
 
-    def step():
+    def step(e0=None, e1=None):
+        """One pass of the path; e0/e1 bracket the GEMM kernel launch."""
+        if w.dtype == "mxfp8":
+            hkg.mx_pack_scales(dSA, hkg.HKG_MX_OPERAND_A, pSA, stream=stream)
+            hkg.mx_pack_scales(dSB, hkg.HKG_MX_OPERAND_B, pSB, stream=stream)
+        if e0 is not None:
+            e0.record(stream)
         if w.dtype == "bf16":
             hkg.gemm_bf16(dA, dB, C, opts=opts, stream=stream)
+        elif w.dtype == "mxfp8":
+            hkg.gemm_mxfp8(dA, dB, pSA, pSB, C, opts=opts, stream=stream)
         else:
             hkg.gemm_fp8(dA, dB, sa, sb, C, opts=opts, stream=stream)
+        if e1 is not None:
+            e1.record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: every launch bracketed by HIP events on the launch stream
+    # timed region: every GEMM launch bracketed by HIP events on the launch stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     outer0 = torch.cuda.Event(enable_timing=True)
@@ -147,9 +168,7 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
     t0 = time.perf_counter()
     outer0.record(stream)
     for s, e in ev:
-        s.record(stream)
-        step()
-        e.record(stream)
+        step(s, e)
     outer1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -177,8 +196,10 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
-                   "inputs": "seeded N(0,1)%s" % ("" if w.dtype == "bf16" else
-                                                  " quantised to e4m3 with amax/448 scales"),
+                   "inputs": "seeded N(0,1)%s" % {
+                       "bf16": "", "fp8": " quantised to e4m3 with amax/448 scales",
+                       "mxfp8": " quantised to MXFP8 (e4m3, one E8M0 scale per 32 along K;"
+                                " step includes packing both scale arrays)"}[w.dtype],
                    "schedule": sched_name,
                    "remap": ({"remap": opts.remap, "W": opts.W, "C": opts.C} if opts else "default")},
         "fraction_of_peak": round(tflops / peak, 4),
@@ -283,6 +304,8 @@ def size_sweep(sizes, dtype: str, warmup: int) -> None:
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     scheds = [("interleave", hkg.HKG_SCHED_INTERLEAVE), ("pingpong", hkg.HKG_SCHED_PINGPONG)]
+    if dtype == "mxfp8":     # the block-scaled path exists in the 4-wave kernel only
+        scheds = scheds[:1]
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     for n in sizes:
@@ -293,6 +316,9 @@ def size_sweep(sizes, dtype: str, warmup: int) -> None:
             dB = torch.from_numpy(B.view(np.int16)).view(torch.bfloat16).to(dev)
         else:
             dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+            if dtype == "mxfp8":   # scales packed once; the sweep times the GEMM kernel
+                pSA = hkg.mx_pack_scales(torch.from_numpy(sa).to(dev), hkg.HKG_MX_OPERAND_A)
+                pSB = hkg.mx_pack_scales(torch.from_numpy(sb).to(dev), hkg.HKG_MX_OPERAND_B)
         del A, B
         C = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
 
@@ -301,6 +327,8 @@ def size_sweep(sizes, dtype: str, warmup: int) -> None:
             for _ in range(k):
                 if dtype == "bf16":
                     hkg.gemm_bf16(dA, dB, C, opts=opts, stream=stream)
+                elif dtype == "mxfp8":
+                    hkg.gemm_mxfp8(dA, dB, pSA, pSB, C, opts=opts, stream=stream)
                 else:
                     hkg.gemm_fp8(dA, dB, sa, sb, C, opts=opts, stream=stream)
 
@@ -319,7 +347,7 @@ def size_sweep(sizes, dtype: str, warmup: int) -> None:
             for name, sc in order:
                 run(sc, 2)
                 times[name].append(timed(sc, steps))
-        peak = 2500.0 if dtype == "bf16" else 5000.0
+        peak = PEAK_TFLOPS[dtype]
         for name, _ in scheds:
             ms = float(np.mean(times[name]))
             tf = w.flops / (ms * 1e-3) / 1e12
@@ -335,7 +363,8 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6],
+                    help="1-5: the five configurations; 6: MXFP8 8192^3")
     ap.add_argument("--all", action="store_true", help="one line per workload 1..5")
     ap.add_argument("--remap", type=str, default=None, help="W,C for the XCD remap")
     ap.add_argument("--row-major", action="store_true")
@@ -343,7 +372,7 @@ def main(argv=None) -> int:
                     default="interleave", help="in-CU schedule (default: the library's, interleave)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shape", type=str, default=None, help="M,N,K (custom size)")
-    ap.add_argument("--dtype", choices=["bf16", "fp8"], default="bf16")
+    ap.add_argument("--dtype", choices=["bf16", "fp8", "mxfp8"], default="bf16")
     ap.add_argument("--sweep", type=str, default=None, help='"W,C W,C ..." grid orders to time')
     ap.add_argument("--sizes", type=str, default=None,
                     help='"n n ..." square sizes: both schedules per size (with --dtype)')

@@ -1,11 +1,12 @@
 """dense_gemm_fp8_amd -- Python binding of libhkg, the MI355X (gfx950) tiled GEMM.
 
-    C[M,N] = A[M,K] · B[N,K]ᵀ     (bf16 or OCP e4m3 inputs, fp32 accumulate, bf16 out)
+    C[M,N] = A[M,K] · B[N,K]ᵀ     (bf16, OCP e4m3 or MXFP8 inputs, fp32 accumulate, bf16 out)
 
 The C ABI (include/hkg.h) is the product; this module only marshals
 arguments.  The functions with the C names (hkg_gemm_bf16, ...) take integers
 for device pointers and the stream, exactly like the C entry points.  The
-torch helpers (gemm_bf16, gemm_fp8, remap_tiles_device) take torch tensors that
+torch helpers (gemm_bf16, gemm_fp8, gemm_mxfp8, mx_pack_scales,
+remap_tiles_device) take torch tensors that
 already live on the GPU; torch is used for device memory and streams only,
 every step of the GEMM runs in the library's own kernels.
 
@@ -39,12 +40,19 @@ HKG_SCHED_PINGPONG = 1
 HKG_SCHED_LOCKSTEP = 2
 HKG_SCHED_INTERLEAVE = 3
 
+HKG_MX_OPERAND_A = 0
+HKG_MX_OPERAND_B = 1
+
 # exported symbols, in the order include/hkg.h declares them
 EXPORTS = (
     "hkg_gemm_bf16",
     "hkg_gemm_fp8",
     "hkg_gemm_bf16_ex",
     "hkg_gemm_fp8_ex",
+    "hkg_gemm_mxfp8",
+    "hkg_gemm_mxfp8_ex",
+    "hkg_mx_packed_scale_bytes",
+    "hkg_mx_pack_scales",
     "hkg_default_remap",
     "hkg_remap_tile",
     "hkg_remap_tiles_device",
@@ -94,6 +102,10 @@ def load() -> ctypes.CDLL:
         "hkg_gemm_fp8": [i64, i64, i64, p, p, f32, f32, p, p, p],
         "hkg_gemm_bf16_ex": [i64, i64, i64, p, p, p, p, p, popts],
         "hkg_gemm_fp8_ex": [i64, i64, i64, p, p, f32, f32, p, p, p, popts],
+        "hkg_gemm_mxfp8": [i64, i64, i64, p, p, p, p, p, p, p],
+        "hkg_gemm_mxfp8_ex": [i64, i64, i64, p, p, p, p, p, p, p, popts],
+        "hkg_mx_packed_scale_bytes": [i64, i64],
+        "hkg_mx_pack_scales": [i32, i64, i64, p, p, p],
         "hkg_default_remap": [i64, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)],
         "hkg_remap_tile": [i64, i64, i32, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)],
         "hkg_remap_tiles_device": [i64, i64, i32, i32, p, p],
@@ -103,7 +115,8 @@ def load() -> ctypes.CDLL:
     for name, args in sig.items():
         fn = getattr(lib, name)
         fn.argtypes = args
-        fn.restype = ctypes.c_char_p if name == "hkg_status_string" else ctypes.c_int
+        fn.restype = {"hkg_status_string": ctypes.c_char_p,
+                      "hkg_mx_packed_scale_bytes": ctypes.c_int64}.get(name, ctypes.c_int)
     _lib = lib
     return lib
 
@@ -126,6 +139,23 @@ def hkg_gemm_bf16_ex(M, N, K, A, B, C, C_f32, stream, opts) -> int:
 def hkg_gemm_fp8_ex(M, N, K, A, B, scale_a, scale_b, C, C_f32, stream, opts) -> int:
     return load().hkg_gemm_fp8_ex(M, N, K, A, B, scale_a, scale_b, C, C_f32, stream,
                                   ctypes.byref(opts) if opts is not None else None)
+
+
+def hkg_gemm_mxfp8(M, N, K, A, B, SA_packed, SB_packed, C, C_f32, stream) -> int:
+    return load().hkg_gemm_mxfp8(M, N, K, A, B, SA_packed, SB_packed, C, C_f32, stream)
+
+
+def hkg_gemm_mxfp8_ex(M, N, K, A, B, SA_packed, SB_packed, C, C_f32, stream, opts) -> int:
+    return load().hkg_gemm_mxfp8_ex(M, N, K, A, B, SA_packed, SB_packed, C, C_f32, stream,
+                                    ctypes.byref(opts) if opts is not None else None)
+
+
+def hkg_mx_packed_scale_bytes(rows, K) -> int:
+    return load().hkg_mx_packed_scale_bytes(rows, K)
+
+
+def hkg_mx_pack_scales(operand, rows, K, scales, packed, stream) -> int:
+    return load().hkg_mx_pack_scales(operand, rows, K, scales, packed, stream)
 
 
 def hkg_default_remap(M, N, K, dtype):
@@ -223,6 +253,57 @@ def gemm_fp8(A, B, scale_a, scale_b, C=None, C_f32=None, opts=None, stream=None)
                          _stream_handle(stream), opts)
     if rc != HKG_OK:
         raise HkgError(rc, "hkg_gemm_fp8_ex")
+    return C
+
+
+def mx_pack_scales(scales, operand, packed=None, stream=None):
+    """Pack one MXFP8 operand's E8M0 scales (uint8 GPU tensor [rows, K/32]) into
+    the kernel's order (hkg_mx_pack_scales); returns the packed uint8 tensor."""
+    import torch
+    if scales.dtype != torch.uint8 or scales.dim() != 2:
+        raise TypeError("scales must be a 2-D uint8 tensor [rows, K/32]")
+    rows, nblk = scales.shape
+    K = 32 * nblk
+    nbytes = hkg_mx_packed_scale_bytes(rows, K)
+    if nbytes < 0:
+        raise HkgError(nbytes, "hkg_mx_packed_scale_bytes")
+    if packed is None:
+        packed = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=scales.device)
+    if packed.dtype != torch.uint8 or packed.numel() < nbytes:
+        raise ValueError("packed must be a uint8 tensor of at least %d bytes" % nbytes)
+    rc = hkg_mx_pack_scales(operand, rows, K, _dev_ptr(scales, "scales"), _dev_ptr(packed, "packed"),
+                            _stream_handle(stream))
+    if rc != HKG_OK:
+        raise HkgError(rc, "hkg_mx_pack_scales")
+    return packed
+
+
+def gemm_mxfp8(A, B, SA_packed, SB_packed, C=None, C_f32=None, opts=None, stream=None):
+    """C[M,N] (bf16) = A[M,K] · B[N,K]ᵀ for MXFP8 operands: e4m3 code tensors A, B
+    and their scales packed by mx_pack_scales (operand A resp. B); returns C."""
+    import torch
+    ok = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+    if A.dtype not in ok or B.dtype not in ok:
+        raise TypeError("A and B must hold e4m3 bytes (uint8 or float8_e4m3fn)")
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("A is [M,K] and B is [N,K]")
+    for t, rows, name in ((SA_packed, M, "SA_packed"), (SB_packed, N, "SB_packed")):
+        need = hkg_mx_packed_scale_bytes(rows, K)
+        if need >= 0 and (t.dtype != torch.uint8 or t.numel() < need):
+            raise ValueError("%s must be a uint8 tensor of at least %d bytes" % (name, need))
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if tuple(C.shape) != (M, N) or C.dtype != torch.bfloat16:
+        raise ValueError("C must be a [M,N] bfloat16 tensor")
+    if C_f32 is not None and (tuple(C_f32.shape) != (M, N) or C_f32.dtype != torch.float32):
+        raise ValueError("C_f32 must be a [M,N] float32 tensor")
+    rc = hkg_gemm_mxfp8_ex(M, N, K, _dev_ptr(A, "A"), _dev_ptr(B, "B"),
+                           _dev_ptr(SA_packed, "SA_packed"), _dev_ptr(SB_packed, "SB_packed"),
+                           _dev_ptr(C, "C"), _dev_ptr(C_f32, "C_f32"), _stream_handle(stream), opts)
+    if rc != HKG_OK:
+        raise HkgError(rc, "hkg_gemm_mxfp8_ex")
     return C
 
 

@@ -607,8 +607,12 @@ __device__ __forceinline__ int slot_xor_b(int r)
     return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 4) & 1) << 2);
 }
 
-// Lane part of a fragment read, chunk half h (q or 4 + q): A row x, B row
-// (x & 3) + 8 (x >> 2) of a block pair, x = lane % 16, q = lane / 16.
+// Lane part of a fragment read, chunk half h (chunk 4 h + q): A row x, B row
+// (x & 3) + 8 (x >> 2) of a block pair, x = lane % 16, q = lane / 16.  For
+// bf16 the halves are the two DOT_SLICEs.  For e4m3 this is the 16x16x128
+// MFMA's own k order (lane group q supplies k 16q..16q+15 and 64 + 16q..+15,
+// probed on gfx950); the block-scaled form applies the scale in lane group b
+// to the 32 k of block b, so the MXFP8 scales follow the same order.
 struct QuadLane {
     int a[2], b[2];
 };
@@ -623,6 +627,49 @@ __device__ __forceinline__ QuadLane quad_lane(int lane)
         l.b[h] = rb * kRowBytes + (((4 * h + q) ^ slot_xor_b(rb)) << 4);
     }
     return l;
+}
+
+// MXFP8 scales of one K step for one lane l: byte e of a[e >> 2] is the E8M0
+// scale of A fragment e's row for lane l and k block 4 t + l / 16 (the block
+// the MFMA scales with lane group l / 16's value), b likewise for B fragment
+// e.  Unused by the other dtypes.
+struct MxScales {
+    uint32_t a[2], b[2];
+};
+
+// v_mfma_scale_f32_16x16x128_f8f6f4 with e4m3 operands: the scale byte
+// (chosen by op_sel) of lane group b multiplies the products of k block b of
+// that lane's row (probed on gfx950); the first scale goes with the first
+// operand.  op_sel must be a constant: the switch
+// folds away once the caller's block indices are unrolled.
+template <int kOx, int kOy>
+__device__ __forceinline__ f32x4 mma_mx_c(const i32x8 &x, const i32x8 &y, const f32x4 &c,
+                                          uint32_t sx, uint32_t sy)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, c, 0, 0, kOx, (int)sx, kOy,
+                                                            (int)sy);
+}
+__device__ __forceinline__ f32x4 mma_mx(const i32x8 &x, const i32x8 &y, const f32x4 &c,
+                                        uint32_t sx, uint32_t sy, int ox, int oy)
+{
+    switch (ox * 4 + oy) {
+    case 0: return mma_mx_c<0, 0>(x, y, c, sx, sy);
+    case 1: return mma_mx_c<0, 1>(x, y, c, sx, sy);
+    case 2: return mma_mx_c<0, 2>(x, y, c, sx, sy);
+    case 3: return mma_mx_c<0, 3>(x, y, c, sx, sy);
+    case 4: return mma_mx_c<1, 0>(x, y, c, sx, sy);
+    case 5: return mma_mx_c<1, 1>(x, y, c, sx, sy);
+    case 6: return mma_mx_c<1, 2>(x, y, c, sx, sy);
+    case 7: return mma_mx_c<1, 3>(x, y, c, sx, sy);
+    case 8: return mma_mx_c<2, 0>(x, y, c, sx, sy);
+    case 9: return mma_mx_c<2, 1>(x, y, c, sx, sy);
+    case 10: return mma_mx_c<2, 2>(x, y, c, sx, sy);
+    case 11: return mma_mx_c<2, 3>(x, y, c, sx, sy);
+    case 12: return mma_mx_c<3, 0>(x, y, c, sx, sy);
+    case 13: return mma_mx_c<3, 1>(x, y, c, sx, sy);
+    case 14: return mma_mx_c<3, 2>(x, y, c, sx, sy);
+    default: return mma_mx_c<3, 3>(x, y, c, sx, sy);
+    }
 }
 // Offsets of A fragment i (rows 16 i ..) and B fragment j (rows 32 (j >> 1)
 // + 4 (j & 1) + interleave) from the lane's base.
@@ -672,7 +719,8 @@ struct Quad<kBf16> {
     // reads from; dma(v) issues the half's load v.
     template <int kH, class Dma>
     __device__ __forceinline__ static void half(Frags &f, f32x4 (&acc)[8][8], const char *smem,
-                                                const QuadLane &l, int a_off, int b_off, Dma &&dma)
+                                                const QuadLane &l, int a_off, int b_off,
+                                                const MxScales &, Dma &&dma)
     {
         constexpr int s = 1 - kH;
         const int ba = opaque(l.a[s] + a_off), bb = opaque(l.b[s] + b_off);
@@ -698,8 +746,9 @@ struct Quad<kBf16> {
     }
 };
 
-template <>
-struct Quad<kFp8> {
+template <bool kMxScaled>
+struct QuadF8 {
+    // e4m3 with per-tensor scales (kMxScaled false) or MXFP8 block scales.
     // half 0 runs blocks (i, j < 4), half 1 blocks (i, j >= 4), both i-major.
     // Half 0 reads B fragments 4..7 of step t; half 1 reads B fragments 0..3
     // of step t+1 and A fragment i of step t+1 right after the last MFMA
@@ -735,7 +784,8 @@ struct Quad<kFp8> {
     }
     template <int kH, class Dma>
     __device__ __forceinline__ static void half(Frags &f, f32x4 (&acc)[8][8], const char *smem,
-                                                const QuadLane &l, int a_off, int b_off, Dma &&dma)
+                                                const QuadLane &l, int a_off, int b_off,
+                                                const MxScales &sc, Dma &&dma)
     {
         int ba0 = 0, ba1 = 0;
         if (kH == 1)
@@ -744,7 +794,11 @@ struct Quad<kFp8> {
 #pragma unroll
         for (int n = 0; n < kMfmas; ++n) {
             const int i = n >> 2, j = 4 * kH + (n & 3);
-            acc[i][j] = F::mma(f.b[j], f.a[i], acc[i][j]);
+            if (kMxScaled)
+                acc[i][j] = mma_mx(f.b[j], f.a[i], acc[i][j], sc.b[j >> 2], sc.a[i >> 2], j & 3,
+                                   i & 3);
+            else
+                acc[i][j] = F::mma(f.b[j], f.a[i], acc[i][j]);
 #pragma unroll
             for (int v = 0; v < 8; ++v)
                 if (dma_slot(v) == n)
@@ -763,6 +817,13 @@ struct Quad<kFp8> {
     }
 };
 
+template <>
+struct Quad<kFp8> : QuadF8<false> {
+};
+template <>
+struct Quad<kMx> : QuadF8<true> {
+};
+
 // every memory instruction of a half has an MFMA to follow
 static_assert(Quad<kBf16>::dma_slot(7) < Quad<kBf16>::kMfmas &&
                   Quad<kBf16>::read_slot(15) < Quad<kBf16>::kMfmas, "bf16 slot plan");
@@ -778,15 +839,36 @@ struct QuadCtx {
     int voff_a, voff_b;              // lane's load offsets (swizzled chunk of its row)
     int cb_a, cb_b;                  // byte of that chunk inside a K step
     QuadLane l;
+    // MXFP8 only: the packed scales (hkg_mx_pack_scales layout) and the byte
+    // offsets of this wave's 128-row groups in them at K step 0
+    __amdgpu_buffer_rsrc_t rsa, rsb;
+    int sa_group, sb_group;
 };
+
+// MXFP8: this lane's scales of K step k (one 8-byte load per operand; steps
+// past the end read other groups' or out-of-range bytes and are never used).
+__device__ __forceinline__ MxScales mx_load_scales(const QuadCtx &c, int lane, int k)
+{
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const int so = __builtin_amdgcn_readfirstlane(k * 512);
+    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(c.rsa, lane * 8, c.sa_group + so, 0);
+    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(c.rsb, lane * 8, c.sb_group + so, 0);
+    return MxScales{{a[0], a[1]}, {b[0], b[1]}};
+}
 
 // K step t: the loads it issues are of step t+2; kMasked: that step may be a
 // partial or absent one (lanes whose chunk lies past K load zeros).
+// MXFP8: sc holds the scales of step t on entry and of step t+1 on exit (the
+// load is issued first, so the barrier's vmcnt wait also covers it).
 template <int kDtype, bool kMasked>
 __device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4 (&acc)[8][8],
-                                          const QuadCtx &c, int ldk, int t)
+                                          MxScales &sc, const QuadCtx &c, int ldk, int t,
+                                          int lane)
 {
     using Q = Quad<kDtype>;
+    MxScales next;
+    if constexpr (kDtype == kMx)
+        next = mx_load_scales(c, lane, t + 1);
     const int k2 = t + 2;
     const int va = kMasked ? kstep_voff(c.voff_a, c.cb_a, k2, ldk) : c.voff_a;
     const int vb = kMasked ? kstep_voff(c.voff_b, c.cb_b, k2, ldk) : c.voff_b;
@@ -801,13 +883,15 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4
     char *const a_dst = c.smem + pa;
     char *const b_dst = c.smem + kBRing + pb2;
     __builtin_amdgcn_sched_barrier(0);
-    Q::template half<0>(f, acc, c.smem, c.l, c.a_rows + pa, c.b_rows + pb,
+    Q::template half<0>(f, acc, c.smem, c.l, c.a_rows + pa, c.b_rows + pb, sc,
                         [&](int v) { dma_rows(c.rb, b_dst, c.wave + 4 * v, vb, so, ldk); });
     wait_lgkmcnt0();
     wait_vmcnt<8>();                               // step t+1 landed (B(t+2) in flight)
     block_barrier();
-    Q::template half<1>(f, acc, c.smem, c.l, c.a_rows + pa1, c.b_rows + pb1,
+    Q::template half<1>(f, acc, c.smem, c.l, c.a_rows + pa1, c.b_rows + pb1, sc,
                         [&](int v) { dma_rows(c.ra, a_dst, c.wave + 4 * v, va, so, ldk); });
+    if constexpr (kDtype == kMx)
+        sc = next;
 }
 
 template <int kDtype>
@@ -840,6 +924,15 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(const GemmParams p)
     c.voff_a = r8 * ldk + c.cb_a;
     c.voff_b = r8 * ldk + c.cb_b;
     c.l = quad_lane(lane);
+    MxScales sc = {{0u, 0u}, {0u, 0u}};
+    if constexpr (kDtype == kMx) {
+        // 128-row group g = 2 tm + (w >> 1) of A, 2 tn + (w & 1) of B;
+        // each group holds nk K steps of 64 lanes x 8 bytes
+        c.rsa = make_rsrc(p.SA, p.sa_bytes);
+        c.rsb = make_rsrc(p.SB, p.sb_bytes);
+        c.sa_group = __builtin_amdgcn_readfirstlane((2 * tm + (c.wave >> 1)) * p.nk * 512);
+        c.sb_group = __builtin_amdgcn_readfirstlane((2 * tn + (c.wave & 1)) * p.nk * 512);
+    }
 
     f32x4 acc[8][8];
 #pragma unroll
@@ -851,6 +944,8 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(const GemmParams p)
     using Q = Quad<kDtype>;
     const int nk = p.nk;
     if (nk > 0) {
+        if constexpr (kDtype == kMx)
+            sc = mx_load_scales(c, lane, 0);       // issued first: covered by the wait below
         // K steps 0 and 1 (for nk == 1 the loads of step 1 write zeros).
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -864,10 +959,60 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(const GemmParams p)
         typename Q::Frags f;
         Q::read_first(f, smem, c.l, c.a_rows, c.b_rows);
         for (int t = 0; t < nk; ++t)
-            quad_step<kDtype, true>(f, acc, c, ldk, t);
+            quad_step<kDtype, true>(f, acc, sc, c, ldk, t, lane);
         wait_vmcnt<0>();
     }
     store_tile<8>(p, tm, tn, c.a_rows / kRowBytes, (c.b_rows - kBRing) / kRowBytes, lane, acc);
+}
+
+// MXFP8 scale packing: entry e (0..7) of lane l at K step t of 128-row group
+// g is the E8M0 scale of row 128 g + rowmap(e, l) and k block 4 t + l / 16,
+// where rowmap is the row the 4-wave kernel's fragment e gives lane l:
+// A: 16 e + x; B: 32 (e >> 1) + 4 (e & 1) + (x & 3) + 8 (x >> 2), x = l % 16.
+// Rows past `rows` and blocks past `nblk` get 127 (scale 1; their elements
+// are zeros).  One workgroup handles one group g and kPackSteps K steps: it
+// reads the 128 x 4 kPackSteps source bytes row by row (coalesced) into LDS,
+// then writes the kPackSteps x 512 packed bytes in order.
+constexpr int kPackSteps = 16;
+constexpr int kPackCols = 4 * kPackSteps;   // source blocks per workgroup
+
+__global__ __launch_bounds__(256) void mx_pack_kernel(int operand, int rows, int nblk, int nk,
+                                                      const uint8_t *src, uint64_t *dst)
+{
+    __shared__ uint8_t tile[128][kPackCols];
+    const int64_t g = blockIdx.x;
+    const int t0 = blockIdx.y * kPackSteps;
+    const int b0 = 4 * t0;
+    // all loads first (a fixed trip count, unrolled), then the LDS stores, so
+    // the loads overlap instead of each store waiting for its own load
+    constexpr int kPer = 128 * kPackCols / 256;
+    uint8_t v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = threadIdx.x + 256 * k;
+        const int64_t row = 128 * g + i / kPackCols;
+        const int blk = b0 + i % kPackCols;
+        v[k] = (row < rows && blk < nblk) ? src[row * nblk + blk] : uint8_t(127);
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        const int i = threadIdx.x + 256 * k;
+        tile[i / kPackCols][i % kPackCols] = v[k];
+    }
+    __syncthreads();
+    const int steps = min(kPackSteps, nk - t0);
+    for (int i = threadIdx.x; i < steps * 64; i += 256) {
+        const int tt = i >> 6, l = i & 63;
+        const int x = l & 15, cblk = 4 * tt + (l >> 4);
+        uint64_t v = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int r_in = operand == 0 ? 16 * e + x
+                                          : 32 * (e >> 1) + 4 * (e & 1) + (x & 3) + 8 * (x >> 2);
+            v |= (uint64_t)tile[r_in][cblk] << (8 * e);
+        }
+        dst[(g * nk + t0 + tt) * 64 + l] = v;
+    }
 }
 
 __global__ void remap_tiles_kernel(int Gm, int Gn, int W, int C, int32_t *out)
@@ -886,7 +1031,11 @@ __global__ void remap_tiles_kernel(int Gm, int Gn, int W, int C, int32_t *out)
 hipError_t launch_gemm(Dtype dt, Schedule s, const GemmParams &p, hipStream_t stream)
 {
     const dim3 grid(p.Gm * p.Gn), block(512);
-    if (s == kInterleave) {
+    if (dt == kMx) {
+        if (s != kInterleave)
+            return hipErrorInvalidValue;   // only the 4-wave kernel has the scaled MFMA path
+        hipLaunchKernelGGL(gemm4_kernel<kMx>, grid, dim3(256), 0, stream, p);
+    } else if (s == kInterleave) {
         if (dt == kBf16)
             hipLaunchKernelGGL(gemm4_kernel<kBf16>, grid, dim3(256), 0, stream, p);
         else
@@ -902,6 +1051,17 @@ hipError_t launch_gemm(Dtype dt, Schedule s, const GemmParams &p, hipStream_t st
         else
             hipLaunchKernelGGL((gemm_kernel<kFp8, kLockstep>), grid, block, 0, stream, p);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_pack(int operand, int rows, int nblk, int nk, int groups,
+                          const uint8_t *src, uint8_t *dst, hipStream_t stream)
+{
+    if (groups == 0 || nk == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)groups, (unsigned)((nk + kPackSteps - 1) / kPackSteps));
+    hipLaunchKernelGGL(mx_pack_kernel, grid, dim3(256), 0, stream, operand, rows, nblk, nk, src,
+                       reinterpret_cast<uint64_t *>(dst));
     return hipGetLastError();
 }
 

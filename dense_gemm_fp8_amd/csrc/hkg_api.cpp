@@ -19,8 +19,16 @@ constexpr int64_t kKStepBf16 = 64;     // K elements per step (one 128-byte LDS 
 constexpr int64_t kKStepFp8 = 128;
 constexpr int64_t kKAlignBf16 = 8;     // K granule: operand rows stay 16-byte aligned
 constexpr int64_t kKAlignFp8 = 16;
+constexpr int64_t kKAlignMx = 32;      // one E8M0 scale per 32 elements along K
+constexpr int64_t kMxGroupRows = 128;  // packed scales: 128-row groups ...
+constexpr int64_t kMxStepBytes = 512;  // ... of 64 lanes x 8 bytes per K step
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t mx_packed_bytes(int64_t rows, int64_t K)
+{
+    return ceil_div(rows, kMxGroupRows) * ceil_div(K, kKStepFp8) * kMxStepBytes;
+}
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -121,14 +129,29 @@ int resolve_opts(const hkg_gemm_opts *opts, int64_t Gm, int64_t Gn, int32_t *W, 
 }
 
 int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const void *B, float sa,
-         float sb, void *C, float *C_f32, void *stream, const hkg_gemm_opts *opts)
+         float sb, const void *SA, const void *SB, void *C, float *C_f32, void *stream,
+         const hkg_gemm_opts *opts)
 {
     const int64_t kstep = dt == hkg::kBf16 ? kKStepBf16 : kKStepFp8;
-    const int64_t kalign = dt == hkg::kBf16 ? kKAlignBf16 : kKAlignFp8;
+    const int64_t kalign =
+        dt == hkg::kBf16 ? kKAlignBf16 : (dt == hkg::kFp8 ? kKAlignFp8 : kKAlignMx);
     const int64_t elem = dt == hkg::kBf16 ? 2 : 1;
     int rc = validate(M, N, K, kalign, elem, A, B, C, C_f32);
     if (rc != HKG_OK)
         return rc;
+    if (dt == hkg::kMx && M > 0 && N > 0 && K > 0) {
+        if (!SA || !SB)
+            return HKG_ERR_NULL;
+        if (!aligned16(SA) || !aligned16(SB))
+            return HKG_ERR_ALIGN;
+        // the packed scales are read through 32-bit buffer ranges
+        if (mx_packed_bytes(M, K) >= (int64_t(1) << 31) || mx_packed_bytes(N, K) >= (int64_t(1) << 31))
+            return HKG_ERR_SIZE;
+    }
+    // only the 4-wave kernel has the block-scaled MFMA path
+    if (dt == hkg::kMx && opts && opts->schedule != HKG_SCHED_DEFAULT &&
+        opts->schedule != HKG_SCHED_INTERLEAVE)
+        return HKG_ERR_OPTS;
     const int64_t Gm = ceil_div(M, kTile), Gn = ceil_div(N, kTile);
     int32_t W = 1, Cc = 1;
     hkg::Schedule sched = hkg::kInterleave;
@@ -157,7 +180,11 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
     p.Cc = Cc;
     p.nk = static_cast<int>(ceil_div(K, kstep));
     // The product of the two per-tensor scales, rounded once to fp32.
-    p.scale = dt == hkg::kBf16 ? 1.0f : static_cast<float>(static_cast<double>(sa) * sb);
+    p.scale = dt == hkg::kFp8 ? static_cast<float>(static_cast<double>(sa) * sb) : 1.0f;
+    p.SA = SA;
+    p.SB = SB;
+    p.sa_bytes = dt == hkg::kMx ? static_cast<int>(mx_packed_bytes(M, K)) : 0;
+    p.sb_bytes = dt == hkg::kMx ? static_cast<int>(mx_packed_bytes(N, K)) : 0;
 
     hipError_t e = hkg::launch_gemm(dt, sched, p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
@@ -174,34 +201,89 @@ extern "C" {
 int hkg_gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
                   float *C_f32, void *stream)
 {
-    return gemm(hkg::kBf16, M, N, K, A, B, 1.0f, 1.0f, C, C_f32, stream, nullptr);
+    return gemm(hkg::kBf16, M, N, K, A, B, 1.0f, 1.0f, nullptr, nullptr, C, C_f32, stream,
+                nullptr);
 }
 
 int hkg_gemm_fp8(int64_t M, int64_t N, int64_t K, const void *A, const void *B, float scale_a,
                  float scale_b, void *C, float *C_f32, void *stream)
 {
-    return gemm(hkg::kFp8, M, N, K, A, B, scale_a, scale_b, C, C_f32, stream, nullptr);
+    return gemm(hkg::kFp8, M, N, K, A, B, scale_a, scale_b, nullptr, nullptr, C, C_f32, stream,
+                nullptr);
 }
 
 int hkg_gemm_bf16_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *B, void *C,
                      float *C_f32, void *stream, const hkg_gemm_opts *opts)
 {
-    return gemm(hkg::kBf16, M, N, K, A, B, 1.0f, 1.0f, C, C_f32, stream, opts);
+    return gemm(hkg::kBf16, M, N, K, A, B, 1.0f, 1.0f, nullptr, nullptr, C, C_f32, stream, opts);
 }
 
 int hkg_gemm_fp8_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                     float scale_a, float scale_b, void *C, float *C_f32, void *stream,
                     const hkg_gemm_opts *opts)
 {
-    return gemm(hkg::kFp8, M, N, K, A, B, scale_a, scale_b, C, C_f32, stream, opts);
+    return gemm(hkg::kFp8, M, N, K, A, B, scale_a, scale_b, nullptr, nullptr, C, C_f32, stream,
+                opts);
+}
+
+int hkg_gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                   const void *SA_packed, const void *SB_packed, void *C, float *C_f32,
+                   void *stream)
+{
+    return gemm(hkg::kMx, M, N, K, A, B, 1.0f, 1.0f, SA_packed, SB_packed, C, C_f32, stream,
+                nullptr);
+}
+
+int hkg_gemm_mxfp8_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                      const void *SA_packed, const void *SB_packed, void *C, float *C_f32,
+                      void *stream, const hkg_gemm_opts *opts)
+{
+    return gemm(hkg::kMx, M, N, K, A, B, 1.0f, 1.0f, SA_packed, SB_packed, C, C_f32, stream,
+                opts);
+}
+
+int64_t hkg_mx_packed_scale_bytes(int64_t rows, int64_t K)
+{
+    if (rows < 0 || K < 0 || K % kKAlignMx)
+        return HKG_ERR_SHAPE;
+    return mx_packed_bytes(rows, K);
+}
+
+int hkg_mx_pack_scales(int32_t operand, int64_t rows, int64_t K, const void *scales,
+                       void *packed, void *stream)
+{
+    if (operand != HKG_MX_OPERAND_A && operand != HKG_MX_OPERAND_B)
+        return HKG_ERR_OPTS;
+    if (rows < 0 || K < 0 || K % kKAlignMx)
+        return HKG_ERR_SHAPE;
+    if (rows == 0 || K == 0)
+        return HKG_OK;
+    if (!scales || !packed)
+        return HKG_ERR_NULL;
+    if (!aligned16(packed))
+        return HKG_ERR_ALIGN;
+    // the same K bound as the GEMM (one 256-row e4m3 panel below 2 GiB)
+    if (rows >= (int64_t(1) << 31) || kTile * K >= (int64_t(1) << 31) ||
+        mx_packed_bytes(rows, K) >= (int64_t(1) << 31))
+        return HKG_ERR_SIZE;
+    hipError_t e = hkg::launch_mx_pack(
+        operand, static_cast<int>(rows), static_cast<int>(K / kKAlignMx),
+        static_cast<int>(ceil_div(K, kKStepFp8)), static_cast<int>(ceil_div(rows, kMxGroupRows)),
+        static_cast<const uint8_t *>(scales), static_cast<uint8_t *>(packed),
+        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        g_last_hip_error = static_cast<int>(e);
+        return HKG_ERR_LAUNCH;
+    }
+    return HKG_OK;
 }
 
 int hkg_default_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *W, int32_t *C)
 {
     if (!W || !C)
         return HKG_ERR_NULL;
-    const int64_t kalign = dtype == 0 ? kKAlignBf16 : kKAlignFp8;
-    if ((dtype != 0 && dtype != 1) || M <= 0 || N <= 0 || K < 0 || K % kalign)
+    const int64_t kalign = dtype == 0 ? kKAlignBf16 : (dtype == 1 ? kKAlignFp8 : kKAlignMx);
+    if ((dtype < 0 || dtype > 2) || M <= 0 || N <= 0 || K < 0 || K % kalign)
         return HKG_ERR_SHAPE;
     default_remap(ceil_div(M, kTile), ceil_div(N, kTile), W, C);
     return HKG_OK;
@@ -251,7 +333,8 @@ const char *hkg_status_string(int status)
     switch (status) {
     case HKG_OK: return "ok";
     case HKG_ERR_NULL: return "a required pointer is NULL";
-    case HKG_ERR_SHAPE: return "unsupported shape (negative, or K not a multiple of 8 bf16 / 16 e4m3)";
+    case HKG_ERR_SHAPE:
+        return "unsupported shape (negative, or K not a multiple of 8 bf16 / 16 e4m3 / 32 MXFP8)";
     case HKG_ERR_ALIGN: return "pointer not 16-byte aligned";
     case HKG_ERR_SIZE: return "operand panel exceeds the 32-bit buffer range";
     case HKG_ERR_OPTS: return "invalid hkg_gemm_opts";

@@ -17,13 +17,20 @@ struct GemmParams {
     int Gm, Gn;         // tile grid (M/256, N/256)
     int W, Cc;          // remap window height and per-XCD chunk
     int nk;             // number of K steps
-    float scale;        // fp32(scale_a * scale_b) for e4m3, 1 for bf16
+    float scale;        // fp32(scale_a * scale_b) for e4m3, 1 for bf16 and MXFP8
+    const void *SA;     // MXFP8: packed E8M0 scales of A (see hkg_mx_pack_scales), else null
+    const void *SB;     // MXFP8: packed E8M0 scales of B
+    int sa_bytes;       // sizes of the packed scale buffers
+    int sb_bytes;
 };
 
-enum Dtype { kBf16 = 0, kFp8 = 1 };
+enum Dtype { kBf16 = 0, kFp8 = 1, kMx = 2 };
 enum Schedule { kPingPong = 0, kLockstep = 1, kInterleave = 2 };
 
 hipError_t launch_gemm(Dtype dt, Schedule s, const GemmParams &p, hipStream_t stream);
 hipError_t launch_remap_tiles(int Gm, int Gn, int W, int C, int32_t *out, hipStream_t stream);
+// MXFP8 scale packing: src [rows][nblk] E8M0 bytes -> dst, groups x nk x 64 lanes x 8 bytes.
+hipError_t launch_mx_pack(int operand, int rows, int nblk, int nk, int groups,
+                          const uint8_t *src, uint8_t *dst, hipStream_t stream);
 
 }  // namespace hkg

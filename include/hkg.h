@@ -43,7 +43,8 @@ extern "C" {
 typedef enum {
     HKG_OK = 0,
     HKG_ERR_NULL = -1,    /* a required pointer is NULL                              */
-    HKG_ERR_SHAPE = -2,   /* M, N, K negative, or K not a multiple of 8 (bf16) / 16 (e4m3) */
+    HKG_ERR_SHAPE = -2,   /* M, N, K negative, or K not a multiple of 8 (bf16) / 16 (e4m3)
+                             / 32 (MXFP8)                                            */
     HKG_ERR_ALIGN = -3,   /* a pointer is not 16-byte aligned                        */
     HKG_ERR_SIZE = -4,    /* a per-tile operand panel exceeds the 32-bit buffer range */
     HKG_ERR_OPTS = -5,    /* invalid hkg_gemm_opts                                   */
@@ -111,8 +112,58 @@ int hkg_gemm_fp8_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *
                     const hkg_gemm_opts *opts);
 
 /*
+ * MXFP8 GEMM: the "MXFP8" input type of the HipKittens L2 note (section 3,
+ * "Target operation" table), in the OCP Microscaling Formats v1.0 encoding.
+ *   A [M][K], B [N][K]: e4m3 bytes, row-major
+ *   each run of 32 consecutive elements along K of a row has one E8M0 scale
+ *   byte E standing for 2^(E-127) (0xFF = NaN); element k of row r of A means
+ *   e4m3(A[r][k]) * 2^(SA[r][k/32]-127), likewise for B
+ *   SA_packed, SB_packed: those scales after hkg_mx_pack_scales (operand A
+ *   resp. B), device, 16-byte aligned, hkg_mx_packed_scale_bytes(M resp. N, K)
+ *   bytes
+ *   C [M][N] bfloat16 = RNE(fp32 accumulator); C_f32: NULL or that fp32 value
+ * Shapes: any M, N >= 0; K >= 0 with K % 32 == 0.  Otherwise as the bf16
+ * entry point.  Runs the 4-wave interleave kernel (opts->schedule must be
+ * HKG_SCHED_DEFAULT or HKG_SCHED_INTERLEAVE, else HKG_ERR_OPTS).
+ */
+int hkg_gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                   const void *SA_packed, const void *SB_packed, void *C, float *C_f32,
+                   void *stream);
+int hkg_gemm_mxfp8_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+                      const void *SA_packed, const void *SB_packed, void *C, float *C_f32,
+                      void *stream, const hkg_gemm_opts *opts);
+
+/* Which operand a packed scale buffer is for. */
+enum { HKG_MX_OPERAND_A = 0, HKG_MX_OPERAND_B = 1 };
+
+/*
+ * Bytes of the packed scales of one MXFP8 operand with `rows` rows:
+ * ceil(rows/128) * ceil(K/128) * 512 (host only).  Negative hkg_status
+ * (HKG_ERR_SHAPE) if rows < 0, K < 0 or K % 32 != 0.
+ */
+int64_t hkg_mx_packed_scale_bytes(int64_t rows, int64_t K);
+
+/*
+ * Rearrange one operand's E8M0 scales into the order the GEMM kernel reads.
+ *   scales  [rows][K/32] bytes, row-major, device (no alignment needed)
+ *   packed  device, 16-byte aligned, hkg_mx_packed_scale_bytes(rows, K) bytes,
+ *           caller-owned; must not overlap `scales`
+ * Layout: byte e (0..7) of lane l (0..63) of K step t of 128-row group g, at
+ * offset ((g * ceil(K/128) + t) * 64 + l) * 8 + e, is the scale of row
+ * 128 g + rho(e, l) and k block 4 t + l / 16, where with x = l % 16
+ *   operand A: rho = 16 e + x
+ *   operand B: rho = 32 (e >> 1) + 4 (e & 1) + (x & 3) + 8 (x >> 2)
+ * Rows past `rows` and blocks past K/32 read 127 (scale 1).  Enqueued on
+ * `stream`; weights' scales can be packed once and reused.  HKG_ERR_SIZE if
+ * K >= 2^23 (the GEMM's own bound) or the packed size reaches 2 GiB.
+ */
+int hkg_mx_pack_scales(int32_t operand, int64_t rows, int64_t K, const void *scales,
+                       void *packed, void *stream);
+
+/*
  * The (W, C) the library uses for HKG_REMAP_DEFAULT on a shape (host only, no
- * HIP call).  dtype: 0 = bf16, 1 = fp8.  Returns HKG_ERR_NULL/SHAPE on bad input.
+ * HIP call).  dtype: 0 = bf16, 1 = fp8, 2 = MXFP8.  Returns HKG_ERR_NULL/SHAPE
+ * on bad input.
  */
 int hkg_default_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *W, int32_t *C);
 

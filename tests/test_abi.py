@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = hkg.load()
     names = _declared()
-    assert len(names) == 9
+    assert len(names) == 13
     assert sorted(hkg.EXPORTS) == names
     for n in names:
         assert getattr(lib, n) is not None
@@ -102,9 +102,48 @@ def test_remap_rejects_bad_arguments():
 def test_default_remap():
     rc, W, C = hkg.hkg_default_remap(8192, 8192, 8192, 0)
     assert rc == hkg.HKG_OK and (W, C) == (8, 32)
-    assert hkg.hkg_default_remap(8192, 8192, 8192, 2)[0] == hkg.HKG_ERR_SHAPE
+    assert hkg.hkg_default_remap(8192, 8192, 8192, 3)[0] == hkg.HKG_ERR_SHAPE
+    assert hkg.hkg_default_remap(8192, 8192, 8192, 2)[0] == hkg.HKG_OK       # MXFP8
+    assert hkg.hkg_default_remap(8192, 8192, 8176, 2)[0] == hkg.HKG_ERR_SHAPE
     assert hkg.hkg_default_remap(8192, 8192, 8190, 0)[0] == hkg.HKG_ERR_SHAPE
     rc, W, C = hkg.hkg_default_remap(256, 256, 256, 1)
     assert rc == hkg.HKG_OK and (W, C) == (1, 1)
     rc, W, C = hkg.hkg_default_remap(300, 9000, 64, 0)     # ragged: 2 x 36 tiles
     assert rc == hkg.HKG_OK and (W, C) == (2, 10)
+
+
+# ---------------------------------------------------------------- MXFP8 -------------
+
+def test_mx_packed_scale_bytes():
+    # ceil(rows/128) groups x ceil(K/128) K steps x 64 lanes x 8 bytes
+    assert hkg.hkg_mx_packed_scale_bytes(8192, 8192) == 64 * 64 * 512
+    assert hkg.hkg_mx_packed_scale_bytes(129, 160) == 2 * 2 * 512
+    assert hkg.hkg_mx_packed_scale_bytes(1, 32) == 512
+    assert hkg.hkg_mx_packed_scale_bytes(0, 64) == 0
+    assert hkg.hkg_mx_packed_scale_bytes(100, 0) == 0
+    for rows, K in ((-1, 64), (10, -32), (10, 48)):
+        assert hkg.hkg_mx_packed_scale_bytes(rows, K) == hkg.HKG_ERR_SHAPE
+
+
+def test_mx_pack_rejects_bad_arguments():
+    A, B = hkg.HKG_MX_OPERAND_A, hkg.HKG_MX_OPERAND_B
+    assert hkg.hkg_mx_pack_scales(2, 10, 64, FAKE, FAKE, None) == hkg.HKG_ERR_OPTS
+    assert hkg.hkg_mx_pack_scales(A, 10, 48, FAKE, FAKE, None) == hkg.HKG_ERR_SHAPE
+    assert hkg.hkg_mx_pack_scales(B, -1, 64, FAKE, FAKE, None) == hkg.HKG_ERR_SHAPE
+    assert hkg.hkg_mx_pack_scales(A, 10, 64, None, FAKE, None) == hkg.HKG_ERR_NULL
+    assert hkg.hkg_mx_pack_scales(A, 10, 64, FAKE, FAKE + 8, None) == hkg.HKG_ERR_ALIGN
+    assert hkg.hkg_mx_pack_scales(A, 0, 64, None, None, None) == hkg.HKG_OK      # nothing to do
+    assert hkg.hkg_mx_pack_scales(A, 1, 1 << 23, FAKE, FAKE, None) == hkg.HKG_ERR_SIZE
+
+
+def test_mxfp8_validation():
+    g = hkg.hkg_gemm_mxfp8
+    for K in (16, 48, 100):
+        assert g(256, 256, K, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == hkg.HKG_ERR_SHAPE
+    assert g(256, 256, 64, FAKE, FAKE, None, FAKE, FAKE, None, None) == hkg.HKG_ERR_NULL
+    assert g(256, 256, 64, FAKE, FAKE, FAKE, FAKE + 8, FAKE, None, None) == hkg.HKG_ERR_ALIGN
+    assert g(0, 256, 64, None, None, None, None, None, None, None) == hkg.HKG_OK
+    for sched in (hkg.HKG_SCHED_PINGPONG, hkg.HKG_SCHED_LOCKSTEP):
+        o = hkg.make_opts(schedule=sched)
+        assert hkg.hkg_gemm_mxfp8_ex(256, 256, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                     o) == hkg.HKG_ERR_OPTS
