@@ -406,7 +406,13 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
     const int r8 = lane >> 3;
     const int cbytes = ((lane & 7) ^ slot_xor(r8 | (w4 << 3))) << 4;
     const int voff0 = r8 * ldk + cbytes;
-    auto voff = [&](int k) { return kstep_voff(voff0, cbytes, k, ldk); };
+    // K step k covers row bytes [128 k - shift, +128): a partial step is step
+    // 0, whose lanes with a chunk below byte 0 load zeros, and every later
+    // step is whole (the loads of steps past the end are never issued).
+    const int shift = __builtin_amdgcn_readfirstlane(p.nk * kRowBytes - ldk);
+    const int voff_first = cbytes >= shift ? voff0 - shift : kOutOfRange;
+    auto voff = [&](int k) { return k == 0 ? voff_first : voff0; };
+    auto soff = [&](int k) { return k == 0 ? 0 : k * kRowBytes - shift; };
 
     const LaneOffsets lo = lane_offsets(lane);
     f32x4 acc[8][4];
@@ -425,12 +431,12 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
     if (kSched == kLockstep) {
         // Each wave loads its 16 of the 64 row groups of a K step.
         if (nk > 0) {
-            dma_panel_part<4>(ra, a_panel(0), 16 * g, w4, voff(0), 0, ldk);
-            dma_panel_part<4>(rb, b_panel2(0), 16 * g, w4, voff(0), 0, ldk);
+            dma_panel_part<4>(ra, a_panel(0), 16 * g, w4, voff(0), soff(0), ldk);
+            dma_panel_part<4>(rb, b_panel2(0), 16 * g, w4, voff(0), soff(0), ldk);
         }
         if (nk > 1) {
-            dma_panel_part<4>(ra, a_panel(1), 16 * g, w4, voff(1), kRowBytes, ldk);
-            dma_panel_part<4>(rb, b_panel2(1), 16 * g, w4, voff(1), kRowBytes, ldk);
+            dma_panel_part<4>(ra, a_panel(1), 16 * g, w4, voff(1), soff(1), ldk);
+            dma_panel_part<4>(rb, b_panel2(1), 16 * g, w4, voff(1), soff(1), ldk);
             wait_vmcnt<8>();
         } else {
             wait_vmcnt<0>();
@@ -442,9 +448,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
             wait_lgkmcnt0();
             block_barrier();                       // every wave is done with K step t
             if (t + 2 < nk) {
-                const int soff = (t + 2) * kRowBytes;
-                dma_panel_part<4>(ra, a_panel(t), 16 * g, w4, voff(t + 2), soff, ldk);
-                dma_panel_part<4>(rb, b_panel2(t), 16 * g, w4, voff(t + 2), soff, ldk);
+                dma_panel_part<4>(ra, a_panel(t), 16 * g, w4, voff(t + 2), soff(t + 2), ldk);
+                dma_panel_part<4>(rb, b_panel2(t), 16 * g, w4, voff(t + 2), soff(t + 2), ldk);
                 wait_vmcnt<8>();                   // K step t+1 has landed
             } else {
                 wait_vmcnt<0>();
@@ -472,20 +477,20 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
         using P = Pipe<kDtype>;
         typename P::Frags frags;
         if (nk > 0) {   // K step 0: both groups share every panel
-            dma_panel_part<4>(ra, a_panel(0), 16 * g, w4, voff(0), 0, ldk);
-            dma_panel_part<4>(rb, b_panel(0), 16 * g, w4, voff(0), 0, ldk);
+            dma_panel_part<4>(ra, a_panel(0), 16 * g, w4, voff(0), soff(0), ldk);
+            dma_panel_part<4>(rb, b_panel(0), 16 * g, w4, voff(0), soff(0), ldk);
         }
         if (g == 0) {
             if (nk > 1) {
-                dma_panel_part<4>(ra, a_panel(1), 0, w4, voff(1), kRowBytes, ldk);
-                dma_panel_part<4>(rb, b_panel(1), 0, w4, voff(1), kRowBytes, ldk);
+                dma_panel_part<4>(ra, a_panel(1), 0, w4, voff(1), soff(1), ldk);
+                dma_panel_part<4>(rb, b_panel(1), 0, w4, voff(1), soff(1), ldk);
                 wait_vmcnt<8>();                   // K step 0 landed
             } else {
                 wait_vmcnt<0>();
             }
         } else {
             if (nk > 1) {
-                dma_panel_part<4>(rb, b_panel(1), 16, w4, voff(1), kRowBytes, ldk);
+                dma_panel_part<4>(rb, b_panel(1), 16, w4, voff(1), soff(1), ldk);
                 wait_vmcnt<4>();                   // K step 0 landed
             } else {
                 wait_vmcnt<0>();
@@ -509,9 +514,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
                 block_barrier();                   // end of c(t)
                 if (t + 2 < nk) {
                     dma_panel_part<4>(ra, a_panel(t + 2), 0, w4, voff(t + 2),
-                                      (t + 2) * kRowBytes, ldk);
+                                      soff(t + 2), ldk);
                     dma_panel_part<4>(rb, b_panel(t + 2), 0, w4, voff(t + 2),
-                                      (t + 2) * kRowBytes, ldk);
+                                      soff(t + 2), ldk);
                 }
                 P::read(frags, a_frag_base(a_panel(t + 1), 0), b_frag_base(b_panel(t + 1), wn), lo);
                 block_barrier();                   // end of m(t)
@@ -519,9 +524,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
         } else if (nk > 0) {
             // m(-1)
             if (nk > 1)
-                dma_panel_part<4>(ra, a_panel(1), 16, w4, voff(1), kRowBytes, ldk);
+                dma_panel_part<4>(ra, a_panel(1), 16, w4, voff(1), soff(1), ldk);
             if (nk > 2)
-                dma_panel_part<4>(rb, b_panel(2), 16, w4, voff(2), 2 * kRowBytes, ldk);
+                dma_panel_part<4>(rb, b_panel(2), 16, w4, voff(2), soff(2), ldk);
             P::read(frags, a_frag_base(a_panel(0), 1), b_frag_base(b_panel(0), wn), lo);
             if (nk > 2)
                 wait_vmcnt<8>();                   // B rows 128..255 of step 1 landed
@@ -547,10 +552,10 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
                 block_barrier();                   // end of c(t)
                 if (t + 2 < nk)
                     dma_panel_part<4>(ra, a_panel(t + 2), 16, w4, voff(t + 2),
-                                      (t + 2) * kRowBytes, ldk);
+                                      soff(t + 2), ldk);
                 if (t + 3 < nk)
                     dma_panel_part<4>(rb, b_panel(t + 3), 16, w4, voff(t + 3),
-                                      (t + 3) * kRowBytes, ldk);
+                                      soff(t + 3), ldk);
                 P::read(frags, a_frag_base(a_panel(t + 1), 1), b_frag_base(b_panel(t + 1), wn), lo);
                 if (t + 3 < nk)
                     wait_vmcnt<8>();               // B rows 128..255 of step t+2 landed
@@ -838,6 +843,7 @@ struct QuadCtx {
     int a_rows, b_rows;              // LDS bytes of the wave's rows in an A / B panel 0
     int voff_a, voff_b;              // lane's load offsets (swizzled chunk of its row)
     int cb_a, cb_b;                  // byte of that chunk inside a K step
+    int shift;                       // K step k covers row bytes [128 k - shift, +128)
     QuadLane l;
     // MXFP8 only: the packed scales (hkg_mx_pack_scales layout) and the byte
     // offsets of this wave's 128-row groups in them at K step 0
@@ -856,14 +862,25 @@ __device__ __forceinline__ MxScales mx_load_scales(const QuadCtx &c, int lane, i
     return MxScales{{a[0], a[1]}, {b[0], b[1]}};
 }
 
-// K step t: the loads it issues are of step t+2; kMasked: that step may be a
-// partial or absent one (lanes whose chunk lies past K load zeros).
+// LDS byte offsets of the panels step t uses: A panel of step t (step t+1
+// has the other one), B panels of steps t, t+1 and t+2 (being loaded).
+// Carried from step to step so that each step only rotates them.
+struct Ring {
+    int pa, pb, pb1, pb2;
+};
+
+// K step t: the loads it issues are of step t+2.
+// kMasked (MXFP8): step t+2 may be a partial or absent one, and lanes whose
+// chunk lies past K load zeros.  Otherwise the partial step (if any) is step
+// 0, loaded before the loop (c.shift), so every step the loop loads is
+// either whole or absent; an absent one's loads fill a panel no MFMA reads
+// (reads past the tile's rows return zeros, as for any out-of-range offset).
 // MXFP8: sc holds the scales of step t on entry and of step t+1 on exit (the
 // load is issued first, so the barrier's vmcnt wait also covers it).
 template <int kDtype, bool kMasked>
 __device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4 (&acc)[8][8],
                                           MxScales &sc, const QuadCtx &c, int ldk, int t,
-                                          int lane)
+                                          int lane, Ring &rg)
 {
     using Q = Quad<kDtype>;
     MxScales next;
@@ -874,22 +891,19 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4
     const int vb = kMasked ? kstep_voff(c.voff_b, c.cb_b, k2, ldk) : c.voff_b;
     // (readfirstlane keeps loop strength reduction from deriving this scalar
     // offset from the lane's k2 * 128 + chunk byte)
-    const int so = __builtin_amdgcn_readfirstlane(k2 * kRowBytes);
-    const int pa = (t & 1) * kPanelBytes, pa1 = kPanelBytes - pa;
-    const int m3 = t % kBPanels;
-    const int pb = m3 * kPanelBytes;
-    const int pb1 = (m3 == 2 ? 0 : m3 + 1) * kPanelBytes;
-    const int pb2 = (m3 == 0 ? 2 : m3 - 1) * kPanelBytes;
+    const int so = __builtin_amdgcn_readfirstlane(k2 * kRowBytes - c.shift);
+    const int pa = rg.pa, pa1 = rg.pa ^ kPanelBytes;
     char *const a_dst = c.smem + pa;
-    char *const b_dst = c.smem + kBRing + pb2;
+    char *const b_dst = c.smem + kBRing + rg.pb2;
     __builtin_amdgcn_sched_barrier(0);
-    Q::template half<0>(f, acc, c.smem, c.l, c.a_rows + pa, c.b_rows + pb, sc,
+    Q::template half<0>(f, acc, c.smem, c.l, c.a_rows + pa, c.b_rows + rg.pb, sc,
                         [&](int v) { dma_rows(c.rb, b_dst, c.wave + 4 * v, vb, so, ldk); });
     wait_lgkmcnt0();
     wait_vmcnt<8>();                               // step t+1 landed (B(t+2) in flight)
     block_barrier();
-    Q::template half<1>(f, acc, c.smem, c.l, c.a_rows + pa1, c.b_rows + pb1, sc,
+    Q::template half<1>(f, acc, c.smem, c.l, c.a_rows + pa1, c.b_rows + rg.pb1, sc,
                         [&](int v) { dma_rows(c.ra, a_dst, c.wave + 4 * v, va, so, ldk); });
+    rg = Ring{pa1, rg.pb1, rg.pb2, rg.pb};
     if constexpr (kDtype == kMx)
         sc = next;
 }
@@ -924,6 +938,10 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(const GemmParams p)
     c.voff_a = r8 * ldk + c.cb_a;
     c.voff_b = r8 * ldk + c.cb_b;
     c.l = quad_lane(lane);
+    // MXFP8's scales are packed per whole K step, so it keeps a partial step
+    // last (masked); the others take it first.
+    constexpr bool kMasked = kDtype == kMx;
+    c.shift = kMasked ? 0 : __builtin_amdgcn_readfirstlane(p.nk * kRowBytes - ldk);
     MxScales sc = {{0u, 0u}, {0u, 0u}};
     if constexpr (kDtype == kMx) {
         // 128-row group g = 2 tm + (w >> 1) of A, 2 tn + (w & 1) of B;
@@ -946,20 +964,33 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(const GemmParams p)
     if (nk > 0) {
         if constexpr (kDtype == kMx)
             sc = mx_load_scales(c, lane, 0);       // issued first: covered by the wait below
-        // K steps 0 and 1 (for nk == 1 the loads of step 1 write zeros).
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            dma_panel_part<8>(c.ra, smem + k * kPanelBytes, 0, c.wave,
-                              kstep_voff(c.voff_a, c.cb_a, k, ldk), k * kRowBytes, ldk);
-            dma_panel_part<8>(c.rb, smem + kBRing + k * kPanelBytes, 0, c.wave,
-                              kstep_voff(c.voff_b, c.cb_b, k, ldk), k * kRowBytes, ldk);
+        // K steps 0 and 1.  Masked: either may be partial or (step 1, for
+        // nk == 1) absent, and lanes past K load zeros.  Otherwise step 0
+        // covers row bytes [-shift, 128 - shift): lanes whose chunk starts
+        // below 0 load zeros, the rest read `shift` bytes earlier; step 1 is
+        // whole, or absent for nk == 1 (then no MFMA reads its panel).
+        int va0, vb0;
+        if constexpr (kMasked) {
+            va0 = kstep_voff(c.voff_a, c.cb_a, 0, ldk);
+            vb0 = kstep_voff(c.voff_b, c.cb_b, 0, ldk);
+        } else {
+            va0 = c.cb_a >= c.shift ? c.voff_a - c.shift : kOutOfRange;
+            vb0 = c.cb_b >= c.shift ? c.voff_b - c.shift : kOutOfRange;
         }
+        const int va1 = kMasked ? kstep_voff(c.voff_a, c.cb_a, 1, ldk) : c.voff_a;
+        const int vb1 = kMasked ? kstep_voff(c.voff_b, c.cb_b, 1, ldk) : c.voff_b;
+        const int so1 = kRowBytes - c.shift;
+        dma_panel_part<8>(c.ra, smem, 0, c.wave, va0, 0, ldk);
+        dma_panel_part<8>(c.rb, smem + kBRing, 0, c.wave, vb0, 0, ldk);
+        dma_panel_part<8>(c.ra, smem + kPanelBytes, 0, c.wave, va1, so1, ldk);
+        dma_panel_part<8>(c.rb, smem + kBRing + kPanelBytes, 0, c.wave, vb1, so1, ldk);
         wait_vmcnt<16>();                          // step 0 landed
         block_barrier();
         typename Q::Frags f;
         Q::read_first(f, smem, c.l, c.a_rows, c.b_rows);
+        Ring rg = {0, 0, kPanelBytes, 2 * kPanelBytes};
         for (int t = 0; t < nk; ++t)
-            quad_step<kDtype, true>(f, acc, sc, c, ldk, t, lane);
+            quad_step<kDtype, kMasked>(f, acc, sc, c, ldk, t, lane, rg);
         wait_vmcnt<0>();
     }
     store_tile<8>(p, tm, tn, c.a_rows / kRowBytes, (c.b_rows - kBRing) / kRowBytes, lane, acc);
