@@ -68,6 +68,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "kernels.h"
 #include "remap.h"
 
@@ -692,6 +695,59 @@ __device__ __forceinline__ int opaque(int x)
     return x;
 }
 
+// Scalar counterparts.  Instruction selection orders a whole K step (one
+// basic block) as a single graph, so plain arithmetic drifts away from the
+// MFMA slot it is written in and bunches up; bunched, it delays the next
+// MFMA (one wave per SIMD issues only a few other instructions for free in
+// an MFMA's shadow).  Arithmetic whose inputs come out of pin_s() and whose
+// result goes into pin_s() in one slot stays in that slot.
+__device__ __forceinline__ int pin_s(int x)
+{
+    asm volatile("" : "+s"(x));
+    return x;
+}
+// A copy into a fresh register, issued here: a loop-carried value is then
+// rotated in a chosen slot rather than by copies at the loop's back edge.
+__device__ __forceinline__ int mov_s(int x)
+{
+    int y;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(y) : "s"(x));
+    return y;
+}
+
+// f(std::integral_constant<int, n>) for n = 0 .. kN-1, in order: a slot loop
+// whose slot number is a constant in the body without relying on the unroller
+// (a long body exceeds its full-unroll threshold, and a run-time slot number
+// would index the accumulators dynamically).
+template <class F, int... kN>
+__device__ __forceinline__ void for_slots_seq(F &&f, std::integer_sequence<int, kN...>)
+{
+    (f(std::integral_constant<int, kN>{}), ...);
+}
+template <int kN, class F>
+__device__ __forceinline__ void for_slots(F &&f)
+{
+    for_slots_seq(f, std::make_integer_sequence<int, kN>{});
+}
+
+// One wave-wide HBM->LDS load of 8 panel rows into LDS byte ring_off +
+// fixed_off + u * 1 KiB, K step offset soff_kstep, row group u (callers pin
+// ring_off and soff_kstep so that the address arithmetic stays at the call).
+__device__ __forceinline__ void dma_rows_at(__amdgpu_buffer_rsrc_t rs, char *smem, int ring_off,
+                                            int fixed_off, int u, int voff, int soff_kstep,
+                                            int ldk)
+{
+    const int m = ring_off + fixed_off + u * kDmaBytes;
+    const int so = soff_kstep + u * kDmaRows * ldk;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(smem + m), 16, voff, so, 0, 0);
+}
+
+// LDS lane bases of one half's fragment reads (opaque, see above): A and B,
+// one per 16-byte chunk h of a fragment (bf16 fragments use h = 0 only).
+struct Bases {
+    int a[2], b[2];
+};
+
 template <int kDtype>
 struct Quad;
 
@@ -708,6 +764,24 @@ struct Quad<kBf16> {
     // the MFMA after which load v (0..7) / fragment read r (0..15) issues
     __device__ static constexpr int dma_slot(int v) { return 8 * v + 4; }
     __device__ static constexpr int read_slot(int r) { return 3 * r; }
+    // gaps (no memory instruction) for the step's bookkeeping: the next
+    // half's A and B lane bases (late, so that fragments have died to make
+    // room), the three B-ring moves, and the A ring / K offset update after
+    // the half's last load
+    // (base_slot(h, w): half h forms lane base w = A, -, B, - ; -1 = none)
+    __device__ static constexpr int base_slot(int, int w) { return w == 0 ? 50 : w == 2 ? 53 : -1; }
+    __device__ static constexpr int rot_slot(int i) { return 55 + i; }
+    static constexpr int kSlotTail = 61;
+
+    // lane base w of half kH's reads: slice 1 - kH of the panel at off
+    template <int kH, int kW>
+    __device__ __forceinline__ static void base(Bases &bs, const QuadLane &l, int off)
+    {
+        if constexpr (kW == 0)
+            bs.a[0] = opaque(l.a[1 - kH] + off);
+        if constexpr (kW == 2)
+            bs.b[0] = opaque(l.b[1 - kH] + off);
+    }
 
     __device__ __forceinline__ static void read_first(Frags &f, const char *smem,
                                                       const QuadLane &l, int a_off, int b_off)
@@ -720,18 +794,18 @@ struct Quad<kBf16> {
         for (int i = 0; i < 8; ++i)
             f.a[0][i] = *reinterpret_cast<const bf16x8 *>(smem + qa_blk(i) + ba);
     }
-    // a_off / b_off: LDS bytes of the wave's rows of the panels this half
-    // reads from; dma(v) issues the half's load v.
-    template <int kH, class Dma>
+    // bs: this half's read bases; dma(v) issues the half's load v; hook(n)
+    // runs after MFMA n (the caller's per-slot work).
+    template <int kH, class Dma, class Hook>
     __device__ __forceinline__ static void half(Frags &f, f32x4 (&acc)[8][8], const char *smem,
-                                                const QuadLane &l, int a_off, int b_off,
-                                                const MxScales &, Dma &&dma)
+                                                const Bases &bs, const MxScales &, Dma &&dma,
+                                                Hook &&hook)
     {
         constexpr int s = 1 - kH;
-        const int ba = opaque(l.a[s] + a_off), bb = opaque(l.b[s] + b_off);
-#pragma unroll
-        for (int n = 0; n < kMfmas; ++n) {
-            const int i = n >> 3, j = n & 7;
+        const int ba = bs.a[0], bb = bs.b[0];
+        for_slots<kMfmas>([&](auto slot) __attribute__((always_inline)) {
+            constexpr int n = decltype(slot)::value;
+            constexpr int i = n >> 3, j = n & 7;
             acc[i][j] = F::mma(f.b[kH][j], f.a[kH][i], acc[i][j]);
 #pragma unroll
             for (int v = 0; v < 8; ++v)
@@ -746,8 +820,9 @@ struct Quad<kBf16> {
                 else
                     f.a[s][r - 8] = *reinterpret_cast<const bf16x8 *>(smem + qa_blk(r - 8) + ba);
             }
+            hook(slot);
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     }
 };
 
@@ -768,6 +843,24 @@ struct QuadF8 {
     __device__ static constexpr int dma_slot(int v) { return 4 * v + 1; }
     // B fragment 4 + r (half 0) or r (half 1)
     __device__ static constexpr int b_read_slot(int h, int r) { return h == 0 ? 4 * r + 2 : r; }
+    // bookkeeping gaps, as for bf16 (no load or read there in either half)
+    // (lane bases w = A chunk 0, A chunk 1, B chunk 0, B chunk 1; no slot
+    // just before a load slot, whose address arithmetic tends to move up a gap)
+    __device__ static constexpr int base_slot(int h, int w) { return (h == 0 ? 18 : 6) + 4 * w; }
+    __device__ static constexpr int rot_slot(int i) { return 20 + 4 * i; }
+    static constexpr int kSlotTail = 30;
+
+    // lane base w of half kH's reads at panel offset off (half 0 reads B only)
+    template <int kH, int kW>
+    __device__ __forceinline__ static void base(Bases &bs, const QuadLane &l, int off)
+    {
+        if constexpr (kW < 2) {
+            if constexpr (kH == 1)
+                bs.a[kW] = opaque(l.a[kW] + off);
+        } else {
+            bs.b[kW - 2] = opaque(l.b[kW - 2] + off);
+        }
+    }
 
     __device__ __forceinline__ static i32x8 frag(const char *smem, int blk, int base0, int base1)
     {
@@ -787,18 +880,15 @@ struct QuadF8 {
         for (int i = 0; i < 8; ++i)
             f.a[i] = frag(smem, qa_blk(i), ba0, ba1);
     }
-    template <int kH, class Dma>
+    template <int kH, class Dma, class Hook>
     __device__ __forceinline__ static void half(Frags &f, f32x4 (&acc)[8][8], const char *smem,
-                                                const QuadLane &l, int a_off, int b_off,
-                                                const MxScales &sc, Dma &&dma)
+                                                const Bases &bs, const MxScales &sc, Dma &&dma,
+                                                Hook &&hook)
     {
-        int ba0 = 0, ba1 = 0;
-        if (kH == 1)
-            ba0 = opaque(l.a[0] + a_off), ba1 = opaque(l.a[1] + a_off);
-        const int bb0 = opaque(l.b[0] + b_off), bb1 = opaque(l.b[1] + b_off);
-#pragma unroll
-        for (int n = 0; n < kMfmas; ++n) {
-            const int i = n >> 2, j = 4 * kH + (n & 3);
+        const int ba0 = bs.a[0], ba1 = bs.a[1], bb0 = bs.b[0], bb1 = bs.b[1];
+        for_slots<kMfmas>([&](auto slot) __attribute__((always_inline)) {
+            constexpr int n = decltype(slot)::value;
+            constexpr int i = n >> 2, j = 4 * kH + (n & 3);
             if (kMxScaled)
                 acc[i][j] = mma_mx(f.b[j], f.a[i], acc[i][j], sc.b[j >> 2], sc.a[i >> 2], j & 3,
                                    i & 3);
@@ -817,8 +907,9 @@ struct QuadF8 {
             }
             if (kH == 1 && (n & 3) == 3)
                 f.a[i] = frag(smem, qa_blk(i), ba0, ba1);
+            hook(slot);
             __builtin_amdgcn_sched_barrier(0);
-        }
+        });
     }
 };
 
@@ -834,6 +925,17 @@ static_assert(Quad<kBf16>::dma_slot(7) < Quad<kBf16>::kMfmas &&
                   Quad<kBf16>::read_slot(15) < Quad<kBf16>::kMfmas, "bf16 slot plan");
 static_assert(Quad<kFp8>::dma_slot(7) < Quad<kFp8>::kMfmas &&
                   Quad<kFp8>::b_read_slot(0, 3) < Quad<kFp8>::kMfmas, "e4m3 slot plan");
+// bookkeeping order in half 1: lane bases, then the B-ring moves, then the
+// tail after the last load
+template <class Q>
+constexpr bool bookkeeping_ok()
+{
+    return Q::base_slot(1, 2) < Q::rot_slot(0) && Q::base_slot(1, 3) < Q::rot_slot(0) &&
+           Q::base_slot(0, 3) < Q::kMfmas && Q::rot_slot(2) < Q::kSlotTail &&
+           Q::kSlotTail > Q::dma_slot(7) && Q::kSlotTail < Q::kMfmas;
+}
+static_assert(bookkeeping_ok<Quad<kBf16>>(), "bf16 bookkeeping slots");
+static_assert(bookkeeping_ok<Quad<kFp8>>(), "e4m3 bookkeeping slots");
 
 // What the 4-wave loop of one workgroup works on.
 struct QuadCtx {
@@ -863,10 +965,10 @@ __device__ __forceinline__ MxScales mx_load_scales(const QuadCtx &c, int lane, i
 }
 
 // LDS byte offsets of the panels step t uses: A panel of step t (step t+1
-// has the other one), B panels of steps t, t+1 and t+2 (being loaded).
-// Carried from step to step so that each step only rotates them.
+// has the other one), B panels of steps t, t+1 and t+2 (being loaded); and
+// the scalar K offset of step t+2's loads.  Carried from step to step.
 struct Ring {
-    int pa, pb, pb1, pb2;
+    int pa, pb, pb1, pb2, so;
 };
 
 // K step t: the loads it issues are of step t+2.
@@ -877,10 +979,14 @@ struct Ring {
 // (reads past the tile's rows return zeros, as for any out-of-range offset).
 // MXFP8: sc holds the scales of step t on entry and of step t+1 on exit (the
 // load is issued first, so the barrier's vmcnt wait also covers it).
+// bs0 holds the bases of half 0 of step t on entry and of step t+1 on exit.
+// All of the step's bookkeeping (next bases, ring rotation, K offset) is
+// issued in fixed MFMA gaps of the halves, none of it at the loop's head or
+// back edge.
 template <int kDtype, bool kMasked>
 __device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4 (&acc)[8][8],
                                           MxScales &sc, const QuadCtx &c, int ldk, int t,
-                                          int lane, Ring &rg)
+                                          int lane, Ring &rg, Bases &bs0)
 {
     using Q = Quad<kDtype>;
     MxScales next;
@@ -889,21 +995,72 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4
     const int k2 = t + 2;
     const int va = kMasked ? kstep_voff(c.voff_a, c.cb_a, k2, ldk) : c.voff_a;
     const int vb = kMasked ? kstep_voff(c.voff_b, c.cb_b, k2, ldk) : c.voff_b;
-    // (readfirstlane keeps loop strength reduction from deriving this scalar
-    // offset from the lane's k2 * 128 + chunk byte)
-    const int so = __builtin_amdgcn_readfirstlane(k2 * kRowBytes - c.shift);
-    const int pa = rg.pa, pa1 = rg.pa ^ kPanelBytes;
-    char *const a_dst = c.smem + pa;
-    char *const b_dst = c.smem + kBRing + rg.pb2;
+    // Each ring value is threaded through one chain of pins in program
+    // order (every pin is then its value's last use, so none needs a copy).
+    int pa = rg.pa, pb1 = rg.pb1, pb2 = rg.pb2, so = rg.so;
+    // lane base w of the half reading slice 0 (half 1) or 1 (next step's
+    // half 0) of step t+1: A panel pa ^ 32 KiB, B panel pb1
+    auto next_base = [&](Bases &bs, auto kh, auto w) __attribute__((always_inline)) {
+        constexpr int kW = decltype(w)::value;
+        if constexpr (kW < 2) {
+            pa = pin_s(pa);
+            Q::template base<decltype(kh)::value, kW>(bs, c.l,
+                                                      pin_s(c.a_rows + (pa ^ kPanelBytes)));
+        } else {
+            pb1 = pin_s(pb1);
+            Q::template base<decltype(kh)::value, kW>(bs, c.l, pin_s(c.b_rows + pb1));
+        }
+    };
+    // (kh: the half whose bases these are; the running half is the other one)
+    auto bases_at = [&](Bases &bs, auto kh, auto slot) __attribute__((always_inline)) {
+        constexpr int n = decltype(slot)::value;
+        if constexpr (n == Q::base_slot(1 - decltype(kh)::value, 0))
+            next_base(bs, kh, std::integral_constant<int, 0>{});
+        if constexpr (n == Q::base_slot(1 - decltype(kh)::value, 1))
+            next_base(bs, kh, std::integral_constant<int, 1>{});
+        if constexpr (n == Q::base_slot(1 - decltype(kh)::value, 2))
+            next_base(bs, kh, std::integral_constant<int, 2>{});
+        if constexpr (n == Q::base_slot(1 - decltype(kh)::value, 3))
+            next_base(bs, kh, std::integral_constant<int, 3>{});
+    };
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    Bases bs1;
+    Ring nr;
     __builtin_amdgcn_sched_barrier(0);
-    Q::template half<0>(f, acc, c.smem, c.l, c.a_rows + pa, c.b_rows + rg.pb, sc,
-                        [&](int v) { dma_rows(c.rb, b_dst, c.wave + 4 * v, vb, so, ldk); });
+    Q::template half<0>(
+        f, acc, c.smem, bs0, sc,
+        [&](int v) {
+            pb2 = pin_s(pb2);
+            so = pin_s(so);
+            dma_rows_at(c.rb, c.smem, pb2, kBRing, c.wave + 4 * v, vb, so, ldk);
+        },
+        [&](auto slot) __attribute__((always_inline)) { bases_at(bs1, H1{}, slot); });
     wait_lgkmcnt0();
     wait_vmcnt<8>();                               // step t+1 landed (B(t+2) in flight)
     block_barrier();
-    Q::template half<1>(f, acc, c.smem, c.l, c.a_rows + pa1, c.b_rows + rg.pb1, sc,
-                        [&](int v) { dma_rows(c.ra, a_dst, c.wave + 4 * v, va, so, ldk); });
-    rg = Ring{pa1, rg.pb1, rg.pb2, rg.pb};
+    Q::template half<1>(
+        f, acc, c.smem, bs1, sc,
+        [&](int v) {
+            pa = pin_s(pa);
+            so = pin_s(so);
+            dma_rows_at(c.ra, c.smem, pa, 0, c.wave + 4 * v, va, so, ldk);
+        },
+        [&](auto slot) __attribute__((always_inline)) {
+            constexpr int n = decltype(slot)::value;
+            bases_at(bs0, H0{}, slot);
+            if constexpr (n == Q::rot_slot(0))
+                nr.pb = mov_s(pb1);
+            if constexpr (n == Q::rot_slot(1))
+                nr.pb1 = mov_s(pb2);
+            if constexpr (n == Q::rot_slot(2))
+                nr.pb2 = mov_s(rg.pb);
+            if constexpr (n == Q::kSlotTail) {
+                nr.pa = pin_s(pin_s(pa) ^ kPanelBytes);
+                nr.so = pin_s(pin_s(so) + kRowBytes);
+            }
+        });
+    rg = nr;
     if constexpr (kDtype == kMx)
         sc = next;
 }
@@ -988,9 +1145,14 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(const GemmParams p)
         block_barrier();
         typename Q::Frags f;
         Q::read_first(f, smem, c.l, c.a_rows, c.b_rows);
-        Ring rg = {0, 0, kPanelBytes, 2 * kPanelBytes};
+        Ring rg = {0, 0, kPanelBytes, 2 * kPanelBytes, 2 * kRowBytes - c.shift};
+        Bases bs0 = {{0, 0}, {0, 0}};
+        Q::template base<0, 0>(bs0, c.l, c.a_rows);
+        Q::template base<0, 1>(bs0, c.l, c.a_rows);
+        Q::template base<0, 2>(bs0, c.l, c.b_rows);
+        Q::template base<0, 3>(bs0, c.l, c.b_rows);
         for (int t = 0; t < nk; ++t)
-            quad_step<kDtype, kMasked>(f, acc, sc, c, ldk, t, lane, rg);
+            quad_step<kDtype, kMasked>(f, acc, sc, c, ldk, t, lane, rg, bs0);
         wait_vmcnt<0>();
     }
     store_tile<8>(p, tm, tn, c.a_rows / kRowBytes, (c.b_rows - kBRing) / kRowBytes, lane, acc);
