@@ -761,8 +761,11 @@ struct Quad<kBf16> {
         bf16x8 a[2][8], b[2][8];   // [slice][block]
     };
     static constexpr int kMfmas = 64;   // per half
-    // the MFMA after which load v (0..7) / fragment read r (0..15) issues
-    __device__ static constexpr int dma_slot(int v) { return 8 * v + 4; }
+    // the MFMA after which load v (0..7) of half h / fragment read r (0..15)
+    // issues; half 1's A loads go early (their panel is free once the
+    // barrier has passed), which leaves them 85 MFMAs to land before the
+    // next barrier waits for them, against 68 when spread like the B loads
+    __device__ static constexpr int dma_slot(int h, int v) { return h == 0 ? 8 * v + 4 : 6 * v + 1; }
     __device__ static constexpr int read_slot(int r) { return 3 * r; }
     // gaps (no memory instruction) for the step's bookkeeping: the next
     // half's A and B lane bases (late, so that fragments have died to make
@@ -809,7 +812,7 @@ struct Quad<kBf16> {
             acc[i][j] = F::mma(f.b[kH][j], f.a[kH][i], acc[i][j]);
 #pragma unroll
             for (int v = 0; v < 8; ++v)
-                if (dma_slot(v) == n)
+                if (dma_slot(kH, v) == n)
                     dma(v);
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -840,7 +843,7 @@ struct QuadF8 {
         i32x8 a[8], b[8];
     };
     static constexpr int kMfmas = 32;   // per half
-    __device__ static constexpr int dma_slot(int v) { return 4 * v + 1; }
+    __device__ static constexpr int dma_slot(int, int v) { return 4 * v + 1; }
     // B fragment 4 + r (half 0) or r (half 1)
     __device__ static constexpr int b_read_slot(int h, int r) { return h == 0 ? 4 * r + 2 : r; }
     // bookkeeping gaps, as for bf16 (no load or read there in either half)
@@ -896,7 +899,7 @@ struct QuadF8 {
                 acc[i][j] = F::mma(f.b[j], f.a[i], acc[i][j]);
 #pragma unroll
             for (int v = 0; v < 8; ++v)
-                if (dma_slot(v) == n)
+                if (dma_slot(kH, v) == n)
                     dma(v);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -921,9 +924,10 @@ struct Quad<kMx> : QuadF8<true> {
 };
 
 // every memory instruction of a half has an MFMA to follow
-static_assert(Quad<kBf16>::dma_slot(7) < Quad<kBf16>::kMfmas &&
+static_assert(Quad<kBf16>::dma_slot(0, 7) < Quad<kBf16>::kMfmas &&
+                  Quad<kBf16>::dma_slot(1, 7) < Quad<kBf16>::kMfmas &&
                   Quad<kBf16>::read_slot(15) < Quad<kBf16>::kMfmas, "bf16 slot plan");
-static_assert(Quad<kFp8>::dma_slot(7) < Quad<kFp8>::kMfmas &&
+static_assert(Quad<kFp8>::dma_slot(0, 7) < Quad<kFp8>::kMfmas &&
                   Quad<kFp8>::b_read_slot(0, 3) < Quad<kFp8>::kMfmas, "e4m3 slot plan");
 // bookkeeping order in half 1: lane bases, then the B-ring moves, then the
 // tail after the last load
@@ -932,7 +936,7 @@ constexpr bool bookkeeping_ok()
 {
     return Q::base_slot(1, 2) < Q::rot_slot(0) && Q::base_slot(1, 3) < Q::rot_slot(0) &&
            Q::base_slot(0, 3) < Q::kMfmas && Q::rot_slot(2) < Q::kSlotTail &&
-           Q::kSlotTail > Q::dma_slot(7) && Q::kSlotTail < Q::kMfmas;
+           Q::kSlotTail > Q::dma_slot(1, 7) && Q::kSlotTail < Q::kMfmas;
 }
 static_assert(bookkeeping_ok<Quad<kBf16>>(), "bf16 bookkeeping slots");
 static_assert(bookkeeping_ok<Quad<kFp8>>(), "e4m3 bookkeeping slots");
