@@ -714,6 +714,12 @@ __device__ __forceinline__ int mov_s(int x)
     asm volatile("s_mov_b32 %0, %1" : "=s"(y) : "s"(x));
     return y;
 }
+__device__ __forceinline__ uint32_t mov_v(uint32_t x)
+{
+    uint32_t y;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+    return y;
+}
 
 // f(std::integral_constant<int, n>) for n = 0 .. kN-1, in order: a slot loop
 // whose slot number is a constant in the body without relying on the unroller
@@ -852,6 +858,11 @@ struct QuadF8 {
     __device__ static constexpr int base_slot(int h, int w) { return (h == 0 ? 18 : 6) + 4 * w; }
     __device__ static constexpr int rot_slot(int i) { return 20 + 4 * i; }
     static constexpr int kSlotTail = 30;
+    // MXFP8 only: half 0 forms step t+2's masked A load offset after MFMA
+    // 23; half 1 forms step t+3's B offset after MFMA 12 and moves the next
+    // scales of B blocks 0..3 (last used in half 0) and A blocks 0..3 (last
+    // used by MFMA 15) into fresh registers after MFMA 8 and 16
+    static constexpr int kSlotMaskA = 23, kSlotMaskB = 12, kSlotScaleB = 8, kSlotScaleA = 16;
 
     // lane base w of half kH's reads at panel offset off (half 0 reads B only)
     template <int kH, int kW>
@@ -973,6 +984,9 @@ __device__ __forceinline__ MxScales mx_load_scales(const QuadCtx &c, int lane, i
 // the scalar K offset of step t+2's loads.  Carried from step to step.
 struct Ring {
     int pa, pb, pb1, pb2, so;
+    // MXFP8 only: byte offsets of step t+1's packed scales (A, B), row bytes
+    // left from step t+2's start, and step t+2's masked B load offset
+    int ma, mb, rem, vb;
 };
 
 // K step t: the loads it issues are of step t+2.
@@ -993,15 +1007,24 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4
                                           int lane, Ring &rg, Bases &bs0)
 {
     using Q = Quad<kDtype>;
-    MxScales next;
-    if constexpr (kDtype == kMx)
-        next = mx_load_scales(c, lane, t + 1);
-    const int k2 = t + 2;
-    const int va = kMasked ? kstep_voff(c.voff_a, c.cb_a, k2, ldk) : c.voff_a;
-    const int vb = kMasked ? kstep_voff(c.voff_b, c.cb_b, k2, ldk) : c.voff_b;
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     // Each ring value is threaded through one chain of pins in program
     // order (every pin is then its value's last use, so none needs a copy).
     int pa = rg.pa, pb1 = rg.pb1, pb2 = rg.pb2, so = rg.so;
+    int ma = rg.ma, mb = rg.mb, rem = rg.rem;
+    // MXFP8: step t+1's scales, loaded first (the barrier's vmcnt wait then
+    // covers them); the masked load offsets of step t+2 (va: formed in half
+    // 0; vb: carried from the previous step)
+    u32x2 next_a = {0u, 0u}, next_b = {0u, 0u};
+    if constexpr (kDtype == kMx) {
+        ma = pin_s(ma);
+        mb = pin_s(mb);
+        next_a = __builtin_amdgcn_raw_buffer_load_b64(c.rsa, lane * 8, ma, 0);
+        next_b = __builtin_amdgcn_raw_buffer_load_b64(c.rsb, lane * 8, mb, 0);
+    }
+    int va = c.voff_a;
+    const int vb = kMasked ? rg.vb : c.voff_b;
+    uint32_t nsc_a0 = 0u, nsc_b0 = 0u;
     // lane base w of the half reading slice 0 (half 1) or 1 (next step's
     // half 0) of step t+1: A panel pa ^ 32 KiB, B panel pb1
     auto next_base = [&](Bases &bs, auto kh, auto w) __attribute__((always_inline)) {
@@ -1039,7 +1062,15 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4
             so = pin_s(so);
             dma_rows_at(c.rb, c.smem, pb2, kBRing, c.wave + 4 * v, vb, so, ldk);
         },
-        [&](auto slot) __attribute__((always_inline)) { bases_at(bs1, H1{}, slot); });
+        [&](auto slot) __attribute__((always_inline)) {
+            bases_at(bs1, H1{}, slot);
+            if constexpr (kMasked) {
+                if constexpr (decltype(slot)::value == Q::kSlotMaskA) {
+                    rem = pin_s(rem);
+                    va = opaque(c.cb_a < rem ? c.voff_a : kOutOfRange);
+                }
+            }
+        });
     wait_lgkmcnt0();
     wait_vmcnt<8>();                               // step t+1 landed (B(t+2) in flight)
     block_barrier();
@@ -1063,10 +1094,25 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4
                 nr.pa = pin_s(pin_s(pa) ^ kPanelBytes);
                 nr.so = pin_s(pin_s(so) + kRowBytes);
             }
+            if constexpr (kMasked) {
+                if constexpr (n == Q::kSlotMaskB) {
+                    rem = pin_s(rem);
+                    nr.vb = opaque(c.cb_b < pin_s(rem - kRowBytes) ? c.voff_b : kOutOfRange);
+                }
+                if constexpr (n == Q::kSlotScaleB)
+                    nsc_b0 = mov_v(next_b[0]);
+                if constexpr (n == Q::kSlotScaleA)
+                    nsc_a0 = mov_v(next_a[0]);
+                if constexpr (n == Q::kSlotTail) {
+                    nr.rem = pin_s(pin_s(rem) - kRowBytes);
+                    nr.ma = pin_s(pin_s(ma) + 512);
+                    nr.mb = pin_s(pin_s(mb) + 512);
+                }
+            }
         });
     rg = nr;
     if constexpr (kDtype == kMx)
-        sc = next;
+        sc = MxScales{{nsc_a0, next_a[1]}, {nsc_b0, next_b[1]}};
 }
 
 template <int kDtype>
@@ -1149,7 +1195,13 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(const GemmParams p)
         block_barrier();
         typename Q::Frags f;
         Q::read_first(f, smem, c.l, c.a_rows, c.b_rows);
-        Ring rg = {0, 0, kPanelBytes, 2 * kPanelBytes, 2 * kRowBytes - c.shift};
+        Ring rg = {0, 0, kPanelBytes, 2 * kPanelBytes, 2 * kRowBytes - c.shift, 0, 0, 0, 0};
+        if constexpr (kMasked) {
+            rg.ma = c.sa_group + 512;
+            rg.mb = c.sb_group + 512;
+            rg.rem = ldk - 2 * kRowBytes;
+            rg.vb = kstep_voff(c.voff_b, c.cb_b, 2, ldk);
+        }
         Bases bs0 = {{0, 0}, {0, 0}};
         Q::template base<0, 0>(bs0, c.l, c.a_rows);
         Q::template base<0, 1>(bs0, c.l, c.a_rows);
