@@ -48,13 +48,27 @@ void clamp_remap(int64_t Gm, int64_t Gn, int64_t *W, int64_t *C)
         *C = 1;
 }
 
-// (W, C) used when the caller does not choose one.  A chunk of 32 tiles
-// gives each XCD one group of 32 consecutive remapped ids per round of the
-// 256-CU machine, and a window of 8 tile rows turns it into an 8 x 4 patch
-// of output tiles (8 A panels + 4 B panels shared in that XCD's L2).
-void default_remap(int64_t Gm, int64_t Gn, int32_t *W, int32_t *C)
+// (W, C) used when the caller does not choose one; row_bytes = K x element
+// size.  Both choices give each XCD's 32 concurrent tiles a patch that
+// shares 12 operand panels in its L2 (the L2 term of the pages' Eq. 1):
+//  - (8, 32): chunks of 32 consecutive remapped ids per XCD, an 8 x 4 patch;
+//    the 256 tiles in flight on the chip form an 8 x 32 strip of the grid
+//    (40 panels);
+//  - (16, 4): chunks of 4, a 4 x 8 patch per XCD; the 256 tiles in flight
+//    form a 16 x 16 block (32 panels).
+// The second keeps the chip-wide working set (panels x 256 rows x row_bytes)
+// inside the last-level cache when the first's would not fit (the LLC term
+// of Eq. 1).  Measured at square sizes: (8, 32) is as good or better while 40
+// panels stay below ~185 MiB (bf16 n <= 9216, e4m3 n <= 12288, K = 4096
+// shapes), and (16, 4) wins above (bf16 10000, 12288, 14592, 16384: +5.4,
+// +1.6, +1.0, +5.1 %).
+constexpr int64_t kLlcPanelBudget = int64_t(185) << 20;
+constexpr int64_t kBigRowBytes = kLlcPanelBudget / (40 * kTile);   // 18944 B (bf16 K > 9472)
+
+void default_remap(int64_t Gm, int64_t Gn, int64_t row_bytes, int32_t *W, int32_t *C)
 {
-    int64_t w = 8, c = 32;
+    const bool big = row_bytes > kBigRowBytes;
+    int64_t w = big ? 16 : 8, c = big ? 4 : 32;
     clamp_remap(Gm, Gn, &w, &c);
     *W = static_cast<int32_t>(w);
     *C = static_cast<int32_t>(c);
@@ -83,10 +97,10 @@ int validate(int64_t M, int64_t N, int64_t K, int64_t kalign, int64_t elem, cons
     return HKG_OK;
 }
 
-int resolve_opts(const hkg_gemm_opts *opts, int64_t Gm, int64_t Gn, int32_t *W, int32_t *C,
-                 hkg::Schedule *sched)
+int resolve_opts(const hkg_gemm_opts *opts, int64_t Gm, int64_t Gn, int64_t row_bytes, int32_t *W,
+                 int32_t *C, hkg::Schedule *sched)
 {
-    default_remap(Gm, Gn, W, C);
+    default_remap(Gm, Gn, row_bytes, W, C);
     *sched = hkg::kInterleave;
     if (!opts)
         return HKG_OK;
@@ -156,7 +170,7 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
     int32_t W = 1, Cc = 1;
     hkg::Schedule sched = hkg::kInterleave;
     if (Gm > 0 && Gn > 0) {
-        rc = resolve_opts(opts, Gm, Gn, &W, &Cc, &sched);
+        rc = resolve_opts(opts, Gm, Gn, K * elem, &W, &Cc, &sched);
         if (rc != HKG_OK)
             return rc;
     } else if (opts && (opts->remap < 0 || opts->remap > 2 || opts->schedule < 0 ||
@@ -285,7 +299,7 @@ int hkg_default_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *W
     const int64_t kalign = dtype == 0 ? kKAlignBf16 : (dtype == 1 ? kKAlignFp8 : kKAlignMx);
     if ((dtype < 0 || dtype > 2) || M <= 0 || N <= 0 || K < 0 || K % kalign)
         return HKG_ERR_SHAPE;
-    default_remap(ceil_div(M, kTile), ceil_div(N, kTile), W, C);
+    default_remap(ceil_div(M, kTile), ceil_div(N, kTile), K * (dtype == 0 ? 2 : 1), W, C);
     return HKG_OK;
 }
 

@@ -163,7 +163,11 @@ int hkg_mx_pack_scales(int32_t operand, int64_t rows, int64_t K, const void *sca
 /*
  * The (W, C) the library uses for HKG_REMAP_DEFAULT on a shape (host only, no
  * HIP call).  dtype: 0 = bf16, 1 = fp8, 2 = MXFP8.  Returns HKG_ERR_NULL/SHAPE
- * on bad input.
+ * on bad input.  Rule (the L2 and LLC terms of the HipKittens L2 note's
+ * section 4 equation): (8, 32) while an operand row holds at most 18944 bytes
+ * (K x element size), else (16, 4), whose 256 concurrent tiles share fewer
+ * operand panels in the last-level cache; both clamped to the grid
+ * (W <= ceil(M/256), C <= tiles/8 + 1).
  */
 int hkg_default_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *W, int32_t *C);
 

@@ -112,6 +112,24 @@ def test_default_remap():
     assert rc == hkg.HKG_OK and (W, C) == (2, 10)
 
 
+@pytest.mark.parametrize("M,N,K,dtype,want", [
+    (9216, 9216, 9216, 0, (8, 32)),         # 40 panels x 4.5 MiB fit the last-level cache
+    (16384, 14336, 4096, 0, (8, 32)),
+    (12288, 12288, 12288, 1, (8, 32)),      # e4m3: 3 MiB panels
+    (10000, 10000, 10000, 0, (16, 4)),      # bf16 rows past 18944 bytes
+    (12288, 12288, 12288, 0, (16, 4)),
+    (16384, 16384, 16384, 0, (16, 4)),
+    (16384, 16384, 20480, 1, (16, 4)),
+    (2048, 2048, 16384, 0, (8, 4)),         # 8 x 8 tiles: (16, 4) with W clamped to 8
+])
+def test_default_remap_follows_panel_bytes(M, N, K, dtype, want):
+    """Rows longer than 18944 bytes switch the default from an 8 x 32 strip of
+    concurrent tiles to a 16 x 16 block (fewer panels in the last-level
+    cache); both keep 12 panels per XCD's L2."""
+    rc, W, C = hkg.hkg_default_remap(M, N, K, dtype)
+    assert rc == hkg.HKG_OK and (W, C) == want
+
+
 # ---------------------------------------------------------------- MXFP8 -------------
 
 def test_mx_packed_scale_bytes():

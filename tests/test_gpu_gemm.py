@@ -244,6 +244,31 @@ def test_output_identical_across_grid_orders_and_schedules():
         np.testing.assert_array_equal(got, base)
 
 
+@pytest.mark.parametrize("dtype,M,N,K", [("bf16", 300, 264, 520), ("bf16", 513, 777, 4104),
+                                         ("bf16", 256, 256, 8), ("bf16", 640, 384, 136),
+                                         ("fp8", 300, 264, 528), ("fp8", 513, 520, 4112),
+                                         ("fp8", 256, 256, 16), ("fp8", 640, 384, 144)])
+def test_ragged_k_identical_across_schedules(dtype, M, N, K):
+    """Both kernels take a partial K step (K not a multiple of 64 bf16 / 128
+    e4m3 elements) first and accumulate the steps in the same order, so
+    every schedule gives the same fp32 accumulator bit for bit at any K."""
+    _say("ragged-K invariance %s %dx%dx%d" % (dtype, M, N, K))
+    outs = []
+    for sched in SCHEDULES:
+        o = hkg.make_opts(schedule=sched)
+        if dtype == "bf16":
+            A = synth.f32_to_bf16_bits(synth.normal_f32(9990 + K, M, K))
+            B = synth.f32_to_bf16_bits(synth.normal_f32(9991 + K, N, K))
+            outs.append(run_bf16(A, B, opts=o))
+        else:
+            A, sa = synth.e4m3_quantize(synth.normal_f32(9992 + K, M, K))
+            B, sb = synth.e4m3_quantize(synth.normal_f32(9993 + K, N, K))
+            outs.append(run_fp8(A, B, sa, sb, opts=o))
+    for cb, cf in outs[1:]:
+        np.testing.assert_array_equal(cf.view(np.uint32), outs[0][1].view(np.uint32))
+        np.testing.assert_array_equal(cb, outs[0][0])
+
+
 def test_repeated_launches_bit_identical_and_no_stray_writes():
     _say("repeat + canary")
     M, N, K = 1024, 1024, 512
