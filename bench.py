@@ -9,10 +9,12 @@ throughput (TFLOPS), the MFMA roofline of the kernel (live HIP-event timing),
 and the CPU oracle timed on a bounded sample as a baseline.
 
   python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload 2]
-                  [--all] [--remap W,C | --row-major] [--schedule interleave|pingpong|lockstep]
+                  [--all] [--remap W,C | --row-major]
+                  [--schedule interleave|pingpong|lockstep|interleave128]
                   [--no-cpu-baseline]
   python bench.py --sizes "1024 2048 ..." [--dtype bf16|fp8]
-        square-size sweep: both schedules per size, one JSON line each
+        square-size sweep: each schedule (4-wave 256 and 128 tiles, ping-pong) per
+        size, one JSON line each
   python bench.py --sweep "1,1 8,32 5,25 ..." [--workload N | --shape M,N,K --dtype bf16|fp8]
         grid-order sweep: one JSON line per (W, C) on the same resident inputs
         ("1,1" is row-major order); used to choose the library's default (W, C)
@@ -71,6 +73,8 @@ def algorithmic_bytes(w: synth.Workload) -> int:
 def kernel_name(dtype: str, schedule: str) -> str:
     if schedule == "interleave":
         return "gemm4_kernel<%s>" % dtype
+    if schedule == "interleave128":
+        return "gemm4_kernel<%s,128>" % dtype
     return "gemm_kernel<%s,%s>" % (dtype, schedule)
 
 
@@ -303,8 +307,9 @@ def size_sweep(sizes, dtype: str, warmup: int) -> None:
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    scheds = [("interleave", hkg.HKG_SCHED_INTERLEAVE), ("pingpong", hkg.HKG_SCHED_PINGPONG)]
-    if dtype == "mxfp8":     # the block-scaled path exists in the 4-wave kernel only
+    scheds = [("interleave", hkg.HKG_SCHED_INTERLEAVE), ("pingpong", hkg.HKG_SCHED_PINGPONG),
+              ("interleave128", hkg.HKG_SCHED_INTERLEAVE_128)]
+    if dtype == "mxfp8":     # the block-scaled path exists in the 4-wave 256 x 256 kernel only
         scheds = scheds[:1]
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -368,14 +373,14 @@ def main(argv=None) -> int:
     ap.add_argument("--all", action="store_true", help="one line per workload 1..5")
     ap.add_argument("--remap", type=str, default=None, help="W,C for the XCD remap")
     ap.add_argument("--row-major", action="store_true")
-    ap.add_argument("--schedule", choices=["interleave", "pingpong", "lockstep"],
+    ap.add_argument("--schedule", choices=["interleave", "pingpong", "lockstep", "interleave128"],
                     default="interleave", help="in-CU schedule (default: the library's, interleave)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shape", type=str, default=None, help="M,N,K (custom size)")
     ap.add_argument("--dtype", choices=["bf16", "fp8", "mxfp8"], default="bf16")
     ap.add_argument("--sweep", type=str, default=None, help='"W,C W,C ..." grid orders to time')
     ap.add_argument("--sizes", type=str, default=None,
-                    help='"n n ..." square sizes: both schedules per size (with --dtype)')
+                    help='"n n ..." square sizes: every schedule per size (with --dtype)')
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -386,7 +391,8 @@ def main(argv=None) -> int:
     import dense_gemm_fp8_amd as hkg
     hkg.load()
     sched = {"pingpong": hkg.HKG_SCHED_PINGPONG, "lockstep": hkg.HKG_SCHED_LOCKSTEP,
-             "interleave": hkg.HKG_SCHED_INTERLEAVE}[args.schedule]
+             "interleave": hkg.HKG_SCHED_INTERLEAVE,
+             "interleave128": hkg.HKG_SCHED_INTERLEAVE_128}[args.schedule]
     opts = None
     if args.row_major:
         opts = hkg.make_opts(remap=hkg.HKG_REMAP_ROW_MAJOR, schedule=sched)

@@ -336,24 +336,26 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 // 32 h + 8 q .. 32 h + 8 q + 7 (blocks 2 h and 2 h + 1, interleaved as above).
 // Tiles inside M x N with N % 8 == 0 use 16-byte stores; edge tiles store
 // only rows < M and columns < N (element by element when N % 8 != 0).
-template <int kBlocks>
+// kRB x kCB blocks of 16 x 16 of a kT x kT output tile (tile (tm, tn)), the
+// wave's part starting at (row_off, col_off) inside it.
+template <int kRB, int kCB, int kT>
 __device__ __forceinline__ void store_tile(const GemmParams &p, int tm, int tn, int row_off,
-                                           int col_off, int lane, f32x4 (&acc)[8][kBlocks])
+                                           int col_off, int lane, f32x4 (&acc)[kRB][kCB])
 {
     const int q = lane >> 4;
-    const int64_t row0 = (int64_t)tm * kTile + row_off + (lane & 15);
-    const int64_t col0 = (int64_t)tn * kTile + col_off + 8 * q;
+    const int64_t row0 = (int64_t)tm * kT + row_off + (lane & 15);
+    const int64_t col0 = (int64_t)tn * kT + col_off + 8 * q;
     const float sc = p.scale;
     uint16_t *C = static_cast<uint16_t *>(p.C);
     const bool vec = (p.N & 7) == 0;
-    const bool inside = (tm + 1) * kTile <= p.M && (tn + 1) * kTile <= p.N && vec;
+    const bool inside = (tm + 1) * kT <= p.M && (tn + 1) * kT <= p.N && vec;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kRB; ++i) {
         const int64_t m = row0 + 16 * i;
         if (!inside && m >= p.M)
             continue;
 #pragma unroll
-        for (int h = 0; h < kBlocks / 2; ++h) {
+        for (int h = 0; h < kCB / 2; ++h) {
             const f32x4 lo = acc[i][2 * h] * sc;
             const f32x4 hi = acc[i][2 * h + 1] * sc;
             const int64_t n0 = col0 + 32 * h;
@@ -571,7 +573,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
             }
         }
     }
-    store_tile<4>(p, tm, tn, 128 * g, 64 * wn, lane, acc);
+    store_tile<8, 4, kTile>(p, tm, tn, 128 * g, 64 * wn, lane, acc);
 }
 
 // ---- 4-wave interleave (one wave per SIMD) --------------------------------
@@ -754,33 +756,45 @@ struct Bases {
     int a[2], b[2];
 };
 
-template <int kDtype>
+// kB: 16 x 16 blocks per side of a wave's quarter of the tile -- 8 for the
+// 256 x 256 tile (a 128 x 128 quarter), 4 for the 128 x 128 tile.
+template <int kDtype, int kB>
 struct Quad;
 
-template <>
-struct Quad<kBf16> {
-    // half h runs DOT_SLICE h of all 64 blocks (i-major); half 0 reads slice 1
-    // of step t, half 1 reads slice 0 of step t+1 (B fragments 0..7 first,
-    // then A fragments 0..7: the order the next half's MFMAs need them).
+template <int kB>
+struct Quad<kBf16, kB> {
+    // half h runs DOT_SLICE h of all kB x kB blocks (i-major); half 0 reads
+    // slice 1 of step t, half 1 reads slice 0 of step t+1 (B fragments
+    // first, then A fragments: the order the next half's MFMAs need them).
     using F = Frag<kBf16>;
     struct Frags {
-        bf16x8 a[2][8], b[2][8];   // [slice][block]
+        bf16x8 a[2][kB], b[2][kB];   // [slice][block]
     };
-    static constexpr int kMfmas = 64;   // per half
-    // the MFMA after which load v (0..7) of half h / fragment read r (0..15)
-    // issues; half 1's A loads go early (their panel is free once the
-    // barrier has passed), which leaves them 85 MFMAs to land before the
-    // next barrier waits for them, against 68 when spread like the B loads
-    __device__ static constexpr int dma_slot(int h, int v) { return h == 0 ? 8 * v + 4 : 6 * v + 1; }
-    __device__ static constexpr int read_slot(int r) { return 3 * r; }
-    // gaps (no memory instruction) for the step's bookkeeping: the next
-    // half's A and B lane bases (late, so that fragments have died to make
-    // room), the three B-ring moves, and the A ring / K offset update after
-    // the half's last load
+    static constexpr int kBlk = kB;
+    static constexpr int kMfmas = kB * kB;   // per half
+    // The MFMA after which load v (0..kB-1) of half h / fragment read r
+    // (0..2kB-1) issues.  kB = 8: half 1's A loads go early (their panel is
+    // free once the barrier has passed), which leaves them 85 MFMAs to land
+    // before the next barrier waits for them, against 68 when spread like
+    // the B loads.  kB = 4 (16 MFMAs a half): reads on even gaps, loads on
+    // odd ones, A loads again early.
+    __device__ static constexpr int dma_slot(int h, int v)
+    {
+        return kB == 8 ? (h == 0 ? 8 * v + 4 : 6 * v + 1) : (h == 0 ? 4 * v + 1 : 2 * v + 1);
+    }
+    __device__ static constexpr int read_slot(int r) { return kB == 8 ? 3 * r : 2 * r; }
+    // gaps (no load there) for the step's bookkeeping: the next half's A and
+    // B lane bases (late, so that fragments have died to make room), the
+    // three B-ring moves, and the A ring / K offset update after the half's
+    // last load
     // (base_slot(h, w): half h forms lane base w = A, -, B, - ; -1 = none)
-    __device__ static constexpr int base_slot(int, int w) { return w == 0 ? 50 : w == 2 ? 53 : -1; }
-    __device__ static constexpr int rot_slot(int i) { return 55 + i; }
-    static constexpr int kSlotTail = 61;
+    __device__ static constexpr int base_slot(int h, int w)
+    {
+        return kB == 8 ? (w == 0 ? 50 : w == 2 ? 53 : -1)
+                       : (w == 0 ? (h == 0 ? 7 : 9) : w == 2 ? 11 : -1);
+    }
+    __device__ static constexpr int rot_slot(int i) { return kB == 8 ? 55 + i : 12 + i; }
+    static constexpr int kSlotTail = kB == 8 ? 61 : 15;
 
     // lane base w of half kH's reads: slice 1 - kH of the panel at off
     template <int kH, int kW>
@@ -797,16 +811,16 @@ struct Quad<kBf16> {
     {
         const int ba = opaque(l.a[0] + a_off), bb = opaque(l.b[0] + b_off);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < kB; ++j)
             f.b[0][j] = *reinterpret_cast<const bf16x8 *>(smem + qb_blk(j) + bb);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < kB; ++i)
             f.a[0][i] = *reinterpret_cast<const bf16x8 *>(smem + qa_blk(i) + ba);
     }
     // bs: this half's read bases; dma(v) issues the half's load v; hook(n)
     // runs after MFMA n (the caller's per-slot work).
     template <int kH, class Dma, class Hook>
-    __device__ __forceinline__ static void half(Frags &f, f32x4 (&acc)[8][8], const char *smem,
+    __device__ __forceinline__ static void half(Frags &f, f32x4 (&acc)[kB][kB], const char *smem,
                                                 const Bases &bs, const MxScales &, Dma &&dma,
                                                 Hook &&hook)
     {
@@ -814,20 +828,20 @@ struct Quad<kBf16> {
         const int ba = bs.a[0], bb = bs.b[0];
         for_slots<kMfmas>([&](auto slot) __attribute__((always_inline)) {
             constexpr int n = decltype(slot)::value;
-            constexpr int i = n >> 3, j = n & 7;
+            constexpr int i = n / kB, j = n % kB;
             acc[i][j] = F::mma(f.b[kH][j], f.a[kH][i], acc[i][j]);
 #pragma unroll
-            for (int v = 0; v < 8; ++v)
+            for (int v = 0; v < kB; ++v)
                 if (dma_slot(kH, v) == n)
                     dma(v);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int r = 0; r < 2 * kB; ++r) {
                 if (read_slot(r) != n)
                     continue;
-                if (r < 8)
+                if (r < kB)
                     f.b[s][r] = *reinterpret_cast<const bf16x8 *>(smem + qb_blk(r) + bb);
                 else
-                    f.a[s][r - 8] = *reinterpret_cast<const bf16x8 *>(smem + qa_blk(r - 8) + ba);
+                    f.a[s][r - kB] = *reinterpret_cast<const bf16x8 *>(smem + qa_blk(r - kB) + ba);
             }
             hook(slot);
             __builtin_amdgcn_sched_barrier(0);
@@ -835,29 +849,40 @@ struct Quad<kBf16> {
     }
 };
 
-template <bool kMxScaled>
+template <bool kMxScaled, int kB>
 struct QuadF8 {
     // e4m3 with per-tensor scales (kMxScaled false) or MXFP8 block scales.
-    // half 0 runs blocks (i, j < 4), half 1 blocks (i, j >= 4), both i-major.
-    // Half 0 reads B fragments 4..7 of step t; half 1 reads B fragments 0..3
-    // of step t+1 and A fragment i of step t+1 right after the last MFMA
-    // that uses A fragment i of step t, so one K step of fragments (128
-    // registers) is all a wave holds.  A fragment is two 16-byte chunks
-    // (halves h = 0, 1).
+    // half 0 runs blocks (i, j < kB/2), half 1 blocks (i, j >= kB/2), both
+    // i-major.  Half 0 reads the B fragments of its second half of step t;
+    // half 1 reads the first B fragments of step t+1 and A fragment i of
+    // step t+1 right after the last MFMA that uses A fragment i of step t,
+    // so one K step of fragments is all a wave holds.  A fragment is two
+    // 16-byte chunks (halves h = 0, 1).
     using F = Frag<kFp8>;
     struct Frags {
-        i32x8 a[8], b[8];
+        i32x8 a[kB], b[kB];
     };
-    static constexpr int kMfmas = 32;   // per half
-    __device__ static constexpr int dma_slot(int, int v) { return 4 * v + 1; }
-    // B fragment 4 + r (half 0) or r (half 1)
+    static constexpr int kBlk = kB;
+    static constexpr int kHalfCols = kB / 2;
+    static constexpr int kMfmas = kB * kHalfCols;   // per half
+    // kB = 4 (8 MFMAs a half, each 32 cycles): half 1 loads on even gaps so
+    // that its tail gap (7) follows the last one
+    __device__ static constexpr int dma_slot(int h, int v)
+    {
+        return kB == 8 ? 4 * v + 1 : (h == 0 ? 2 * v + 1 : 2 * v);
+    }
+    // B fragment kB/2 + r (half 0) or r (half 1)
     __device__ static constexpr int b_read_slot(int h, int r) { return h == 0 ? 4 * r + 2 : r; }
-    // bookkeeping gaps, as for bf16 (no load or read there in either half)
-    // (lane bases w = A chunk 0, A chunk 1, B chunk 0, B chunk 1; no slot
+    // bookkeeping gaps, as for bf16 (kB = 8: no load or read there in either
+    // half; lane bases w = A chunk 0, A chunk 1, B chunk 0, B chunk 1; no slot
     // just before a load slot, whose address arithmetic tends to move up a gap)
-    __device__ static constexpr int base_slot(int h, int w) { return (h == 0 ? 18 : 6) + 4 * w; }
-    __device__ static constexpr int rot_slot(int i) { return 20 + 4 * i; }
-    static constexpr int kSlotTail = 30;
+    __device__ static constexpr int base_slot(int h, int w)
+    {
+        return kB == 8 ? (h == 0 ? 18 : 6) + 4 * w
+                       : (h == 0 ? 2 * w : (w < 2 ? -1 : 2 * w - 1));
+    }
+    __device__ static constexpr int rot_slot(int i) { return kB == 8 ? 20 + 4 * i : 2 + 2 * i; }
+    static constexpr int kSlotTail = kB == 8 ? 30 : 7;
     // MXFP8 only: half 0 forms step t+2's masked A load offset after MFMA
     // 23; half 1 forms step t+3's B offset after MFMA 12 and moves the next
     // scales of B blocks 0..3 (last used in half 0) and A blocks 0..3 (last
@@ -888,38 +913,38 @@ struct QuadF8 {
         const int ba0 = opaque(l.a[0] + a_off), ba1 = opaque(l.a[1] + a_off);
         const int bb0 = opaque(l.b[0] + b_off), bb1 = opaque(l.b[1] + b_off);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kHalfCols; ++j)
             f.b[j] = frag(smem, qb_blk(j), bb0, bb1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < kB; ++i)
             f.a[i] = frag(smem, qa_blk(i), ba0, ba1);
     }
     template <int kH, class Dma, class Hook>
-    __device__ __forceinline__ static void half(Frags &f, f32x4 (&acc)[8][8], const char *smem,
+    __device__ __forceinline__ static void half(Frags &f, f32x4 (&acc)[kB][kB], const char *smem,
                                                 const Bases &bs, const MxScales &sc, Dma &&dma,
                                                 Hook &&hook)
     {
         const int ba0 = bs.a[0], ba1 = bs.a[1], bb0 = bs.b[0], bb1 = bs.b[1];
         for_slots<kMfmas>([&](auto slot) __attribute__((always_inline)) {
             constexpr int n = decltype(slot)::value;
-            constexpr int i = n >> 2, j = 4 * kH + (n & 3);
+            constexpr int i = n / kHalfCols, j = kHalfCols * kH + n % kHalfCols;
             if (kMxScaled)
                 acc[i][j] = mma_mx(f.b[j], f.a[i], acc[i][j], sc.b[j >> 2], sc.a[i >> 2], j & 3,
                                    i & 3);
             else
                 acc[i][j] = F::mma(f.b[j], f.a[i], acc[i][j]);
 #pragma unroll
-            for (int v = 0; v < 8; ++v)
+            for (int v = 0; v < kB; ++v)
                 if (dma_slot(kH, v) == n)
                     dma(v);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
+            for (int r = 0; r < kHalfCols; ++r) {
                 if (b_read_slot(kH, r) != n)
                     continue;
-                const int jb = 4 * (1 - kH) + r;
+                const int jb = kHalfCols * (1 - kH) + r;
                 f.b[jb] = frag(smem, qb_blk(jb), bb0, bb1);
             }
-            if (kH == 1 && (n & 3) == 3)
+            if (kH == 1 && n % kHalfCols == kHalfCols - 1)
                 f.a[i] = frag(smem, qa_blk(i), ba0, ba1);
             hook(slot);
             __builtin_amdgcn_sched_barrier(0);
@@ -927,30 +952,35 @@ struct QuadF8 {
     }
 };
 
-template <>
-struct Quad<kFp8> : QuadF8<false> {
+template <int kB>
+struct Quad<kFp8, kB> : QuadF8<false, kB> {
 };
-template <>
-struct Quad<kMx> : QuadF8<true> {
+template <int kB>
+struct Quad<kMx, kB> : QuadF8<true, kB> {
 };
 
-// every memory instruction of a half has an MFMA to follow
-static_assert(Quad<kBf16>::dma_slot(0, 7) < Quad<kBf16>::kMfmas &&
-                  Quad<kBf16>::dma_slot(1, 7) < Quad<kBf16>::kMfmas &&
-                  Quad<kBf16>::read_slot(15) < Quad<kBf16>::kMfmas, "bf16 slot plan");
-static_assert(Quad<kFp8>::dma_slot(0, 7) < Quad<kFp8>::kMfmas &&
-                  Quad<kFp8>::b_read_slot(0, 3) < Quad<kFp8>::kMfmas, "e4m3 slot plan");
-// bookkeeping order in half 1: lane bases, then the B-ring moves, then the
-// tail after the last load
+// Every memory instruction and bookkeeping slot of a half has an MFMA to
+// follow, and the tail (A ring / K offset update) comes after the half's
+// last load (the loads read the values it replaces).
 template <class Q>
-constexpr bool bookkeeping_ok()
+constexpr bool slots_ok()
 {
-    return Q::base_slot(1, 2) < Q::rot_slot(0) && Q::base_slot(1, 3) < Q::rot_slot(0) &&
-           Q::base_slot(0, 3) < Q::kMfmas && Q::rot_slot(2) < Q::kSlotTail &&
-           Q::kSlotTail > Q::dma_slot(1, 7) && Q::kSlotTail < Q::kMfmas;
+    bool ok = Q::kSlotTail > Q::dma_slot(1, Q::kBlk - 1) && Q::kSlotTail < Q::kMfmas;
+    for (int h = 0; h < 2; ++h)
+        for (int v = 0; v < Q::kBlk; ++v)
+            ok = ok && Q::dma_slot(h, v) < Q::kMfmas;
+    for (int h = 0; h < 2; ++h)
+        for (int w = 0; w < 4; ++w)
+            ok = ok && Q::base_slot(h, w) < Q::kMfmas;
+    for (int i = 0; i < 3; ++i)
+        ok = ok && Q::rot_slot(i) < Q::kMfmas;
+    return ok;
 }
-static_assert(bookkeeping_ok<Quad<kBf16>>(), "bf16 bookkeeping slots");
-static_assert(bookkeeping_ok<Quad<kFp8>>(), "e4m3 bookkeeping slots");
+static_assert(slots_ok<Quad<kBf16, 8>>() && slots_ok<Quad<kBf16, 4>>(), "bf16 slot plans");
+static_assert(slots_ok<Quad<kFp8, 8>>() && slots_ok<Quad<kFp8, 4>>(), "e4m3 slot plans");
+static_assert(Quad<kBf16, 8>::read_slot(15) < 64 && Quad<kBf16, 4>::read_slot(7) < 16 &&
+                  Quad<kFp8, 8>::b_read_slot(0, 3) < 32 && Quad<kFp8, 4>::b_read_slot(0, 1) < 8,
+              "read slots");
 
 // What the 4-wave loop of one workgroup works on.
 struct QuadCtx {
@@ -1001,12 +1031,13 @@ struct Ring {
 // All of the step's bookkeeping (next bases, ring rotation, K offset) is
 // issued in fixed MFMA gaps of the halves, none of it at the loop's head or
 // back edge.
-template <int kDtype, bool kMasked>
-__device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4 (&acc)[8][8],
-                                          MxScales &sc, const QuadCtx &c, int ldk, int t,
-                                          int lane, Ring &rg, Bases &bs0)
+template <int kDtype, bool kMasked, int kB>
+__device__ __forceinline__ void quad_step(typename Quad<kDtype, kB>::Frags &f,
+                                          f32x4 (&acc)[kB][kB], MxScales &sc, const QuadCtx &c,
+                                          int ldk, int t, int lane, Ring &rg, Bases &bs0)
 {
-    using Q = Quad<kDtype>;
+    using Q = Quad<kDtype, kB>;
+    constexpr int kP = 32 * kB * kRowBytes;   // panel bytes (32 kB rows)
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     // Each ring value is threaded through one chain of pins in program
     // order (every pin is then its value's last use, so none needs a copy).
@@ -1026,13 +1057,12 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4
     const int vb = kMasked ? rg.vb : c.voff_b;
     uint32_t nsc_a0 = 0u, nsc_b0 = 0u;
     // lane base w of the half reading slice 0 (half 1) or 1 (next step's
-    // half 0) of step t+1: A panel pa ^ 32 KiB, B panel pb1
+    // half 0) of step t+1: A panel pa ^ kP, B panel pb1
     auto next_base = [&](Bases &bs, auto kh, auto w) __attribute__((always_inline)) {
         constexpr int kW = decltype(w)::value;
         if constexpr (kW < 2) {
             pa = pin_s(pa);
-            Q::template base<decltype(kh)::value, kW>(bs, c.l,
-                                                      pin_s(c.a_rows + (pa ^ kPanelBytes)));
+            Q::template base<decltype(kh)::value, kW>(bs, c.l, pin_s(c.a_rows + (pa ^ kP)));
         } else {
             pb1 = pin_s(pb1);
             Q::template base<decltype(kh)::value, kW>(bs, c.l, pin_s(c.b_rows + pb1));
@@ -1060,7 +1090,7 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4
         [&](int v) {
             pb2 = pin_s(pb2);
             so = pin_s(so);
-            dma_rows_at(c.rb, c.smem, pb2, kBRing, c.wave + 4 * v, vb, so, ldk);
+            dma_rows_at(c.rb, c.smem, pb2, 2 * kP, c.wave + 4 * v, vb, so, ldk);
         },
         [&](auto slot) __attribute__((always_inline)) {
             bases_at(bs1, H1{}, slot);
@@ -1072,7 +1102,7 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4
             }
         });
     wait_lgkmcnt0();
-    wait_vmcnt<8>();                               // step t+1 landed (B(t+2) in flight)
+    wait_vmcnt<kB>();                              // step t+1 landed (B(t+2) in flight)
     block_barrier();
     Q::template half<1>(
         f, acc, c.smem, bs1, sc,
@@ -1091,7 +1121,7 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4
             if constexpr (n == Q::rot_slot(2))
                 nr.pb2 = mov_s(rg.pb);
             if constexpr (n == Q::kSlotTail) {
-                nr.pa = pin_s(pin_s(pa) ^ kPanelBytes);
+                nr.pa = pin_s(pin_s(pa) ^ kP);
                 nr.so = pin_s(pin_s(so) + kRowBytes);
             }
             if constexpr (kMasked) {
@@ -1115,29 +1145,37 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype>::Frags &f, f32x4
         sc = MxScales{{nsc_a0, next_a[1]}, {nsc_b0, next_b[1]}};
 }
 
-template <int kDtype>
-__global__ __launch_bounds__(256, 1) void gemm4_kernel(const GemmParams p)
+// kT: output tile edge, 256 (one workgroup per CU, the 160 KiB LDS ring) or
+// 128 (a quarter of the work per tile and an 80 KiB ring, so that two
+// workgroups can share a CU: for grids with too few 256 x 256 tiles to fill
+// the chip).  The wave layout, swizzles, schedule and K order are the same;
+// each wave owns a (kT/2) x (kT/2) quarter, kB = kT/32 blocks a side.
+template <int kDtype, int kT>
+__global__ __launch_bounds__(256, kT == 256 ? 1 : 2) void gemm4_kernel(const GemmParams p)
 {
-    __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+    constexpr int kB = kT / 32;
+    constexpr int kP = kT * kRowBytes;   // one panel: kT rows x one K step
+    constexpr int kRing = 2 * kP;        // B ring after the 2 A panels
+    __shared__ __attribute__((aligned(1024))) char smem[5 * kP];
 
     const int lane = threadIdx.x & 63;
     QuadCtx c;
     c.smem = smem;
     c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    c.a_rows = 128 * (c.wave >> 1) * kRowBytes;            // tile rows 128 (w >> 1) ..
-    c.b_rows = kBRing + 128 * (c.wave & 1) * kRowBytes;    // tile columns 128 (w & 1) ..
+    c.a_rows = (kT / 2) * (c.wave >> 1) * kRowBytes;           // tile rows kT/2 (w >> 1) ..
+    c.b_rows = kRing + (kT / 2) * (c.wave & 1) * kRowBytes;    // tile columns kT/2 (w & 1) ..
 
     int tm, tn;
     remap_tile(blockIdx.x, p.Gm, p.Gn, p.W, p.Cc, tm, tn);
 
     constexpr int kElem = kDtype == kBf16 ? 2 : 1;
     const int ldk = p.K * kElem;
-    const int rows_a = min(kTile, p.M - tm * kTile);
-    const int rows_b = min(kTile, p.N - tn * kTile);
-    c.ra = make_rsrc(static_cast<const char *>(p.A) + (int64_t)tm * kTile * ldk, rows_a * ldk);
-    c.rb = make_rsrc(static_cast<const char *>(p.B) + (int64_t)tn * kTile * ldk, rows_b * ldk);
+    const int rows_a = min(kT, p.M - tm * kT);
+    const int rows_b = min(kT, p.N - tn * kT);
+    c.ra = make_rsrc(static_cast<const char *>(p.A) + (int64_t)tm * kT * ldk, rows_a * ldk);
+    c.rb = make_rsrc(static_cast<const char *>(p.B) + (int64_t)tn * kT * ldk, rows_b * ldk);
 
-    // Each wave loads row groups u = wave + 4 v (v < 8) of every panel, so
+    // Each wave loads row groups u = wave + 4 v (v < kB) of every panel, so
     // row bits 3,4 equal the wave index for all its loads.
     const int r8 = lane >> 3;
     c.cb_a = ((lane & 7) ^ slot_xor_a(r8 | (c.wave << 3))) << 4;
@@ -1150,6 +1188,7 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(const GemmParams p)
     constexpr bool kMasked = kDtype == kMx;
     c.shift = kMasked ? 0 : __builtin_amdgcn_readfirstlane(p.nk * kRowBytes - ldk);
     MxScales sc = {{0u, 0u}, {0u, 0u}};
+    static_assert(kDtype != kMx || kT == 256, "MXFP8 scales are packed per 128-row wave quarter");
     if constexpr (kDtype == kMx) {
         // 128-row group g = 2 tm + (w >> 1) of A, 2 tn + (w & 1) of B;
         // each group holds nk K steps of 64 lanes x 8 bytes
@@ -1159,14 +1198,14 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(const GemmParams p)
         c.sb_group = __builtin_amdgcn_readfirstlane((2 * tn + (c.wave & 1)) * p.nk * 512);
     }
 
-    f32x4 acc[8][8];
+    f32x4 acc[kB][kB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < kB; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < kB; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    using Q = Quad<kDtype>;
+    using Q = Quad<kDtype, kB>;
     const int nk = p.nk;
     if (nk > 0) {
         if constexpr (kDtype == kMx)
@@ -1187,15 +1226,15 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(const GemmParams p)
         const int va1 = kMasked ? kstep_voff(c.voff_a, c.cb_a, 1, ldk) : c.voff_a;
         const int vb1 = kMasked ? kstep_voff(c.voff_b, c.cb_b, 1, ldk) : c.voff_b;
         const int so1 = kRowBytes - c.shift;
-        dma_panel_part<8>(c.ra, smem, 0, c.wave, va0, 0, ldk);
-        dma_panel_part<8>(c.rb, smem + kBRing, 0, c.wave, vb0, 0, ldk);
-        dma_panel_part<8>(c.ra, smem + kPanelBytes, 0, c.wave, va1, so1, ldk);
-        dma_panel_part<8>(c.rb, smem + kBRing + kPanelBytes, 0, c.wave, vb1, so1, ldk);
-        wait_vmcnt<16>();                          // step 0 landed
+        dma_panel_part<kB>(c.ra, smem, 0, c.wave, va0, 0, ldk);
+        dma_panel_part<kB>(c.rb, smem + kRing, 0, c.wave, vb0, 0, ldk);
+        dma_panel_part<kB>(c.ra, smem + kP, 0, c.wave, va1, so1, ldk);
+        dma_panel_part<kB>(c.rb, smem + kRing + kP, 0, c.wave, vb1, so1, ldk);
+        wait_vmcnt<2 * kB>();                      // step 0 landed
         block_barrier();
         typename Q::Frags f;
         Q::read_first(f, smem, c.l, c.a_rows, c.b_rows);
-        Ring rg = {0, 0, kPanelBytes, 2 * kPanelBytes, 2 * kRowBytes - c.shift, 0, 0, 0, 0};
+        Ring rg = {0, 0, kP, 2 * kP, 2 * kRowBytes - c.shift, 0, 0, 0, 0};
         if constexpr (kMasked) {
             rg.ma = c.sa_group + 512;
             rg.mb = c.sb_group + 512;
@@ -1208,10 +1247,11 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(const GemmParams p)
         Q::template base<0, 2>(bs0, c.l, c.b_rows);
         Q::template base<0, 3>(bs0, c.l, c.b_rows);
         for (int t = 0; t < nk; ++t)
-            quad_step<kDtype, kMasked>(f, acc, sc, c, ldk, t, lane, rg, bs0);
+            quad_step<kDtype, kMasked, kB>(f, acc, sc, c, ldk, t, lane, rg, bs0);
         wait_vmcnt<0>();
     }
-    store_tile<8>(p, tm, tn, c.a_rows / kRowBytes, (c.b_rows - kBRing) / kRowBytes, lane, acc);
+    store_tile<kB, kB, kT>(p, tm, tn, c.a_rows / kRowBytes, (c.b_rows - kRing) / kRowBytes, lane,
+                           acc);
 }
 
 // MXFP8 scale packing: entry e (0..7) of lane l at K step t of 128-row group
@@ -1282,13 +1322,18 @@ hipError_t launch_gemm(Dtype dt, Schedule s, const GemmParams &p, hipStream_t st
     const dim3 grid(p.Gm * p.Gn), block(512);
     if (dt == kMx) {
         if (s != kInterleave)
-            return hipErrorInvalidValue;   // only the 4-wave kernel has the scaled MFMA path
-        hipLaunchKernelGGL(gemm4_kernel<kMx>, grid, dim3(256), 0, stream, p);
+            return hipErrorInvalidValue;   // only the 4-wave 256 x 256 kernel has the scaled MFMA path
+        hipLaunchKernelGGL((gemm4_kernel<kMx, 256>), grid, dim3(256), 0, stream, p);
     } else if (s == kInterleave) {
         if (dt == kBf16)
-            hipLaunchKernelGGL(gemm4_kernel<kBf16>, grid, dim3(256), 0, stream, p);
+            hipLaunchKernelGGL((gemm4_kernel<kBf16, 256>), grid, dim3(256), 0, stream, p);
         else
-            hipLaunchKernelGGL(gemm4_kernel<kFp8>, grid, dim3(256), 0, stream, p);
+            hipLaunchKernelGGL((gemm4_kernel<kFp8, 256>), grid, dim3(256), 0, stream, p);
+    } else if (s == kInterleave128) {
+        if (dt == kBf16)
+            hipLaunchKernelGGL((gemm4_kernel<kBf16, 128>), grid, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((gemm4_kernel<kFp8, 128>), grid, dim3(256), 0, stream, p);
     } else if (dt == kBf16) {
         if (s == kPingPong)
             hipLaunchKernelGGL((gemm_kernel<kBf16, kPingPong>), grid, block, 0, stream, p);

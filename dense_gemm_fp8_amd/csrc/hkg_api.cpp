@@ -97,28 +97,56 @@ int validate(int64_t M, int64_t N, int64_t K, int64_t kalign, int64_t elem, cons
     return HKG_OK;
 }
 
-int resolve_opts(const hkg_gemm_opts *opts, int64_t Gm, int64_t Gn, int64_t row_bytes, int32_t *W,
-                 int32_t *C, hkg::Schedule *sched)
+// Output tile edge of a schedule's kernel.
+int64_t tile_edge(hkg::Schedule s) { return s == hkg::kInterleave128 ? 128 : kTile; }
+
+// The default schedule: the 4-wave kernel on 256 x 256 tiles, or on 128 x 128
+// tiles when the 256 x 256 grid would leave more than half of the 256 CUs
+// idle (at most 128 tiles; 128 x 128 tiles give four times as many, two per
+// CU).  Square sizes: 1024^3 and 2048^3 run 1.8-2.6x faster on 128 x 128
+// tiles, 3072^3 (144 tiles of 256) 10-15 % slower.  small_ok is false for
+// MXFP8, whose block-scaled path exists on 256 x 256 tiles only.
+hkg::Schedule default_schedule(int64_t M, int64_t N, bool small_ok)
 {
-    default_remap(Gm, Gn, row_bytes, W, C);
-    *sched = hkg::kInterleave;
+    const bool small = ceil_div(M, kTile) * ceil_div(N, kTile) <= 128;
+    return small && small_ok ? hkg::kInterleave128 : hkg::kInterleave;
+}
+
+// Schedule, tile grid (Gm x Gn tiles of the schedule's edge) and grid order
+// of a call; M, N > 0.
+int resolve_opts(const hkg_gemm_opts *opts, int64_t M, int64_t N, int64_t row_bytes,
+                 bool small_ok, int64_t *Gm, int64_t *Gn, int32_t *W, int32_t *C,
+                 hkg::Schedule *sched)
+{
+    *sched = default_schedule(M, N, small_ok);
+    if (opts) {
+        switch (opts->schedule) {
+        case HKG_SCHED_DEFAULT:
+            break;
+        case HKG_SCHED_PINGPONG:
+            *sched = hkg::kPingPong;
+            break;
+        case HKG_SCHED_LOCKSTEP:
+            *sched = hkg::kLockstep;
+            break;
+        case HKG_SCHED_INTERLEAVE:
+            *sched = hkg::kInterleave;
+            break;
+        case HKG_SCHED_INTERLEAVE_128:
+            *sched = hkg::kInterleave128;
+            break;
+        default:
+            return HKG_ERR_OPTS;
+        }
+    }
+    const int64_t t = tile_edge(*sched);
+    *Gm = ceil_div(M, t);
+    *Gn = ceil_div(N, t);
+    if (*Gm * *Gn >= (int64_t(1) << 30))
+        return HKG_ERR_SIZE;
+    default_remap(*Gm, *Gn, row_bytes, W, C);
     if (!opts)
         return HKG_OK;
-    switch (opts->schedule) {
-    case HKG_SCHED_DEFAULT:
-        break;
-    case HKG_SCHED_PINGPONG:
-        *sched = hkg::kPingPong;
-        break;
-    case HKG_SCHED_LOCKSTEP:
-        *sched = hkg::kLockstep;
-        break;
-    case HKG_SCHED_INTERLEAVE:
-        *sched = hkg::kInterleave;
-        break;
-    default:
-        return HKG_ERR_OPTS;
-    }
     switch (opts->remap) {
     case HKG_REMAP_DEFAULT:
         break;
@@ -131,7 +159,7 @@ int resolve_opts(const hkg_gemm_opts *opts, int64_t Gm, int64_t Gn, int64_t row_
             return HKG_ERR_OPTS;
         {
             int64_t w = opts->W, c = opts->C;
-            clamp_remap(Gm, Gn, &w, &c);
+            clamp_remap(*Gm, *Gn, &w, &c);
             *W = static_cast<int32_t>(w);
             *C = static_cast<int32_t>(c);
         }
@@ -162,19 +190,19 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
         if (mx_packed_bytes(M, K) >= (int64_t(1) << 31) || mx_packed_bytes(N, K) >= (int64_t(1) << 31))
             return HKG_ERR_SIZE;
     }
-    // only the 4-wave kernel has the block-scaled MFMA path
+    // only the 4-wave 256 x 256 kernel has the block-scaled MFMA path
     if (dt == hkg::kMx && opts && opts->schedule != HKG_SCHED_DEFAULT &&
         opts->schedule != HKG_SCHED_INTERLEAVE)
         return HKG_ERR_OPTS;
-    const int64_t Gm = ceil_div(M, kTile), Gn = ceil_div(N, kTile);
+    int64_t Gm = 0, Gn = 0;
     int32_t W = 1, Cc = 1;
     hkg::Schedule sched = hkg::kInterleave;
-    if (Gm > 0 && Gn > 0) {
-        rc = resolve_opts(opts, Gm, Gn, K * elem, &W, &Cc, &sched);
+    if (M > 0 && N > 0) {
+        rc = resolve_opts(opts, M, N, K * elem, dt != hkg::kMx, &Gm, &Gn, &W, &Cc, &sched);
         if (rc != HKG_OK)
             return rc;
     } else if (opts && (opts->remap < 0 || opts->remap > 2 || opts->schedule < 0 ||
-                        opts->schedule > 3)) {
+                        opts->schedule > 4)) {
         return HKG_ERR_OPTS;
     }
     if (M == 0 || N == 0)
@@ -299,7 +327,8 @@ int hkg_default_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *W
     const int64_t kalign = dtype == 0 ? kKAlignBf16 : (dtype == 1 ? kKAlignFp8 : kKAlignMx);
     if ((dtype < 0 || dtype > 2) || M <= 0 || N <= 0 || K < 0 || K % kalign)
         return HKG_ERR_SHAPE;
-    default_remap(ceil_div(M, kTile), ceil_div(N, kTile), K * (dtype == 0 ? 2 : 1), W, C);
+    const int64_t t = tile_edge(default_schedule(M, N, dtype != 2));
+    default_remap(ceil_div(M, t), ceil_div(N, t), K * (dtype == 0 ? 2 : 1), W, C);
     return HKG_OK;
 }
 

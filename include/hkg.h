@@ -14,7 +14,9 @@
  * shape"): one workgroup per 256 x 256 output tile -- 256 threads (4 waves,
  * the default 4-wave interleave) or 512 threads (8 waves, the ping-pong and
  * lockstep schedules) -- on a flat grid of ceil(M/256) * ceil(N/256)
- * workgroups, K consumed 64 (bf16) or 128 (e4m3) at a time; rows past M or N
+ * workgroups (HKG_SCHED_INTERLEAVE_128: 128 x 128 tiles, ceil(M/128) *
+ * ceil(N/128) workgroups of 256 threads), K consumed 64 (bf16) or 128 (e4m3)
+ * at a time; rows past M or N
  * and K past the end read as zeros.  Workgroup ids are remapped to tiles by the
  * chiplet-aware schedule of the same note, section 2 (Pillar 3) / section 7
  * (Algorithm 1), with window height W and per-XCD chunk C.
@@ -61,13 +63,20 @@ enum {
 
 /* In-CU schedule (HipKittens L2 note, section 2 Pillar 2 and section 9.2). */
 enum {
-    HKG_SCHED_DEFAULT = 0,  /* 4-wave interleave (HKG_SCHED_INTERLEAVE)             */
+    HKG_SCHED_DEFAULT = 0,  /* 4-wave interleave: HKG_SCHED_INTERLEAVE, or
+                               HKG_SCHED_INTERLEAVE_128 (bf16, e4m3) when
+                               ceil(M/256) * ceil(N/256) <= 128, i.e. when 256 x 256
+                               tiles would leave over half of the 256 CUs idle      */
     HKG_SCHED_PINGPONG = 1, /* 8-wave ping-pong: 2 groups of 4 waves alternate the
                                MFMA and HBM->LDS roles via s_setprio + barriers      */
     HKG_SCHED_LOCKSTEP = 2, /* all 8 waves compute the same K step (ablation only)   */
-    HKG_SCHED_INTERLEAVE = 3/* 4 waves (one per SIMD), each 128 x 128 of the tile,
+    HKG_SCHED_INTERLEAVE = 3,/* 4 waves (one per SIMD), each 128 x 128 of the tile,
                                loads and LDS reads slotted between its own MFMAs
                                (the note's section 9.1 4-wave interleave)            */
+    HKG_SCHED_INTERLEAVE_128 = 4 /* the same schedule on 128 x 128 output tiles (each
+                               wave 64 x 64; 80 KiB of LDS, two workgroups per CU):
+                               four times the tiles, for grids too small to fill the
+                               GPU with 256 x 256 ones (bf16 and e4m3 only)          */
 };
 
 typedef struct {
@@ -163,11 +172,12 @@ int hkg_mx_pack_scales(int32_t operand, int64_t rows, int64_t K, const void *sca
 /*
  * The (W, C) the library uses for HKG_REMAP_DEFAULT on a shape (host only, no
  * HIP call).  dtype: 0 = bf16, 1 = fp8, 2 = MXFP8.  Returns HKG_ERR_NULL/SHAPE
- * on bad input.  Rule (the L2 and LLC terms of the HipKittens L2 note's
- * section 4 equation): (8, 32) while an operand row holds at most 18944 bytes
- * (K x element size), else (16, 4), whose 256 concurrent tiles share fewer
- * operand panels in the last-level cache; both clamped to the grid
- * (W <= ceil(M/256), C <= tiles/8 + 1).
+ * on bad input.  The grid is the one the default schedule uses (tiles of 256,
+ * or of 128 where HKG_SCHED_DEFAULT picks them).  Rule (the L2 and LLC terms
+ * of the HipKittens L2 note's section 4 equation): (8, 32) while an operand
+ * row holds at most 18944 bytes (K x element size), else (16, 4), whose 256
+ * concurrent tiles share fewer operand panels in the last-level cache; both
+ * clamped to the grid (W <= tile rows, C <= tiles/8 + 1).
  */
 int hkg_default_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *W, int32_t *C);
 

@@ -106,10 +106,15 @@ def test_default_remap():
     assert hkg.hkg_default_remap(8192, 8192, 8192, 2)[0] == hkg.HKG_OK       # MXFP8
     assert hkg.hkg_default_remap(8192, 8192, 8176, 2)[0] == hkg.HKG_ERR_SHAPE
     assert hkg.hkg_default_remap(8192, 8192, 8190, 0)[0] == hkg.HKG_ERR_SHAPE
-    rc, W, C = hkg.hkg_default_remap(256, 256, 256, 1)
+    # small grids run on 128 x 128 tiles by default, and the order is for that grid
+    rc, W, C = hkg.hkg_default_remap(256, 256, 256, 1)     # 2 x 2 tiles of 128
+    assert rc == hkg.HKG_OK and (W, C) == (2, 1)
+    rc, W, C = hkg.hkg_default_remap(256, 256, 256, 2)     # MXFP8: 1 tile of 256
     assert rc == hkg.HKG_OK and (W, C) == (1, 1)
-    rc, W, C = hkg.hkg_default_remap(300, 9000, 64, 0)     # ragged: 2 x 36 tiles
-    assert rc == hkg.HKG_OK and (W, C) == (2, 10)
+    rc, W, C = hkg.hkg_default_remap(300, 9000, 64, 0)     # ragged: 3 x 71 tiles of 128
+    assert rc == hkg.HKG_OK and (W, C) == (3, 27)
+    rc, W, C = hkg.hkg_default_remap(1000, 9000, 64, 0)    # ragged: 4 x 36 tiles of 256
+    assert rc == hkg.HKG_OK and (W, C) == (4, 19)
 
 
 @pytest.mark.parametrize("M,N,K,dtype,want", [
@@ -120,7 +125,8 @@ def test_default_remap():
     (12288, 12288, 12288, 0, (16, 4)),
     (16384, 16384, 16384, 0, (16, 4)),
     (16384, 16384, 20480, 1, (16, 4)),
-    (2048, 2048, 16384, 0, (8, 4)),         # 8 x 8 tiles: (16, 4) with W clamped to 8
+    (2048, 2048, 16384, 0, (16, 4)),        # 16 x 16 tiles of 128: (16, 4) fits
+    (2048, 2048, 32768, 2, (8, 4)),         # MXFP8, 8 x 8 tiles of 256: W clamped to 8
 ])
 def test_default_remap_follows_panel_bytes(M, N, K, dtype, want):
     """Rows longer than 18944 bytes switch the default from an 8 x 32 strip of

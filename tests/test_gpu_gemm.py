@@ -63,8 +63,9 @@ def run_fp8(A, B, sa, sb, opts=None, want_f32=True):
     return _host_bits(C), (Cf.cpu().numpy() if want_f32 else None)
 
 
-SCHEDULES = [hkg.HKG_SCHED_PINGPONG, hkg.HKG_SCHED_LOCKSTEP, hkg.HKG_SCHED_INTERLEAVE]
-SCHED_IDS = ["pingpong", "lockstep", "interleave"]
+SCHEDULES = [hkg.HKG_SCHED_PINGPONG, hkg.HKG_SCHED_LOCKSTEP, hkg.HKG_SCHED_INTERLEAVE,
+             hkg.HKG_SCHED_INTERLEAVE_128]
+SCHED_IDS = ["pingpong", "lockstep", "interleave", "interleave128"]
 
 
 # ---------------------------------------------------------------- remap ------------
@@ -238,7 +239,10 @@ def test_output_identical_across_grid_orders_and_schedules():
                 hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=1, C=6),
                 hkg.make_opts(schedule=hkg.HKG_SCHED_LOCKSTEP),
                 hkg.make_opts(schedule=hkg.HKG_SCHED_INTERLEAVE),
-                hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=3, C=9, schedule=hkg.HKG_SCHED_INTERLEAVE)]
+                hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=3, C=9, schedule=hkg.HKG_SCHED_INTERLEAVE),
+                hkg.make_opts(schedule=hkg.HKG_SCHED_INTERLEAVE_128),
+                hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=8, C=32,
+                              schedule=hkg.HKG_SCHED_INTERLEAVE_128)]
     for o in variants:
         got, _ = run_bf16(A, B, opts=o, want_f32=False)
         np.testing.assert_array_equal(got, base)

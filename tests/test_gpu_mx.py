@@ -196,13 +196,16 @@ def test_no_stray_writes(M, N, K):
     assert (buf[:pad] == 12345).all() and (buf[pad + M * N:] == 12345).all()
 
 
-def test_pingpong_schedule_rejected():
-    _say("mx rejected schedule")
+@pytest.mark.parametrize("sched", [hkg.HKG_SCHED_PINGPONG, hkg.HKG_SCHED_INTERLEAVE_128],
+                         ids=["pingpong", "interleave128"])
+def test_unsupported_schedules_rejected(sched):
+    """Only the 4-wave 256 x 256 kernel has the block-scaled path."""
+    _say("mx rejected schedule %d" % sched)
     A, SA = synth.small_int_mx(9390, 256, 64)
     pa = hkg.mx_pack_scales(_dev(SA), hkg.HKG_MX_OPERAND_A)
     pb = hkg.mx_pack_scales(_dev(SA), hkg.HKG_MX_OPERAND_B)
     C = torch.full((256, 256), 3.0, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(hkg.HkgError):
-        hkg.gemm_mxfp8(_dev(A), _dev(A), pa, pb, C, opts=hkg.make_opts(schedule=hkg.HKG_SCHED_PINGPONG))
+        hkg.gemm_mxfp8(_dev(A), _dev(A), pa, pb, C, opts=hkg.make_opts(schedule=sched))
     torch.cuda.synchronize()
     assert (C.float() == 3.0).all()
