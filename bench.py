@@ -12,7 +12,7 @@ and the CPU oracle timed on a bounded sample as a baseline.
                   [--all] [--remap W,C | --row-major]
                   [--schedule interleave|pingpong|lockstep|interleave128]
                   [--no-cpu-baseline]
-  python bench.py --sizes "1024 2048 ..." [--dtype bf16|fp8]
+  python bench.py --sizes "1024 2048 ..." [--dtype bf16|fp8|mxfp8] [--vendor]
         square-size sweep: each schedule (4-wave 256 and 128 tiles, ping-pong) per
         size, one JSON line each
   python bench.py --sweep "1,1 8,32 5,25 ..." [--workload N | --shape M,N,K --dtype bf16|fp8]
@@ -298,7 +298,7 @@ def sweep(w: synth.Workload, pairs, steps: int, warmup: int) -> None:
                           "TFLOPS": round(w.flops / (ms * 1e-3) / 1e12, 2)}), flush=True)
 
 
-def size_sweep(sizes, dtype: str, warmup: int) -> None:
+def size_sweep(sizes, dtype: str, warmup: int, vendor: bool = False) -> None:
     """Square sizes n x n x n (any n: edge tiles are masked): both in-CU
     schedules on the same inputs, each timed for ~0.2 s twice (forward and
     reverse order); one JSON line per (size, schedule)."""
@@ -311,6 +311,8 @@ def size_sweep(sizes, dtype: str, warmup: int) -> None:
               ("interleave128", hkg.HKG_SCHED_INTERLEAVE_128)]
     if dtype == "mxfp8":     # the block-scaled path exists in the 4-wave 256 x 256 kernel only
         scheds = scheds[:1]
+    elif vendor:             # context only: the vendor library on the same inputs and timing rule
+        scheds.append(("vendor", "vendor"))
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     for n in sizes:
@@ -328,6 +330,19 @@ def size_sweep(sizes, dtype: str, warmup: int) -> None:
         C = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
 
         def run(sc, k):
+            if sc == "vendor":
+                # torch.mm -> hipBLASLt (bf16); torch._scaled_mm on the same
+                # e4m3 bytes and per-tensor scales
+                if dtype == "bf16":
+                    for _ in range(k):
+                        torch.mm(dA, dB.t(), out=C)
+                else:
+                    ta = torch.tensor(sa, dtype=torch.float32, device=dev)
+                    tb = torch.tensor(sb, dtype=torch.float32, device=dev)
+                    a8, b8 = dA.view(torch.float8_e4m3fn), dB.view(torch.float8_e4m3fn)
+                    for _ in range(k):
+                        torch._scaled_mm(a8, b8.t(), scale_a=ta, scale_b=tb, out_dtype=torch.bfloat16)
+                return
             opts = hkg.make_opts(schedule=sc)
             for _ in range(k):
                 if dtype == "bf16":
@@ -356,9 +371,11 @@ def size_sweep(sizes, dtype: str, warmup: int) -> None:
         for name, _ in scheds:
             ms = float(np.mean(times[name]))
             tf = w.flops / (ms * 1e-3) / 1e12
-            print(json.dumps({"size_sweep": dtype, "n": n, "schedule": name, "steps": steps,
-                              "ms": round(ms, 5), "TFLOPS": round(tf, 1),
-                              "frac_of_peak": round(tf / peak, 4)}), flush=True)
+            rec = {"size_sweep": dtype, "n": n, "schedule": name, "steps": steps,
+                   "ms": round(ms, 5), "TFLOPS": round(tf, 1), "frac_of_peak": round(tf / peak, 4)}
+            if name == "vendor":
+                rec["context_only"] = True
+            print(json.dumps(rec), flush=True)
         del dA, dB, C
         torch.cuda.empty_cache()
 
@@ -381,6 +398,8 @@ def main(argv=None) -> int:
     ap.add_argument("--sweep", type=str, default=None, help='"W,C W,C ..." grid orders to time')
     ap.add_argument("--sizes", type=str, default=None,
                     help='"n n ..." square sizes: every schedule per size (with --dtype)')
+    ap.add_argument("--vendor", action="store_true",
+                    help="with --sizes: also time the vendor library on the same inputs (context)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -403,7 +422,7 @@ def main(argv=None) -> int:
         opts = hkg.make_opts(schedule=sched)
 
     if args.sizes:
-        size_sweep([int(v) for v in args.sizes.split()], args.dtype, args.warmup)
+        size_sweep([int(v) for v in args.sizes.split()], args.dtype, args.warmup, args.vendor)
         return 0
     if args.sweep:
         w = custom_workload(args.shape, args.dtype) if args.shape else synth.workload(args.workload)
