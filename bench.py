@@ -308,7 +308,7 @@ def size_sweep(sizes, dtype: str, warmup: int, vendor: bool = False) -> None:
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     scheds = [("interleave", hkg.HKG_SCHED_INTERLEAVE), ("pingpong", hkg.HKG_SCHED_PINGPONG),
-              ("interleave128", hkg.HKG_SCHED_INTERLEAVE_128)]
+              ("interleave128", hkg.HKG_SCHED_INTERLEAVE_128), ("default", hkg.HKG_SCHED_DEFAULT)]
     if dtype == "mxfp8":     # the block-scaled path exists in the 4-wave 256 x 256 kernel only
         scheds = scheds[:1]
     elif vendor:             # context only: the vendor library on the same inputs and timing rule

@@ -112,6 +112,31 @@ hkg::Schedule default_schedule(int64_t M, int64_t N, bool small_ok)
     return small && small_ok ? hkg::kInterleave128 : hkg::kInterleave;
 }
 
+// Rows of a default 256 x 256 launch to keep when the rest goes to a second
+// launch on 128 x 128 tiles (0: no split).  A grid of G > 256 tiles with a
+// partial last round runs that round on a fraction of the CUs; instead the
+// tile rows that fill whole rounds stay on 256 x 256 tiles and the remaining
+// rows (fewer than a round's worth) run as 128 x 128 tiles spread over the
+// whole chip, if those fit in one pass at two workgroups per CU and the
+// idle share of the plain launch, (256 - G % 256) / 256 of a round out of
+// G / 256 + 1, is at least a tenth (measured: 4352^3 +23 %, 6144^3 +4-9 %,
+// 9216^3 +3 %, 10000^3 +1-2 %; 16448^3, 3 % idle, was 3 % slower split).
+// Every kernel sums a block's K steps in the same order, so the output is
+// the same bit for bit as with one launch.
+int64_t split_rows(int64_t M, int64_t N)
+{
+    const int64_t Gm = ceil_div(M, kTile), Gn = ceil_div(N, kTile), G = Gm * Gn;
+    if (G <= 256 || G % 256 == 0)
+        return 0;
+    if ((256 - G % 256) * 10 < 256 * (G / 256 + 1))
+        return 0;
+    const int64_t Gm1 = (G / 256) * 256 / Gn;   // tile rows that fit in the whole rounds
+    if (Gm1 < 1 || Gm1 >= Gm)
+        return 0;
+    const int64_t rest = ceil_div(M - Gm1 * kTile, 128) * ceil_div(N, 128);
+    return rest <= 512 ? Gm1 * kTile : 0;
+}
+
 // Schedule, tile grid (Gm x Gn tiles of the schedule's edge) and grid order
 // of a call; M, N > 0.
 int resolve_opts(const hkg_gemm_opts *opts, int64_t M, int64_t N, int64_t row_bytes,
@@ -208,12 +233,26 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
     if (M == 0 || N == 0)
         return HKG_OK;
 
+    // default schedule and order on a 256 x 256 grid with a partial last
+    // round: the whole rounds here, the remaining rows as a second launch
+    const bool defaults = !opts || (opts->schedule == HKG_SCHED_DEFAULT &&
+                                    opts->remap == HKG_REMAP_DEFAULT);
+    int64_t M1 = M;
+    if (defaults && sched == hkg::kInterleave && dt != hkg::kMx) {
+        const int64_t rows = split_rows(M, N);
+        if (rows > 0) {
+            M1 = rows;
+            Gm = ceil_div(M1, kTile);
+            default_remap(Gm, Gn, K * elem, &W, &Cc);
+        }
+    }
+
     hkg::GemmParams p;
     p.A = A;
     p.B = B;
     p.C = C;
     p.C_f32 = C_f32;
-    p.M = static_cast<int>(M);
+    p.M = static_cast<int>(M1);
     p.N = static_cast<int>(N);
     p.K = static_cast<int>(K);
     p.Gm = static_cast<int>(Gm);
@@ -229,6 +268,22 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
     p.sb_bytes = dt == hkg::kMx ? static_cast<int>(mx_packed_bytes(N, K)) : 0;
 
     hipError_t e = hkg::launch_gemm(dt, sched, p, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess && M1 < M) {
+        // rows M1.. of A and C (M1 is a multiple of 256, so the offsets keep
+        // 16-byte alignment)
+        hkg::GemmParams q = p;
+        q.A = static_cast<const char *>(A) + M1 * K * elem;
+        q.C = static_cast<uint16_t *>(C) + M1 * N;
+        q.C_f32 = C_f32 ? C_f32 + M1 * N : nullptr;
+        q.M = static_cast<int>(M - M1);
+        q.Gm = static_cast<int>(ceil_div(M - M1, 128));
+        q.Gn = static_cast<int>(ceil_div(N, 128));
+        int32_t W2 = 1, C2 = 1;
+        default_remap(q.Gm, q.Gn, K * elem, &W2, &C2);
+        q.W = W2;
+        q.Cc = C2;
+        e = hkg::launch_gemm(dt, hkg::kInterleave128, q, static_cast<hipStream_t>(stream));
+    }
     if (e != hipSuccess) {
         g_last_hip_error = static_cast<int>(e);
         return HKG_ERR_LAUNCH;

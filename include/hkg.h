@@ -27,8 +27,9 @@
  *    host or synchronises.  Work is enqueued on `stream` (a hipStream_t;
  *    NULL = the default stream) and completes asynchronously; buffers must
  *    stay alive until the stream has passed the kernel.
- *  - All arguments are validated before any HIP call.  On any error nothing
- *    is launched and C is untouched.
+ *  - All arguments are validated before any HIP call.  On a validation error
+ *    nothing is launched and C is untouched (a launch failure of the second
+ *    of two default launches can leave the rows of the first written).
  *  - Return value: HKG_OK (0) or a negative hkg_status.
  *  - The library holds no mutable state apart from a thread-local copy of the
  *    last HIP error; it is safe to call from several host threads.
@@ -66,7 +67,12 @@ enum {
     HKG_SCHED_DEFAULT = 0,  /* 4-wave interleave: HKG_SCHED_INTERLEAVE, or
                                HKG_SCHED_INTERLEAVE_128 (bf16, e4m3) when
                                ceil(M/256) * ceil(N/256) <= 128, i.e. when 256 x 256
-                               tiles would leave over half of the 256 CUs idle      */
+                               tiles would leave over half of the 256 CUs idle.
+                               With the default order (bf16, e4m3), a 256 x 256
+                               grid whose last round is partial may run as two
+                               launches on `stream`: the tile rows of the whole
+                               rounds on 256 x 256 tiles, the remaining rows on
+                               128 x 128 tiles (same result bit for bit)          */
     HKG_SCHED_PINGPONG = 1, /* 8-wave ping-pong: 2 groups of 4 waves alternate the
                                MFMA and HBM->LDS roles via s_setprio + barriers      */
     HKG_SCHED_LOCKSTEP = 2, /* all 8 waves compute the same K step (ablation only)   */

@@ -425,3 +425,63 @@ def test_large_ragged_sampled_parity():
     cf = Cf[ipm, ipn].cpu().numpy()
     cb = C.view(torch.int16)[ipm, ipn].cpu().numpy().view(np.uint16)
     check(oracle.gemm_bf16_pairs(A, B, pm, pn), cf, cb, K, "large ragged")
+
+
+# ------------------------------------------------------- split default launch -------
+
+def _split_rows(M, N):
+    """Host model of the default launch's split: 256 x 256 tile rows kept
+    (0 = one launch), as the library documents it."""
+    cd = lambda a, b: -(-a // b)
+    Gm, Gn = cd(M, 256), cd(N, 256)
+    G = Gm * Gn
+    if G <= 256 or G % 256 == 0 or (256 - G % 256) * 10 < 256 * (G // 256 + 1):
+        return 0
+    Gm1 = (G // 256) * 256 // Gn
+    if Gm1 < 1 or Gm1 >= Gm:
+        return 0
+    return Gm1 * 256 if cd(M - Gm1 * 256, 128) * cd(N, 128) <= 512 else 0
+
+
+@pytest.mark.parametrize("dtype,M,N,K", [("bf16", 4352, 4352, 256), ("bf16", 4500, 4400, 136),
+                                         ("fp8", 4352, 4352, 256), ("fp8", 6144, 6144, 144)])
+def test_split_default_launch_identical_to_single_launch(dtype, M, N, K):
+    """A default call whose 256 x 256 grid ends in a partial round runs the
+    rows of the whole rounds on 256 x 256 tiles and the rest as a second
+    launch on 128 x 128 tiles; the result equals one 256 x 256 launch bit for
+    bit, and nothing past row M is written."""
+    assert _split_rows(M, N) > 0
+    _say("split launch %s %dx%dx%d" % (dtype, M, N, K))
+    pad = 16
+    if dtype == "bf16":
+        A = _dev_bf16(synth.f32_to_bf16_bits(synth.normal_f32(9980 + K, M, K)))
+        B = _dev_bf16(synth.f32_to_bf16_bits(synth.normal_f32(9981 + K, N, K)))
+    else:
+        a, sa = synth.e4m3_quantize(synth.normal_f32(9982 + K, M, K))
+        b, sb = synth.e4m3_quantize(synth.normal_f32(9983 + K, N, K))
+        A, B = _dev_u8(a), _dev_u8(b)
+    outs = []
+    for o in (None, hkg.make_opts(schedule=hkg.HKG_SCHED_INTERLEAVE)):
+        Cb = torch.full((M + pad, N), 7.0, dtype=torch.bfloat16, device="cuda")
+        Cf = torch.full((M + pad, N), 7.0, dtype=torch.float32, device="cuda")
+        if dtype == "bf16":
+            hkg.gemm_bf16(A, B, Cb[:M], Cf[:M], opts=o)
+        else:
+            hkg.gemm_fp8(A, B, sa, sb, Cb[:M], Cf[:M], opts=o)
+        torch.cuda.synchronize()
+        assert (Cb[M:].float() == 7.0).all() and (Cf[M:] == 7.0).all()
+        outs.append((_host_bits(Cb[:M]), Cf[:M].cpu().numpy()))
+    np.testing.assert_array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+
+
+def test_split_default_launch_small_integers_exact():
+    M, N, K = 4500, 4400, 128
+    assert _split_rows(M, N) > 0
+    _say("split launch ints %dx%dx%d" % (M, N, K))
+    A = synth.small_int_bf16(9990, M, K)
+    B = synth.small_int_bf16(9991, N, K)
+    cb, cf = run_bf16(A, B)
+    want = bf16_to_f64(A) @ bf16_to_f64(B).T          # small integers: exact in fp64
+    np.testing.assert_array_equal(cf.astype(np.float64), want)
+    np.testing.assert_array_equal(cb, oracle.bf16_round(want))
