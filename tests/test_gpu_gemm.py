@@ -485,3 +485,62 @@ def test_split_default_launch_small_integers_exact():
     want = bf16_to_f64(A) @ bf16_to_f64(B).T          # small integers: exact in fp64
     np.testing.assert_array_equal(cf.astype(np.float64), want)
     np.testing.assert_array_equal(cb, oracle.bf16_round(want))
+
+
+# ---------------------------------------------------------- graphs and streams ------
+
+def test_graph_capture_replays_match_eager():
+    """The entry points only enqueue kernels on the caller's stream (no
+    allocation, memset or synchronisation), so a captured GEMM replays: each
+    replay, with other eager work and synchronisations in between, gives the
+    eager result bit for bit (the default split launch included)."""
+    _say("graph capture")
+    shapes = [(2048, 2048, 512, "bf16"), (4352, 4352, 256, "bf16"), (1024, 768, 256, "fp8")]
+    for M, N, K, dtype in shapes:
+        if dtype == "bf16":
+            A = _dev_bf16(synth.f32_to_bf16_bits(synth.normal_f32(9900 + M, M, K)))
+            B = _dev_bf16(synth.f32_to_bf16_bits(synth.normal_f32(9901 + N, N, K)))
+            call = lambda C, s: hkg.gemm_bf16(A, B, C, stream=s)
+        else:
+            a, sa = synth.e4m3_quantize(synth.normal_f32(9902, M, K))
+            b, sb = synth.e4m3_quantize(synth.normal_f32(9903, N, K))
+            A, B = _dev_u8(a), _dev_u8(b)
+            call = lambda C, s: hkg.gemm_fp8(A, B, sa, sb, C, stream=s)
+        eager = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        call(eager, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        C = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            call(C, s)
+        for rep in range(3):
+            C.fill_(0.0)
+            x = torch.randn(512, 512, device="cuda")      # unrelated eager work
+            (x @ x).sum().item()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(C.view(torch.int16), eager.view(torch.int16)), (M, N, K, dtype, rep)
+
+
+def test_concurrent_streams_independent():
+    """Two GEMMs in flight on two streams at once give their own results."""
+    _say("two streams")
+    M, N, K = 2048, 1536, 1024
+    A1 = synth.f32_to_bf16_bits(synth.normal_f32(9910, M, K))
+    B1 = synth.f32_to_bf16_bits(synth.normal_f32(9911, N, K))
+    A2 = synth.f32_to_bf16_bits(synth.normal_f32(9912, M, K))
+    B2 = synth.f32_to_bf16_bits(synth.normal_f32(9913, N, K))
+    want1, _ = run_bf16(A1, B1, want_f32=False)
+    want2, _ = run_bf16(A2, B2, want_f32=False)
+    d = [_dev_bf16(x) for x in (A1, B1, A2, B2)]
+    C1 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    C2 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        hkg.gemm_bf16(d[0], d[1], C1, stream=s1)
+        hkg.gemm_bf16(d[2], d[3], C2, stream=s2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_host_bits(C1), want1)
+    np.testing.assert_array_equal(_host_bits(C2), want2)
