@@ -120,6 +120,16 @@ def cpu_baseline(w: synth.Workload, A, B, sa, sb, target_s: float = 12.0) -> dic
                       % (rows, w.N, w.K, w.name, dt)}
 
 
+def launch_plan(w: synth.Workload, opts) -> list:
+    """The library's own account of what one GEMM of this workload launches."""
+    import dense_gemm_fp8_amd as hkg
+    rc, launches = hkg.launch_plan(w.M, w.N, w.K, {"bf16": 0, "fp8": 1, "mxfp8": 2}[w.dtype], opts)
+    names = {hkg.HKG_SCHED_PINGPONG: "pingpong", hkg.HKG_SCHED_LOCKSTEP: "lockstep",
+             hkg.HKG_SCHED_INTERLEAVE: "interleave", hkg.HKG_SCHED_INTERLEAVE_128: "interleave128"}
+    return [{"schedule": names[d["schedule"]], "tile": d["tile"], "rows": d["rows"],
+             "workgroups": d["grid"], "W": d["W"], "C": d["C"]} for d in launches]
+
+
 def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
               with_cpu: bool) -> dict:
     import torch
@@ -185,6 +195,7 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
     peak = PEAK_TFLOPS[w.dtype]
 
     facts = load_profile_facts(w.name)
+    plan = launch_plan(w, opts)
     res = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -205,11 +216,12 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
                        "mxfp8": " quantised to MXFP8 (e4m3, one E8M0 scale per 32 along K;"
                                 " step includes packing both scale arrays)"}[w.dtype],
                    "schedule": sched_name,
-                   "remap": ({"remap": opts.remap, "W": opts.W, "C": opts.C} if opts else "default")},
+                   "remap": ({"remap": opts.remap, "W": opts.W, "C": opts.C} if opts else "default"),
+                   "launches": plan},
         "fraction_of_peak": round(tflops / peak, 4),
         "roofline": {
             "bound": "mfma",
-            "kernel": kernel_name(w.dtype, sched_name),
+            "kernel": kernel_name(w.dtype, plan[0]["schedule"] if plan else sched_name),
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": "TFLOP/s",

@@ -55,6 +55,7 @@ EXPORTS = (
     "hkg_mx_packed_scale_bytes",
     "hkg_mx_pack_scales",
     "hkg_default_remap",
+    "hkg_launch_plan",
     "hkg_remap_tile",
     "hkg_remap_tiles_device",
     "hkg_status_string",
@@ -65,6 +66,12 @@ EXPORTS = (
 class hkg_gemm_opts(ctypes.Structure):
     _fields_ = [("remap", ctypes.c_int32), ("W", ctypes.c_int32), ("C", ctypes.c_int32),
                 ("schedule", ctypes.c_int32)]
+
+
+class hkg_launch_plan_t(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int32), ("schedule", ctypes.c_int32 * 2),
+                ("tile", ctypes.c_int32 * 2), ("rows", ctypes.c_int64 * 2),
+                ("grid", ctypes.c_int64 * 2), ("W", ctypes.c_int32 * 2), ("C", ctypes.c_int32 * 2)]
 
 
 class HkgError(RuntimeError):
@@ -108,6 +115,8 @@ def load() -> ctypes.CDLL:
         "hkg_mx_packed_scale_bytes": [i64, i64],
         "hkg_mx_pack_scales": [i32, i64, i64, p, p, p],
         "hkg_default_remap": [i64, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)],
+        "hkg_launch_plan": [i64, i64, i64, i32, ctypes.POINTER(hkg_gemm_opts),
+                            ctypes.POINTER(hkg_launch_plan_t)],
         "hkg_remap_tile": [i64, i64, i32, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)],
         "hkg_remap_tiles_device": [i64, i64, i32, i32, p, p],
         "hkg_status_string": [ctypes.c_int],
@@ -164,6 +173,17 @@ def hkg_default_remap(M, N, K, dtype):
     W, C = ctypes.c_int32(), ctypes.c_int32()
     rc = load().hkg_default_remap(M, N, K, dtype, ctypes.byref(W), ctypes.byref(C))
     return rc, W.value, C.value
+
+
+def launch_plan(M, N, K, dtype, opts=None):
+    """What a GEMM call launches (hkg_launch_plan): (status, [launch dicts])
+    with keys schedule, tile, rows, grid, W, C; dtype 0 bf16, 1 e4m3, 2 MXFP8."""
+    pl = hkg_launch_plan_t()
+    rc = load().hkg_launch_plan(M, N, K, dtype, ctypes.byref(opts) if opts is not None else None,
+                                ctypes.byref(pl))
+    out = [dict(schedule=pl.schedule[i], tile=pl.tile[i], rows=pl.rows[i], grid=pl.grid[i],
+                W=pl.W[i], C=pl.C[i]) for i in range(pl.launches)] if rc == HKG_OK else []
+    return rc, out
 
 
 def hkg_remap_tile(Gm, Gn, W, C, b):

@@ -195,6 +195,61 @@ int resolve_opts(const hkg_gemm_opts *opts, int64_t M, int64_t N, int64_t row_by
     return HKG_OK;
 }
 
+bool opts_in_range(const hkg_gemm_opts *opts)
+{
+    return !opts || (opts->remap >= 0 && opts->remap <= 2 && opts->schedule >= 0 &&
+                     opts->schedule <= 4);
+}
+
+// only the 4-wave 256 x 256 kernel has the block-scaled MFMA path
+bool schedule_supported(hkg::Dtype dt, const hkg_gemm_opts *opts)
+{
+    return dt != hkg::kMx || !opts || opts->schedule == HKG_SCHED_DEFAULT ||
+           opts->schedule == HKG_SCHED_INTERLEAVE;
+}
+
+// What one call launches: one or two GEMMs over consecutive row ranges of C
+// (the second only for the default split of a partial last round).
+struct Plan {
+    int launches;
+    hkg::Schedule sched[2];
+    int64_t rows[2], Gm[2], Gn[2];
+    int32_t W[2], C[2];
+};
+
+// The launches of a call with valid shapes and M, N > 0.
+int plan_gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const hkg_gemm_opts *opts, Plan *pl)
+{
+    if (!schedule_supported(dt, opts))
+        return HKG_ERR_OPTS;
+    const int64_t row_bytes = K * (dt == hkg::kBf16 ? 2 : 1);
+    pl->launches = 1;
+    pl->rows[0] = M;
+    int rc = resolve_opts(opts, M, N, row_bytes, dt != hkg::kMx, &pl->Gm[0], &pl->Gn[0], &pl->W[0],
+                          &pl->C[0], &pl->sched[0]);
+    if (rc != HKG_OK)
+        return rc;
+    // default schedule and order on a 256 x 256 grid with a partial last
+    // round: the whole rounds in launch 0, the remaining rows as launch 1
+    const bool defaults = !opts || (opts->schedule == HKG_SCHED_DEFAULT &&
+                                    opts->remap == HKG_REMAP_DEFAULT);
+    if (defaults && pl->sched[0] == hkg::kInterleave && dt != hkg::kMx) {
+        const int64_t keep = split_rows(M, N);
+        if (keep > 0) {
+            pl->launches = 2;
+            pl->rows[0] = keep;
+            pl->Gm[0] = ceil_div(keep, kTile);
+            default_remap(pl->Gm[0], pl->Gn[0], row_bytes, &pl->W[0], &pl->C[0]);
+            pl->sched[1] = hkg::kInterleave128;
+            pl->rows[1] = M - keep;
+            pl->Gm[1] = ceil_div(M - keep, 128);
+            pl->Gn[1] = ceil_div(N, 128);
+            default_remap(pl->Gm[1], pl->Gn[1], row_bytes, &pl->W[1], &pl->C[1]);
+        }
+    }
+    return HKG_OK;
+}
+
 int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const void *B, float sa,
          float sb, const void *SA, const void *SB, void *C, float *C_f32, void *stream,
          const hkg_gemm_opts *opts)
@@ -215,50 +270,17 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
         if (mx_packed_bytes(M, K) >= (int64_t(1) << 31) || mx_packed_bytes(N, K) >= (int64_t(1) << 31))
             return HKG_ERR_SIZE;
     }
-    // only the 4-wave 256 x 256 kernel has the block-scaled MFMA path
-    if (dt == hkg::kMx && opts && opts->schedule != HKG_SCHED_DEFAULT &&
-        opts->schedule != HKG_SCHED_INTERLEAVE)
-        return HKG_ERR_OPTS;
-    int64_t Gm = 0, Gn = 0;
-    int32_t W = 1, Cc = 1;
-    hkg::Schedule sched = hkg::kInterleave;
-    if (M > 0 && N > 0) {
-        rc = resolve_opts(opts, M, N, K * elem, dt != hkg::kMx, &Gm, &Gn, &W, &Cc, &sched);
-        if (rc != HKG_OK)
-            return rc;
-    } else if (opts && (opts->remap < 0 || opts->remap > 2 || opts->schedule < 0 ||
-                        opts->schedule > 4)) {
-        return HKG_ERR_OPTS;
-    }
     if (M == 0 || N == 0)
-        return HKG_OK;
-
-    // default schedule and order on a 256 x 256 grid with a partial last
-    // round: the whole rounds here, the remaining rows as a second launch
-    const bool defaults = !opts || (opts->schedule == HKG_SCHED_DEFAULT &&
-                                    opts->remap == HKG_REMAP_DEFAULT);
-    int64_t M1 = M;
-    if (defaults && sched == hkg::kInterleave && dt != hkg::kMx) {
-        const int64_t rows = split_rows(M, N);
-        if (rows > 0) {
-            M1 = rows;
-            Gm = ceil_div(M1, kTile);
-            default_remap(Gm, Gn, K * elem, &W, &Cc);
-        }
-    }
+        return opts_in_range(opts) && schedule_supported(dt, opts) ? HKG_OK : HKG_ERR_OPTS;
+    Plan pl;
+    rc = plan_gemm(dt, M, N, K, opts, &pl);
+    if (rc != HKG_OK)
+        return rc;
 
     hkg::GemmParams p;
-    p.A = A;
     p.B = B;
-    p.C = C;
-    p.C_f32 = C_f32;
-    p.M = static_cast<int>(M1);
     p.N = static_cast<int>(N);
     p.K = static_cast<int>(K);
-    p.Gm = static_cast<int>(Gm);
-    p.Gn = static_cast<int>(Gn);
-    p.W = W;
-    p.Cc = Cc;
     p.nk = static_cast<int>(ceil_div(K, kstep));
     // The product of the two per-tensor scales, rounded once to fp32.
     p.scale = dt == hkg::kFp8 ? static_cast<float>(static_cast<double>(sa) * sb) : 1.0f;
@@ -266,27 +288,24 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
     p.SB = SB;
     p.sa_bytes = dt == hkg::kMx ? static_cast<int>(mx_packed_bytes(M, K)) : 0;
     p.sb_bytes = dt == hkg::kMx ? static_cast<int>(mx_packed_bytes(N, K)) : 0;
-
-    hipError_t e = hkg::launch_gemm(dt, sched, p, static_cast<hipStream_t>(stream));
-    if (e == hipSuccess && M1 < M) {
-        // rows M1.. of A and C (M1 is a multiple of 256, so the offsets keep
-        // 16-byte alignment)
-        hkg::GemmParams q = p;
-        q.A = static_cast<const char *>(A) + M1 * K * elem;
-        q.C = static_cast<uint16_t *>(C) + M1 * N;
-        q.C_f32 = C_f32 ? C_f32 + M1 * N : nullptr;
-        q.M = static_cast<int>(M - M1);
-        q.Gm = static_cast<int>(ceil_div(M - M1, 128));
-        q.Gn = static_cast<int>(ceil_div(N, 128));
-        int32_t W2 = 1, C2 = 1;
-        default_remap(q.Gm, q.Gn, K * elem, &W2, &C2);
-        q.W = W2;
-        q.Cc = C2;
-        e = hkg::launch_gemm(dt, hkg::kInterleave128, q, static_cast<hipStream_t>(stream));
-    }
-    if (e != hipSuccess) {
-        g_last_hip_error = static_cast<int>(e);
-        return HKG_ERR_LAUNCH;
+    int64_t row = 0;
+    for (int i = 0; i < pl.launches; ++i) {
+        // launch i covers output rows [row, row + rows[i]); row is 0 or a
+        // multiple of 256, so the offset pointers keep 16-byte alignment
+        p.A = static_cast<const char *>(A) + row * K * elem;
+        p.C = static_cast<uint16_t *>(C) + row * N;
+        p.C_f32 = C_f32 ? C_f32 + row * N : nullptr;
+        p.M = static_cast<int>(pl.rows[i]);
+        p.Gm = static_cast<int>(pl.Gm[i]);
+        p.Gn = static_cast<int>(pl.Gn[i]);
+        p.W = pl.W[i];
+        p.Cc = pl.C[i];
+        const hipError_t e = hkg::launch_gemm(dt, pl.sched[i], p, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) {
+            g_last_hip_error = static_cast<int>(e);
+            return HKG_ERR_LAUNCH;
+        }
+        row += pl.rows[i];
     }
     return HKG_OK;
 }
@@ -379,11 +398,50 @@ int hkg_default_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *W
 {
     if (!W || !C)
         return HKG_ERR_NULL;
-    const int64_t kalign = dtype == 0 ? kKAlignBf16 : (dtype == 1 ? kKAlignFp8 : kKAlignMx);
-    if ((dtype < 0 || dtype > 2) || M <= 0 || N <= 0 || K < 0 || K % kalign)
+    hkg_launch_plan_t pl;
+    const int rc = hkg_launch_plan(M, N, K, dtype, nullptr, &pl);
+    if (rc != HKG_OK)
+        return rc;
+    if (pl.launches == 0)
         return HKG_ERR_SHAPE;
-    const int64_t t = tile_edge(default_schedule(M, N, dtype != 2));
-    default_remap(ceil_div(M, t), ceil_div(N, t), K * (dtype == 0 ? 2 : 1), W, C);
+    *W = pl.W[0];
+    *C = pl.C[0];
+    return HKG_OK;
+}
+
+int hkg_launch_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, const hkg_gemm_opts *opts,
+                    hkg_launch_plan_t *plan)
+{
+    if (!plan)
+        return HKG_ERR_NULL;
+    if (dtype < 0 || dtype > 2)
+        return HKG_ERR_SHAPE;
+    const hkg::Dtype dt = dtype == 0 ? hkg::kBf16 : (dtype == 1 ? hkg::kFp8 : hkg::kMx);
+    const int64_t kalign = dtype == 0 ? kKAlignBf16 : (dtype == 1 ? kKAlignFp8 : kKAlignMx);
+    const int64_t elem = dtype == 0 ? 2 : 1;
+    if (M < 0 || N < 0 || K < 0 || K % kalign)
+        return HKG_ERR_SHAPE;
+    if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31) ||
+        kTile * K * elem >= (int64_t(1) << 31))
+        return HKG_ERR_SIZE;
+    *plan = hkg_launch_plan_t{};
+    if (M == 0 || N == 0)
+        return opts_in_range(opts) && schedule_supported(dt, opts) ? HKG_OK : HKG_ERR_OPTS;
+    Plan pl;
+    const int rc = plan_gemm(dt, M, N, K, opts, &pl);
+    if (rc != HKG_OK)
+        return rc;
+    plan->launches = pl.launches;
+    for (int i = 0; i < pl.launches; ++i) {
+        static const int32_t kSched[] = {HKG_SCHED_PINGPONG, HKG_SCHED_LOCKSTEP, HKG_SCHED_INTERLEAVE,
+                                         HKG_SCHED_INTERLEAVE_128};
+        plan->schedule[i] = kSched[pl.sched[i]];
+        plan->tile[i] = static_cast<int32_t>(tile_edge(pl.sched[i]));
+        plan->rows[i] = pl.rows[i];
+        plan->grid[i] = pl.Gm[i] * pl.Gn[i];
+        plan->W[i] = pl.W[i];
+        plan->C[i] = pl.C[i];
+    }
     return HKG_OK;
 }
 

@@ -178,14 +178,43 @@ int hkg_mx_pack_scales(int32_t operand, int64_t rows, int64_t K, const void *sca
 /*
  * The (W, C) the library uses for HKG_REMAP_DEFAULT on a shape (host only, no
  * HIP call).  dtype: 0 = bf16, 1 = fp8, 2 = MXFP8.  Returns HKG_ERR_NULL/SHAPE
- * on bad input.  The grid is the one the default schedule uses (tiles of 256,
- * or of 128 where HKG_SCHED_DEFAULT picks them).  Rule (the L2 and LLC terms
+ * on bad input.  The grid is that of the default call's first launch
+ * (hkg_launch_plan: W[0], C[0]; tiles of 256, or of 128 where
+ * HKG_SCHED_DEFAULT picks them).  Rule (the L2 and LLC terms
  * of the HipKittens L2 note's section 4 equation): (8, 32) while an operand
  * row holds at most 18944 bytes (K x element size), else (16, 4), whose 256
  * concurrent tiles share fewer operand panels in the last-level cache; both
  * clamped to the grid (W <= tile rows, C <= tiles/8 + 1).
  */
 int hkg_default_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *W, int32_t *C);
+
+/*
+ * What a GEMM call with these shapes and options launches (host only, no HIP
+ * call; the entry points build their launches from the same plan).  Up to two
+ * launches, over consecutive ranges of output rows (the second only for the
+ * default split of a partial last round, see HKG_SCHED_DEFAULT).
+ *   launches     0 (M == 0 or N == 0), 1 or 2
+ *   schedule[i]  HKG_SCHED_* that launch i runs (never HKG_SCHED_DEFAULT)
+ *   tile[i]      its output tile edge, 256 or 128
+ *   rows[i]      output rows it covers; launch 1 starts at row rows[0]
+ *   grid[i]      its workgroups (tiles)
+ *   W[i], C[i]   its grid order
+ * dtype: 0 = bf16, 1 = e4m3, 2 = MXFP8; opts may be NULL (defaults).  Returns
+ * the status the GEMM entry point would return for the shape and options
+ * (HKG_ERR_SHAPE, HKG_ERR_SIZE, HKG_ERR_OPTS) or HKG_ERR_NULL for plan == NULL.
+ */
+typedef struct {
+    int32_t launches;
+    int32_t schedule[2];
+    int32_t tile[2];
+    int64_t rows[2];
+    int64_t grid[2];
+    int32_t W[2];
+    int32_t C[2];
+} hkg_launch_plan_t;
+
+int hkg_launch_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, const hkg_gemm_opts *opts,
+                    hkg_launch_plan_t *plan);
 
 /*
  * The grid remap itself (HipKittens L2 note, section 7 Algorithm 1 reading): flat

@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = hkg.load()
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 14
     assert sorted(hkg.EXPORTS) == names
     for n in names:
         assert getattr(lib, n) is not None
@@ -171,3 +171,56 @@ def test_mxfp8_validation():
         o = hkg.make_opts(schedule=sched)
         assert hkg.hkg_gemm_mxfp8_ex(256, 256, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
                                      o) == hkg.HKG_ERR_OPTS
+
+
+# ---------------------------------------------------------------- launch plan ------
+
+def _plan(M, N, K, dtype=0, opts=None):
+    rc, launches = hkg.launch_plan(M, N, K, dtype, opts)
+    assert rc == hkg.HKG_OK
+    return [(d["schedule"], d["tile"], d["rows"], d["grid"], d["W"], d["C"]) for d in launches]
+
+
+def test_launch_plan_whole_rounds_one_launch():
+    S4, S128 = hkg.HKG_SCHED_INTERLEAVE, hkg.HKG_SCHED_INTERLEAVE_128
+    assert _plan(8192, 8192, 8192) == [(S4, 256, 8192, 1024, 8, 32)]
+    assert _plan(16384, 16384, 16384) == [(S4, 256, 16384, 4096, 16, 4)]
+    assert _plan(16384, 14336, 4096) == [(S4, 256, 16384, 3584, 8, 32)]
+    assert _plan(8192, 8192, 8192, 1) == [(S4, 256, 8192, 1024, 8, 32)]
+
+
+def test_launch_plan_small_grid_uses_128_tiles():
+    S4, S128 = hkg.HKG_SCHED_INTERLEAVE, hkg.HKG_SCHED_INTERLEAVE_128
+    assert _plan(2048, 2048, 2048) == [(S128, 128, 2048, 256, 8, 32)]
+    assert _plan(256, 256, 256) == [(S128, 128, 256, 4, 2, 1)]
+    assert _plan(2048, 2048, 2048, 2) == [(S4, 256, 2048, 64, 8, 9)]        # MXFP8: 256 only
+    assert _plan(3072, 3072, 3072) == [(S4, 256, 3072, 144, 8, 19)]         # 144 > 128 tiles
+
+
+def test_launch_plan_splits_partial_last_round():
+    S4, S128 = hkg.HKG_SCHED_INTERLEAVE, hkg.HKG_SCHED_INTERLEAVE_128
+    # 6144^3: 24 x 24 = 576 tiles = 2 rounds + 64; 21 tile rows (504 tiles) stay on 256,
+    # the last 768 rows run as 6 x 48 tiles of 128
+    assert _plan(6144, 6144, 6144) == [(S4, 256, 5376, 504, 8, 32), (S128, 128, 768, 288, 6, 32)]
+    p = _plan(4500, 4400, 136)
+    assert len(p) == 2 and p[0][2] + p[1][2] == 4500 and p[0][2] % 256 == 0
+    assert len(_plan(16448, 16448, 16448)) == 1        # 3 % idle: not worth a second launch
+    assert len(_plan(6144, 6144, 6144, 2)) == 1        # MXFP8 never splits
+    # an explicit schedule or order is one launch of what was asked for
+    one = _plan(6144, 6144, 6144, 0, hkg.make_opts(schedule=hkg.HKG_SCHED_INTERLEAVE))
+    assert one == [(S4, 256, 6144, 576, 8, 32)]
+    assert len(_plan(6144, 6144, 6144, 0, hkg.make_opts(remap=hkg.HKG_REMAP_ROW_MAJOR))) == 1
+    pp = _plan(6144, 6144, 6144, 0, hkg.make_opts(schedule=hkg.HKG_SCHED_PINGPONG))
+    assert pp == [(hkg.HKG_SCHED_PINGPONG, 256, 6144, 576, 8, 32)]
+
+
+def test_launch_plan_errors_match_entry_points():
+    assert hkg.launch_plan(0, 256, 64, 0)[0] == hkg.HKG_OK
+    assert hkg.launch_plan(0, 256, 64, 0)[1] == []
+    assert hkg.launch_plan(256, 256, 60, 0)[0] == hkg.HKG_ERR_SHAPE
+    assert hkg.launch_plan(256, 256, 64, 3)[0] == hkg.HKG_ERR_SHAPE
+    assert hkg.launch_plan(256, 256, 1 << 23, 0)[0] == hkg.HKG_ERR_SIZE
+    bad = hkg.make_opts(schedule=hkg.HKG_SCHED_PINGPONG)
+    assert hkg.launch_plan(256, 256, 64, 2, bad)[0] == hkg.HKG_ERR_OPTS      # MXFP8
+    assert hkg.launch_plan(0, 256, 64, 2, bad)[0] == hkg.HKG_ERR_OPTS
+    assert hkg.launch_plan(256, 256, 64, 0, hkg.make_opts(schedule=9))[0] == hkg.HKG_ERR_OPTS
