@@ -884,10 +884,13 @@ struct QuadF8 {
     __device__ static constexpr int rot_slot(int i) { return kB == 8 ? 20 + 4 * i : 2 + 2 * i; }
     static constexpr int kSlotTail = kB == 8 ? 30 : 7;
     // MXFP8 only: half 0 forms step t+2's masked A load offset after MFMA
-    // 23; half 1 forms step t+3's B offset after MFMA 12 and moves the next
-    // scales of B blocks 0..3 (last used in half 0) and A blocks 0..3 (last
-    // used by MFMA 15) into fresh registers after MFMA 8 and 16
-    static constexpr int kSlotMaskA = 23, kSlotMaskB = 12, kSlotScaleB = 8, kSlotScaleA = 16;
+    // kSlotMaskA; half 1 forms step t+3's B offset after MFMA kSlotMaskB and
+    // (kB = 8) moves the next scales of B blocks 0..3 (last used in half 0)
+    // and A blocks 0..3 (last used by MFMA 15) into fresh registers after
+    // MFMA 8 and 16.  kB = 4 uses one 32-bit scale word per operand, needed
+    // by every MFMA of the step.
+    static constexpr int kSlotMaskA = kB == 8 ? 23 : 4, kSlotMaskB = kB == 8 ? 12 : 2;
+    static constexpr int kSlotScaleB = 8, kSlotScaleA = 16;
 
     // lane base w of half kH's reads at panel offset off (half 0 reads B only)
     template <int kH, int kW>
@@ -996,17 +999,27 @@ struct QuadCtx {
     // offsets of this wave's 128-row groups in them at K step 0
     __amdgpu_buffer_rsrc_t rsa, rsb;
     int sa_group, sb_group;
+    int s_off_a, s_off_b;            // lane's byte in a K step's 512 scale bytes
 };
 
-// MXFP8: this lane's scales of K step k (one 8-byte load per operand; steps
-// past the end read other groups' or out-of-range bytes and are never used).
-__device__ __forceinline__ MxScales mx_load_scales(const QuadCtx &c, int lane, int k)
+// MXFP8: this lane's scales of K step k (kB = 8: the lane's 8 bytes per
+// operand; kB = 4: the 4 of them that the wave's 64-row quarter of the
+// 128-row group uses; steps past the end read other groups' or out-of-range
+// bytes and are never used).
+template <int kB>
+__device__ __forceinline__ MxScales mx_load_scales(const QuadCtx &c, int k)
 {
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     const int so = __builtin_amdgcn_readfirstlane(k * 512);
-    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(c.rsa, lane * 8, c.sa_group + so, 0);
-    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(c.rsb, lane * 8, c.sb_group + so, 0);
-    return MxScales{{a[0], a[1]}, {b[0], b[1]}};
+    if constexpr (kB == 8) {
+        const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(c.rsa, c.s_off_a, c.sa_group + so, 0);
+        const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(c.rsb, c.s_off_b, c.sb_group + so, 0);
+        return MxScales{{a[0], a[1]}, {b[0], b[1]}};
+    } else {
+        const uint32_t a = __builtin_amdgcn_raw_buffer_load_b32(c.rsa, c.s_off_a, c.sa_group + so, 0);
+        const uint32_t b = __builtin_amdgcn_raw_buffer_load_b32(c.rsb, c.s_off_b, c.sb_group + so, 0);
+        return MxScales{{a, 0u}, {b, 0u}};
+    }
 }
 
 // LDS byte offsets of the panels step t uses: A panel of step t (step t+1
@@ -1050,8 +1063,13 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype, kB>::Frags &f,
     if constexpr (kDtype == kMx) {
         ma = pin_s(ma);
         mb = pin_s(mb);
-        next_a = __builtin_amdgcn_raw_buffer_load_b64(c.rsa, lane * 8, ma, 0);
-        next_b = __builtin_amdgcn_raw_buffer_load_b64(c.rsb, lane * 8, mb, 0);
+        if constexpr (kB == 8) {
+            next_a = __builtin_amdgcn_raw_buffer_load_b64(c.rsa, c.s_off_a, ma, 0);
+            next_b = __builtin_amdgcn_raw_buffer_load_b64(c.rsb, c.s_off_b, mb, 0);
+        } else {
+            next_a[0] = __builtin_amdgcn_raw_buffer_load_b32(c.rsa, c.s_off_a, ma, 0);
+            next_b[0] = __builtin_amdgcn_raw_buffer_load_b32(c.rsb, c.s_off_b, mb, 0);
+        }
     }
     int va = c.voff_a;
     const int vb = kMasked ? rg.vb : c.voff_b;
@@ -1129,9 +1147,9 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype, kB>::Frags &f,
                     rem = pin_s(rem);
                     nr.vb = opaque(c.cb_b < pin_s(rem - kRowBytes) ? c.voff_b : kOutOfRange);
                 }
-                if constexpr (n == Q::kSlotScaleB)
+                if constexpr (kB == 8 && n == Q::kSlotScaleB)
                     nsc_b0 = mov_v(next_b[0]);
-                if constexpr (n == Q::kSlotScaleA)
+                if constexpr (kB == 8 && n == Q::kSlotScaleA)
                     nsc_a0 = mov_v(next_a[0]);
                 if constexpr (n == Q::kSlotTail) {
                     nr.rem = pin_s(pin_s(rem) - kRowBytes);
@@ -1141,8 +1159,10 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype, kB>::Frags &f,
             }
         });
     rg = nr;
-    if constexpr (kDtype == kMx)
+    if constexpr (kDtype == kMx && kB == 8)
         sc = MxScales{{nsc_a0, next_a[1]}, {nsc_b0, next_b[1]}};
+    if constexpr (kDtype == kMx && kB == 4)
+        sc = MxScales{{next_a[0], 0u}, {next_b[0], 0u}};
 }
 
 // kT: output tile edge, 256 (one workgroup per CU, the 160 KiB LDS ring) or
@@ -1188,14 +1208,21 @@ __global__ __launch_bounds__(256, kT == 256 ? 1 : 2) void gemm4_kernel(const Gem
     constexpr bool kMasked = kDtype == kMx;
     c.shift = kMasked ? 0 : __builtin_amdgcn_readfirstlane(p.nk * kRowBytes - ldk);
     MxScales sc = {{0u, 0u}, {0u, 0u}};
-    static_assert(kDtype != kMx || kT == 256, "MXFP8 scales are packed per 128-row wave quarter");
     if constexpr (kDtype == kMx) {
-        // 128-row group g = 2 tm + (w >> 1) of A, 2 tn + (w & 1) of B;
-        // each group holds nk K steps of 64 lanes x 8 bytes
+        // Each 128-row group holds nk K steps of 64 lanes x 8 bytes.  256 x 256
+        // tiles: the wave's 128-row quarter is group 2 tm + (w >> 1) of A and
+        // 2 tn + (w & 1) of B.  128 x 128 tiles: the tile is group tm of A
+        // and tn of B, and the wave's 64-row half of it is bytes 0..3 or 4..7
+        // of each lane's 8 (fragment rows 16 e + x of A, 32 (e >> 1) + ... of
+        // B lie in rows 0..63 for e < 4).
         c.rsa = make_rsrc(p.SA, p.sa_bytes);
         c.rsb = make_rsrc(p.SB, p.sb_bytes);
-        c.sa_group = __builtin_amdgcn_readfirstlane((2 * tm + (c.wave >> 1)) * p.nk * 512);
-        c.sb_group = __builtin_amdgcn_readfirstlane((2 * tn + (c.wave & 1)) * p.nk * 512);
+        const int ga = kT == 256 ? 2 * tm + (c.wave >> 1) : tm;
+        const int gb = kT == 256 ? 2 * tn + (c.wave & 1) : tn;
+        c.sa_group = __builtin_amdgcn_readfirstlane(ga * p.nk * 512);
+        c.sb_group = __builtin_amdgcn_readfirstlane(gb * p.nk * 512);
+        c.s_off_a = lane * 8 + (kT == 256 ? 0 : 4 * (c.wave >> 1));
+        c.s_off_b = lane * 8 + (kT == 256 ? 0 : 4 * (c.wave & 1));
     }
 
     f32x4 acc[kB][kB];
@@ -1209,7 +1236,7 @@ __global__ __launch_bounds__(256, kT == 256 ? 1 : 2) void gemm4_kernel(const Gem
     const int nk = p.nk;
     if (nk > 0) {
         if constexpr (kDtype == kMx)
-            sc = mx_load_scales(c, lane, 0);       // issued first: covered by the wait below
+            sc = mx_load_scales<kB>(c, 0);         // issued first: covered by the wait below
         // K steps 0 and 1.  Masked: either may be partial or (step 1, for
         // nk == 1) absent, and lanes past K load zeros.  Otherwise step 0
         // covers row bytes [-shift, 128 - shift): lanes whose chunk starts
@@ -1321,9 +1348,13 @@ hipError_t launch_gemm(Dtype dt, Schedule s, const GemmParams &p, hipStream_t st
 {
     const dim3 grid(p.Gm * p.Gn), block(512);
     if (dt == kMx) {
-        if (s != kInterleave)
-            return hipErrorInvalidValue;   // only the 4-wave 256 x 256 kernel has the scaled MFMA path
-        hipLaunchKernelGGL((gemm4_kernel<kMx, 256>), grid, dim3(256), 0, stream, p);
+        // only the 4-wave kernel has the block-scaled MFMA path
+        if (s == kInterleave)
+            hipLaunchKernelGGL((gemm4_kernel<kMx, 256>), grid, dim3(256), 0, stream, p);
+        else if (s == kInterleave128)
+            hipLaunchKernelGGL((gemm4_kernel<kMx, 128>), grid, dim3(256), 0, stream, p);
+        else
+            return hipErrorInvalidValue;
     } else if (s == kInterleave) {
         if (dt == kBf16)
             hipLaunchKernelGGL((gemm4_kernel<kBf16, 256>), grid, dim3(256), 0, stream, p);

@@ -22,6 +22,7 @@ constexpr int64_t kKAlignFp8 = 16;
 constexpr int64_t kKAlignMx = 32;      // one E8M0 scale per 32 elements along K
 constexpr int64_t kMxGroupRows = 128;  // packed scales: 128-row groups ...
 constexpr int64_t kMxStepBytes = 512;  // ... of 64 lanes x 8 bytes per K step
+static_assert(kTile % kMxGroupRows == 0, "a launch's first row starts a scale group");
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -104,12 +105,11 @@ int64_t tile_edge(hkg::Schedule s) { return s == hkg::kInterleave128 ? 128 : kTi
 // tiles when the 256 x 256 grid would leave more than half of the 256 CUs
 // idle (at most 128 tiles; 128 x 128 tiles give four times as many, two per
 // CU).  Square sizes: 1024^3 and 2048^3 run 1.8-2.6x faster on 128 x 128
-// tiles, 3072^3 (144 tiles of 256) 10-15 % slower.  small_ok is false for
-// MXFP8, whose block-scaled path exists on 256 x 256 tiles only.
-hkg::Schedule default_schedule(int64_t M, int64_t N, bool small_ok)
+// tiles, 3072^3 (144 tiles of 256) 10-15 % slower.
+hkg::Schedule default_schedule(int64_t M, int64_t N)
 {
     const bool small = ceil_div(M, kTile) * ceil_div(N, kTile) <= 128;
-    return small && small_ok ? hkg::kInterleave128 : hkg::kInterleave;
+    return small ? hkg::kInterleave128 : hkg::kInterleave;
 }
 
 // Rows of a default 256 x 256 launch to keep when the rest goes to a second
@@ -140,10 +140,9 @@ int64_t split_rows(int64_t M, int64_t N)
 // Schedule, tile grid (Gm x Gn tiles of the schedule's edge) and grid order
 // of a call; M, N > 0.
 int resolve_opts(const hkg_gemm_opts *opts, int64_t M, int64_t N, int64_t row_bytes,
-                 bool small_ok, int64_t *Gm, int64_t *Gn, int32_t *W, int32_t *C,
-                 hkg::Schedule *sched)
+                 int64_t *Gm, int64_t *Gn, int32_t *W, int32_t *C, hkg::Schedule *sched)
 {
-    *sched = default_schedule(M, N, small_ok);
+    *sched = default_schedule(M, N);
     if (opts) {
         switch (opts->schedule) {
         case HKG_SCHED_DEFAULT:
@@ -201,11 +200,11 @@ bool opts_in_range(const hkg_gemm_opts *opts)
                      opts->schedule <= 4);
 }
 
-// only the 4-wave 256 x 256 kernel has the block-scaled MFMA path
+// only the 4-wave kernel (either tile) has the block-scaled MFMA path
 bool schedule_supported(hkg::Dtype dt, const hkg_gemm_opts *opts)
 {
     return dt != hkg::kMx || !opts || opts->schedule == HKG_SCHED_DEFAULT ||
-           opts->schedule == HKG_SCHED_INTERLEAVE;
+           opts->schedule == HKG_SCHED_INTERLEAVE || opts->schedule == HKG_SCHED_INTERLEAVE_128;
 }
 
 // What one call launches: one or two GEMMs over consecutive row ranges of C
@@ -225,15 +224,15 @@ int plan_gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const hkg_gemm_opt
     const int64_t row_bytes = K * (dt == hkg::kBf16 ? 2 : 1);
     pl->launches = 1;
     pl->rows[0] = M;
-    int rc = resolve_opts(opts, M, N, row_bytes, dt != hkg::kMx, &pl->Gm[0], &pl->Gn[0], &pl->W[0],
-                          &pl->C[0], &pl->sched[0]);
+    int rc = resolve_opts(opts, M, N, row_bytes, &pl->Gm[0], &pl->Gn[0], &pl->W[0], &pl->C[0],
+                          &pl->sched[0]);
     if (rc != HKG_OK)
         return rc;
     // default schedule and order on a 256 x 256 grid with a partial last
     // round: the whole rounds in launch 0, the remaining rows as launch 1
     const bool defaults = !opts || (opts->schedule == HKG_SCHED_DEFAULT &&
                                     opts->remap == HKG_REMAP_DEFAULT);
-    if (defaults && pl->sched[0] == hkg::kInterleave && dt != hkg::kMx) {
+    if (defaults && pl->sched[0] == hkg::kInterleave) {
         const int64_t keep = split_rows(M, N);
         if (keep > 0) {
             pl->launches = 2;
@@ -284,15 +283,21 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
     p.nk = static_cast<int>(ceil_div(K, kstep));
     // The product of the two per-tensor scales, rounded once to fp32.
     p.scale = dt == hkg::kFp8 ? static_cast<float>(static_cast<double>(sa) * sb) : 1.0f;
-    p.SA = SA;
     p.SB = SB;
-    p.sa_bytes = dt == hkg::kMx ? static_cast<int>(mx_packed_bytes(M, K)) : 0;
     p.sb_bytes = dt == hkg::kMx ? static_cast<int>(mx_packed_bytes(N, K)) : 0;
     int64_t row = 0;
     for (int i = 0; i < pl.launches; ++i) {
         // launch i covers output rows [row, row + rows[i]); row is 0 or a
-        // multiple of 256, so the offset pointers keep 16-byte alignment
+        // multiple of 256, so the offset pointers keep 16-byte alignment, and
+        // A's packed scales start at the group of 128 rows that holds row
         p.A = static_cast<const char *>(A) + row * K * elem;
+        if (dt == hkg::kMx) {
+            p.SA = static_cast<const char *>(SA) + mx_packed_bytes(row, K);
+            p.sa_bytes = static_cast<int>(mx_packed_bytes(pl.rows[i], K));
+        } else {
+            p.SA = nullptr;
+            p.sa_bytes = 0;
+        }
         p.C = static_cast<uint16_t *>(C) + row * N;
         p.C_f32 = C_f32 ? C_f32 + row * N : nullptr;
         p.M = static_cast<int>(pl.rows[i]);

@@ -65,10 +65,10 @@ enum {
 /* In-CU schedule (HipKittens L2 note, section 2 Pillar 2 and section 9.2). */
 enum {
     HKG_SCHED_DEFAULT = 0,  /* 4-wave interleave: HKG_SCHED_INTERLEAVE, or
-                               HKG_SCHED_INTERLEAVE_128 (bf16, e4m3) when
+                               HKG_SCHED_INTERLEAVE_128 when
                                ceil(M/256) * ceil(N/256) <= 128, i.e. when 256 x 256
                                tiles would leave over half of the 256 CUs idle.
-                               With the default order (bf16, e4m3), a 256 x 256
+                               With the default order, a 256 x 256
                                grid whose last round is partial may run as two
                                launches on `stream`: the tile rows of the whole
                                rounds on 256 x 256 tiles, the remaining rows on
@@ -82,7 +82,7 @@ enum {
     HKG_SCHED_INTERLEAVE_128 = 4 /* the same schedule on 128 x 128 output tiles (each
                                wave 64 x 64; 80 KiB of LDS, two workgroups per CU):
                                four times the tiles, for grids too small to fill the
-                               GPU with 256 x 256 ones (bf16 and e4m3 only)          */
+                               GPU with 256 x 256 ones                              */
 };
 
 typedef struct {
@@ -138,8 +138,10 @@ int hkg_gemm_fp8_ex(int64_t M, int64_t N, int64_t K, const void *A, const void *
  *   bytes
  *   C [M][N] bfloat16 = RNE(fp32 accumulator); C_f32: NULL or that fp32 value
  * Shapes: any M, N >= 0; K >= 0 with K % 32 == 0.  Otherwise as the bf16
- * entry point.  Runs the 4-wave interleave kernel (opts->schedule must be
- * HKG_SCHED_DEFAULT or HKG_SCHED_INTERLEAVE, else HKG_ERR_OPTS).
+ * entry point.  Runs the 4-wave interleave kernel on either tile
+ * (opts->schedule must be HKG_SCHED_DEFAULT, HKG_SCHED_INTERLEAVE or
+ * HKG_SCHED_INTERLEAVE_128, else HKG_ERR_OPTS); one packed layout serves
+ * both tiles.
  */
 int hkg_gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                    const void *SA_packed, const void *SB_packed, void *C, float *C_f32,

@@ -109,8 +109,8 @@ def test_default_remap():
     # small grids run on 128 x 128 tiles by default, and the order is for that grid
     rc, W, C = hkg.hkg_default_remap(256, 256, 256, 1)     # 2 x 2 tiles of 128
     assert rc == hkg.HKG_OK and (W, C) == (2, 1)
-    rc, W, C = hkg.hkg_default_remap(256, 256, 256, 2)     # MXFP8: 1 tile of 256
-    assert rc == hkg.HKG_OK and (W, C) == (1, 1)
+    rc, W, C = hkg.hkg_default_remap(256, 256, 256, 2)     # MXFP8 as well: 2 x 2 tiles of 128
+    assert rc == hkg.HKG_OK and (W, C) == (2, 1)
     rc, W, C = hkg.hkg_default_remap(300, 9000, 64, 0)     # ragged: 3 x 71 tiles of 128
     assert rc == hkg.HKG_OK and (W, C) == (3, 27)
     rc, W, C = hkg.hkg_default_remap(1000, 9000, 64, 0)    # ragged: 4 x 36 tiles of 256
@@ -126,7 +126,9 @@ def test_default_remap():
     (16384, 16384, 16384, 0, (16, 4)),
     (16384, 16384, 20480, 1, (16, 4)),
     (2048, 2048, 16384, 0, (16, 4)),        # 16 x 16 tiles of 128: (16, 4) fits
-    (2048, 2048, 32768, 2, (8, 4)),         # MXFP8, 8 x 8 tiles of 256: W clamped to 8
+    (2048, 2048, 32768, 2, (16, 4)),        # MXFP8, 16 x 16 tiles of 128
+    (2560, 2560, 32768, 2, (16, 4)),        # 100 tiles of 256 -> 20 x 20 of 128: W = 16 fits
+    (3072, 3072, 32768, 2, (12, 4)),        # 144 tiles of 256: (16, 4) with W clamped to 12
 ])
 def test_default_remap_follows_panel_bytes(M, N, K, dtype, want):
     """Rows longer than 18944 bytes switch the default from an 8 x 32 strip of
@@ -193,7 +195,7 @@ def test_launch_plan_small_grid_uses_128_tiles():
     S4, S128 = hkg.HKG_SCHED_INTERLEAVE, hkg.HKG_SCHED_INTERLEAVE_128
     assert _plan(2048, 2048, 2048) == [(S128, 128, 2048, 256, 8, 32)]
     assert _plan(256, 256, 256) == [(S128, 128, 256, 4, 2, 1)]
-    assert _plan(2048, 2048, 2048, 2) == [(S4, 256, 2048, 64, 8, 9)]        # MXFP8: 256 only
+    assert _plan(2048, 2048, 2048, 2) == [(S128, 128, 2048, 256, 8, 32)]    # MXFP8 too
     assert _plan(3072, 3072, 3072) == [(S4, 256, 3072, 144, 8, 19)]         # 144 > 128 tiles
 
 
@@ -205,7 +207,7 @@ def test_launch_plan_splits_partial_last_round():
     p = _plan(4500, 4400, 136)
     assert len(p) == 2 and p[0][2] + p[1][2] == 4500 and p[0][2] % 256 == 0
     assert len(_plan(16448, 16448, 16448)) == 1        # 3 % idle: not worth a second launch
-    assert len(_plan(6144, 6144, 6144, 2)) == 1        # MXFP8 never splits
+    assert len(_plan(6144, 6144, 6144, 2)) == 2        # MXFP8 splits like the others
     # an explicit schedule or order is one launch of what was asked for
     one = _plan(6144, 6144, 6144, 0, hkg.make_opts(schedule=hkg.HKG_SCHED_INTERLEAVE))
     assert one == [(S4, 256, 6144, 576, 8, 32)]

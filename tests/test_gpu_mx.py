@@ -84,13 +84,19 @@ SHAPES_EXACT = [(256, 256, 128), (512, 768, 384), (256, 256, 32), (256, 256, 64)
                 (300, 260, 96), (257, 1, 32), (1, 513, 160), (1000, 777, 544), (640, 384, 2048)]
 
 
+# both tiles of the 4-wave kernel (the default picks 128 x 128 for these small grids)
+TILES = [hkg.HKG_SCHED_INTERLEAVE, hkg.HKG_SCHED_INTERLEAVE_128]
+TILE_IDS = ["tile256", "tile128"]
+
+
+@pytest.mark.parametrize("sched", TILES, ids=TILE_IDS)
 @pytest.mark.parametrize("M,N,K", SHAPES_EXACT)
-def test_small_integer_blocks_bit_exact(M, N, K):
+def test_small_integer_blocks_bit_exact(M, N, K, sched):
     # elements in [-2, 2], scales 2^-2..2^2: every product and partial sum is exact in fp32
-    _say("mx ints %dx%dx%d" % (M, N, K))
+    _say("mx ints %dx%dx%d sched=%d" % (M, N, K, sched))
     A, SA = synth.small_int_mx(9310 + K, M, K)
     B, SB = synth.small_int_mx(9320 + K, N, K)
-    cb, cf = run_mx(A, SA, B, SB)
+    cb, cf = run_mx(A, SA, B, SB, opts=hkg.make_opts(schedule=sched))
     want = oracle.gemm_mxfp8(A, B, SA, SB)
     np.testing.assert_array_equal(cf.astype(np.float64), want)
     np.testing.assert_array_equal(cb, oracle.bf16_round(want))
@@ -112,13 +118,14 @@ def test_unit_scales_equal_per_tensor_fp8():
     np.testing.assert_array_equal(cb, C8.view(torch.int16).cpu().numpy().view(np.uint16))
 
 
+@pytest.mark.parametrize("sched", TILES, ids=TILE_IDS)
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (512, 768, 640), (1024, 512, 1536),
                                    (700, 900, 1056)])
-def test_random_matches_oracle(M, N, K):
-    _say("mx random %dx%dx%d" % (M, N, K))
+def test_random_matches_oracle(M, N, K, sched):
+    _say("mx random %dx%dx%d sched=%d" % (M, N, K, sched))
     A, SA = synth.mx_quantize(synth.normal_f32(9340 + K, M, K))
     B, SB = synth.mx_quantize(synth.normal_f32(9350 + K, N, K))
-    cb, cf = run_mx(A, SA, B, SB)
+    cb, cf = run_mx(A, SA, B, SB, opts=hkg.make_opts(schedule=sched))
     check(oracle.gemm_mxfp8(A, B, SA, SB), cf, cb, K, "mxfp8 %dx%dx%d" % (M, N, K))
 
 
@@ -182,8 +189,9 @@ def test_full_size_sampled_parity():
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 260, 96), (257, 1, 32)])
-def test_no_stray_writes(M, N, K):
-    _say("mx canary %dx%dx%d" % (M, N, K))
+@pytest.mark.parametrize("sched", TILES, ids=TILE_IDS)
+def test_no_stray_writes(M, N, K, sched):
+    _say("mx canary %dx%dx%d sched=%d" % (M, N, K, sched))
     A, SA = synth.small_int_mx(9380, M, K)
     B, SB = synth.small_int_mx(9381, N, K)
     pa = hkg.mx_pack_scales(_dev(SA), hkg.HKG_MX_OPERAND_A)
@@ -191,15 +199,15 @@ def test_no_stray_writes(M, N, K):
     pad = 4096
     buf = torch.full((M * N + 2 * pad,), 12345, dtype=torch.int16, device="cuda")
     C = buf[pad:pad + M * N].view(torch.bfloat16).view(M, N)
-    hkg.gemm_mxfp8(_dev(A), _dev(B), pa, pb, C)
+    hkg.gemm_mxfp8(_dev(A), _dev(B), pa, pb, C, opts=hkg.make_opts(schedule=sched))
     torch.cuda.synchronize()
     assert (buf[:pad] == 12345).all() and (buf[pad + M * N:] == 12345).all()
 
 
-@pytest.mark.parametrize("sched", [hkg.HKG_SCHED_PINGPONG, hkg.HKG_SCHED_INTERLEAVE_128],
-                         ids=["pingpong", "interleave128"])
+@pytest.mark.parametrize("sched", [hkg.HKG_SCHED_PINGPONG, hkg.HKG_SCHED_LOCKSTEP],
+                         ids=["pingpong", "lockstep"])
 def test_unsupported_schedules_rejected(sched):
-    """Only the 4-wave 256 x 256 kernel has the block-scaled path."""
+    """Only the 4-wave kernel (either tile) has the block-scaled path."""
     _say("mx rejected schedule %d" % sched)
     A, SA = synth.small_int_mx(9390, 256, 64)
     pa = hkg.mx_pack_scales(_dev(SA), hkg.HKG_MX_OPERAND_A)
@@ -209,3 +217,19 @@ def test_unsupported_schedules_rejected(sched):
         hkg.gemm_mxfp8(_dev(A), _dev(A), pa, pb, C, opts=hkg.make_opts(schedule=sched))
     torch.cuda.synchronize()
     assert (C.float() == 3.0).all()
+
+
+def test_split_default_launch_identical_to_single_launch():
+    """MXFP8's default launch splits a partial last round like the other
+    dtypes (whole rounds on 256 x 256 tiles, the rest on 128 x 128 reading
+    the same packed scales); the result equals one 256 x 256 launch."""
+    M, N, K = 4352, 4352, 288
+    _say("mx split launch %dx%dx%d" % (M, N, K))
+    rc, plan = hkg.launch_plan(M, N, K, 2)
+    assert rc == hkg.HKG_OK and [d["tile"] for d in plan] == [256, 128]
+    A, SA = synth.mx_quantize(synth.normal_f32(9420, M, K))
+    B, SB = synth.mx_quantize(synth.normal_f32(9421, N, K))
+    split = run_mx(A, SA, B, SB)
+    one = run_mx(A, SA, B, SB, opts=hkg.make_opts(schedule=hkg.HKG_SCHED_INTERLEAVE))
+    np.testing.assert_array_equal(split[1].view(np.uint32), one[1].view(np.uint32))
+    np.testing.assert_array_equal(split[0], one[0])
