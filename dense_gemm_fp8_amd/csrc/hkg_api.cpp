@@ -75,6 +75,14 @@ void default_remap(int64_t Gm, int64_t Gn, int64_t row_bytes, int32_t *W, int32_
     *C = static_cast<int32_t>(c);
 }
 
+// One 256-row operand panel is addressed through a buffer resource with a
+// 32-bit byte range, and tile counts / element offsets use 32-bit ints.
+bool sizes_fit(int64_t M, int64_t N, int64_t K, int64_t elem)
+{
+    return kTile * K * elem < (int64_t(1) << 31) && M < (int64_t(1) << 31) &&
+           N < (int64_t(1) << 31) && ceil_div(M, kTile) * ceil_div(N, kTile) < (int64_t(1) << 30);
+}
+
 int validate(int64_t M, int64_t N, int64_t K, int64_t kalign, int64_t elem, const void *A,
              const void *B, const void *C, const float *C_f32)
 {
@@ -88,14 +96,7 @@ int validate(int64_t M, int64_t N, int64_t K, int64_t kalign, int64_t elem, cons
         return HKG_ERR_NULL;
     if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (C_f32 && !aligned16(C_f32)))
         return HKG_ERR_ALIGN;
-    // One 256-row operand panel is addressed through a buffer resource with a
-    // 32-bit byte range, and tile counts / element offsets use 32-bit ints.
-    if (kTile * K * elem >= (int64_t(1) << 31))
-        return HKG_ERR_SIZE;
-    if (ceil_div(M, kTile) * ceil_div(N, kTile) >= (int64_t(1) << 30) ||
-        M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31))
-        return HKG_ERR_SIZE;
-    return HKG_OK;
+    return sizes_fit(M, N, K, elem) ? HKG_OK : HKG_ERR_SIZE;
 }
 
 // Output tile edge of a schedule's kernel.
@@ -426,12 +427,11 @@ int hkg_launch_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, const hkg_ge
     const int64_t elem = dtype == 0 ? 2 : 1;
     if (M < 0 || N < 0 || K < 0 || K % kalign)
         return HKG_ERR_SHAPE;
-    if (M >= (int64_t(1) << 31) || N >= (int64_t(1) << 31) ||
-        kTile * K * elem >= (int64_t(1) << 31))
-        return HKG_ERR_SIZE;
     *plan = hkg_launch_plan_t{};
-    if (M == 0 || N == 0)
+    if (M == 0 || N == 0)   // as the entry points: no launch, only the options checked
         return opts_in_range(opts) && schedule_supported(dt, opts) ? HKG_OK : HKG_ERR_OPTS;
+    if (!sizes_fit(M, N, K, elem))
+        return HKG_ERR_SIZE;
     Plan pl;
     const int rc = plan_gemm(dt, M, N, K, opts, &pl);
     if (rc != HKG_OK)

@@ -61,6 +61,15 @@ def test_size_limit_rejected():
     assert hkg.hkg_gemm_bf16(256, 256, 1 << 22, FAKE, FAKE, FAKE, None, None) == hkg.HKG_ERR_SIZE
 
 
+def test_launch_plan_sizes_like_the_entry_points():
+    # a 256-row bf16 panel of K = 2^22 is 2 GiB; an empty output launches nothing
+    # and is accepted whatever its other extents, by the plan as by the GEMM
+    assert hkg.launch_plan(256, 256, 1 << 22, 0)[0] == hkg.HKG_ERR_SIZE
+    assert hkg.launch_plan(256, 1 << 31, 64, 0)[0] == hkg.HKG_ERR_SIZE
+    assert hkg.launch_plan(0, 256, 1 << 22, 0)[0] == hkg.HKG_OK
+    assert hkg.hkg_gemm_bf16(0, 256, 1 << 22, FAKE, FAKE, FAKE, None, None) == hkg.HKG_OK
+
+
 def test_bad_opts_rejected():
     bad = [hkg.make_opts(remap=7), hkg.make_opts(schedule=9), hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=0, C=4),
            hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=4, C=0)]
