@@ -427,6 +427,62 @@ def test_large_ragged_sampled_parity():
     check(oracle.gemm_bf16_pairs(A, B, pm, pn), cf, cb, K, "large ragged")
 
 
+def test_output_past_2_31_elements():
+    """An output of more than 2^31 elements (4.3 GB of bf16): output offsets in
+    the epilogue and the operand panel bases pass 32 bits.  Entries in
+    {-1, 0, 1} make every result an exact small integer, so sampled outputs
+    (every tile, the rows around element 2^31, the last rows and columns) are
+    compared bit for bit, and canary bands around C must stay untouched."""
+    M, N, K = 65836, 33000, 64
+    assert M * N > 1 << 31
+    _say("output past 2^31 elements: %dx%dx%d" % (M, N, K))
+    A = synth.small_int_bf16(9995, M, K, -1, 1)
+    B = synth.small_int_bf16(9996, N, K, -1, 1)
+    pad = 4096
+    buf = torch.full((M * N + 2 * pad,), 12345, dtype=torch.int16, device="cuda")
+    C = buf[pad:pad + M * N].view(torch.bfloat16).view(M, N)
+    hkg.gemm_bf16(_dev_bf16(A), _dev_bf16(B), C)
+    torch.cuda.synchronize()
+    assert (buf[:pad] == 12345).all() and (buf[pad + M * N:] == 12345).all()
+    pm, pn = synth.sample_pairs(9997, M, N, 20000)
+    m31 = (1 << 31) // N
+    pm = np.concatenate([pm, np.array([m31 - 1, m31, m31, m31 + 1, M - 1, M - 1, M - 2])])
+    pn = np.concatenate([pn, np.array([N - 1, 0, (1 << 31) % N, N - 1, 0, N - 1, N - 8])])
+    ipm, ipn = torch.from_numpy(pm).cuda(), torch.from_numpy(pn).cuda()
+    cb = C.view(torch.int16)[ipm, ipn].cpu().numpy().view(np.uint16)
+    del C, buf
+    torch.cuda.empty_cache()
+    want = oracle.gemm_bf16_pairs(A, B, pm, pn)
+    assert np.all(want == np.round(want)) and np.abs(want).max() <= K
+    np.testing.assert_array_equal(cb, synth.f32_to_bf16_bits(want.astype(np.float32)))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_long_k_exact(dtype):
+    """K of about 2^20 (a 2 MiB bf16 row; the partial K step first, then 16384
+    whole ones): K-step and load offsets reach megabytes.  Entries in
+    {-1, 0, 1} keep every partial sum an integer below 2^24, so the fp32 copy
+    is exact in any order and is compared bit for bit on sampled outputs."""
+    M, N = 300, 260
+    K = (1 << 20) + (8 if dtype == "bf16" else 16)
+    _say("long K %s %dx%dx%d" % (dtype, M, N, K))
+    pm, pn = synth.sample_pairs(9998, M, N, 300)
+    if dtype == "bf16":
+        A = synth.small_int_bf16(9993, M, K, -1, 1)
+        B = synth.small_int_bf16(9994, N, K, -1, 1)
+        want = oracle.gemm_bf16_pairs(A, B, pm, pn)
+    else:
+        A = synth.small_int_e4m3(9993, M, K, -1, 1)
+        B = synth.small_int_e4m3(9994, N, K, -1, 1)
+        want = oracle.gemm_fp8_pairs(A, B, 1.0, 1.0, pm, pn)
+    assert np.all(want == np.round(want)) and np.abs(want).max() < 1 << 24
+    # the default launch (128 x 128 tiles at this size) and 256 x 256 tiles
+    for opts in (None, hkg.make_opts(schedule=hkg.HKG_SCHED_INTERLEAVE)):
+        cb, cf = run_bf16(A, B, opts) if dtype == "bf16" else run_fp8(A, B, 1.0, 1.0, opts)
+        np.testing.assert_array_equal(cf[pm, pn], want.astype(np.float32))
+        np.testing.assert_array_equal(cb[pm, pn], synth.f32_to_bf16_bits(want.astype(np.float32)))
+
+
 # ------------------------------------------------------- split default launch -------
 
 def _split_rows(M, N):

@@ -102,6 +102,24 @@ def test_small_integer_blocks_bit_exact(M, N, K, sched):
     np.testing.assert_array_equal(cb, oracle.bf16_round(want))
 
 
+def test_long_k_exact():
+    """K of about 2^20 (8193 K steps, the last one partial and masked): scale
+    and element offsets reach megabytes.  Elements in {-1, 0, 1} with unit
+    block scales keep every partial sum an integer below 2^24, so the fp32
+    copy is exact in any order; both tile kernels, sampled outputs."""
+    M, N, K = 300, 260, (1 << 20) + 32
+    _say("mx long K %dx%dx%d" % (M, N, K))
+    A, SA = synth.small_int_mx(9397, M, K, -1, 1, 0, 0)
+    B, SB = synth.small_int_mx(9398, N, K, -1, 1, 0, 0)
+    pm, pn = synth.sample_pairs(9399, M, N, 300)
+    want = oracle.gemm_mxfp8_pairs(A, B, SA, SB, pm, pn)
+    assert np.all(want == np.round(want)) and np.abs(want).max() < 1 << 24
+    for opts in (None, hkg.make_opts(schedule=hkg.HKG_SCHED_INTERLEAVE)):
+        cb, cf = run_mx(A, SA, B, SB, opts=opts)
+        np.testing.assert_array_equal(cf[pm, pn].astype(np.float64), want)
+        np.testing.assert_array_equal(cb[pm, pn], oracle.bf16_round(want))
+
+
 def test_unit_scales_equal_per_tensor_fp8():
     _say("mx unit scales vs fp8")
     M, N, K = 512, 512, 512
