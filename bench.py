@@ -10,7 +10,7 @@ and the CPU oracle timed on a bounded sample as a baseline.
 
   python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload 2]
                   [--all] [--remap W,C | --row-major]
-                  [--schedule interleave|pingpong|lockstep|interleave128]
+                  [--schedule interleave|pingpong|lockstep|interleave128|interleave192]
                   [--no-cpu-baseline]
   python bench.py --sizes "1024 2048 ..." [--dtype bf16|fp8|mxfp8] [--vendor]
         square-size sweep: each schedule (4-wave 256 and 128 tiles, ping-pong) per
@@ -75,6 +75,8 @@ def kernel_name(dtype: str, schedule: str) -> str:
         return "gemm4_kernel<%s>" % dtype
     if schedule == "interleave128":
         return "gemm4_kernel<%s,128>" % dtype
+    if schedule == "interleave192":
+        return "gemm4_kernel<%s,192>" % dtype
     return "gemm_kernel<%s,%s>" % (dtype, schedule)
 
 
@@ -125,7 +127,8 @@ def launch_plan(w: synth.Workload, opts) -> list:
     import dense_gemm_fp8_amd as hkg
     rc, launches = hkg.launch_plan(w.M, w.N, w.K, {"bf16": 0, "fp8": 1, "mxfp8": 2}[w.dtype], opts)
     names = {hkg.HKG_SCHED_PINGPONG: "pingpong", hkg.HKG_SCHED_LOCKSTEP: "lockstep",
-             hkg.HKG_SCHED_INTERLEAVE: "interleave", hkg.HKG_SCHED_INTERLEAVE_128: "interleave128"}
+             hkg.HKG_SCHED_INTERLEAVE: "interleave", hkg.HKG_SCHED_INTERLEAVE_128: "interleave128",
+             hkg.HKG_SCHED_INTERLEAVE_192: "interleave192"}
     return [{"schedule": names[d["schedule"]], "tile": d["tile"], "rows": d["rows"],
              "workgroups": d["grid"], "W": d["W"], "C": d["C"]} for d in launches]
 
@@ -321,6 +324,8 @@ def size_sweep(sizes, dtype: str, warmup: int, vendor: bool = False) -> None:
     stream = torch.cuda.current_stream(dev)
     scheds = [("interleave", hkg.HKG_SCHED_INTERLEAVE), ("pingpong", hkg.HKG_SCHED_PINGPONG),
               ("interleave128", hkg.HKG_SCHED_INTERLEAVE_128), ("default", hkg.HKG_SCHED_DEFAULT)]
+    if dtype == "bf16":      # 192 x 192 tiles exist for bf16
+        scheds.insert(3, ("interleave192", hkg.HKG_SCHED_INTERLEAVE_192))
     if dtype == "mxfp8":     # the block-scaled path exists in the 4-wave kernel only
         scheds = [sc for sc in scheds if sc[0] != "pingpong"]
     elif vendor:             # context only: the vendor library on the same inputs and timing rule
@@ -402,7 +407,8 @@ def main(argv=None) -> int:
     ap.add_argument("--all", action="store_true", help="one line per workload 1..5")
     ap.add_argument("--remap", type=str, default=None, help="W,C for the XCD remap")
     ap.add_argument("--row-major", action="store_true")
-    ap.add_argument("--schedule", choices=["interleave", "pingpong", "lockstep", "interleave128"],
+    ap.add_argument("--schedule", choices=["interleave", "pingpong", "lockstep", "interleave128",
+                                           "interleave192"],
                     default="interleave", help="in-CU schedule (default: the library's, interleave)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shape", type=str, default=None, help="M,N,K (custom size)")
@@ -423,7 +429,8 @@ def main(argv=None) -> int:
     hkg.load()
     sched = {"pingpong": hkg.HKG_SCHED_PINGPONG, "lockstep": hkg.HKG_SCHED_LOCKSTEP,
              "interleave": hkg.HKG_SCHED_INTERLEAVE,
-             "interleave128": hkg.HKG_SCHED_INTERLEAVE_128}[args.schedule]
+             "interleave128": hkg.HKG_SCHED_INTERLEAVE_128,
+             "interleave192": hkg.HKG_SCHED_INTERLEAVE_192}[args.schedule]
     opts = None
     if args.row_major:
         opts = hkg.make_opts(remap=hkg.HKG_REMAP_ROW_MAJOR, schedule=sched)

@@ -40,6 +40,7 @@ HKG_SCHED_PINGPONG = 1
 HKG_SCHED_LOCKSTEP = 2
 HKG_SCHED_INTERLEAVE = 3
 HKG_SCHED_INTERLEAVE_128 = 4
+HKG_SCHED_INTERLEAVE_192 = 5
 
 HKG_MX_OPERAND_A = 0
 HKG_MX_OPERAND_B = 1

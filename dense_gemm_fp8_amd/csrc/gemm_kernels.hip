@@ -776,11 +776,13 @@ struct Quad<kBf16, kB> {
     // (0..2kB-1) issues.  kB = 8: half 1's A loads go early (their panel is
     // free once the barrier has passed), which leaves them 85 MFMAs to land
     // before the next barrier waits for them, against 68 when spread like
-    // the B loads.  kB = 4 (16 MFMAs a half): reads on even gaps, loads on
-    // odd ones, A loads again early.
+    // the B loads.  kB = 6 (36 MFMAs a half) and kB = 4 (16): reads on even
+    // gaps, loads on odd ones, A loads again early.
     __device__ static constexpr int dma_slot(int h, int v)
     {
-        return kB == 8 ? (h == 0 ? 8 * v + 4 : 6 * v + 1) : (h == 0 ? 4 * v + 1 : 2 * v + 1);
+        return kB == 8   ? (h == 0 ? 8 * v + 4 : 6 * v + 1)
+               : kB == 6 ? (h == 0 ? 6 * v + 3 : 4 * v + 1)
+                         : (h == 0 ? 4 * v + 1 : 2 * v + 1);
     }
     __device__ static constexpr int read_slot(int r) { return kB == 8 ? 3 * r : 2 * r; }
     // gaps (no load there) for the step's bookkeeping: the next half's A and
@@ -790,11 +792,15 @@ struct Quad<kBf16, kB> {
     // (base_slot(h, w): half h forms lane base w = A, -, B, - ; -1 = none)
     __device__ static constexpr int base_slot(int h, int w)
     {
-        return kB == 8 ? (w == 0 ? 50 : w == 2 ? 53 : -1)
-                       : (w == 0 ? (h == 0 ? 7 : 9) : w == 2 ? 11 : -1);
+        return kB == 8   ? (w == 0 ? 50 : w == 2 ? 53 : -1)
+               : kB == 6 ? (w == 0 ? 24 : w == 2 ? 26 : -1)
+                         : (w == 0 ? (h == 0 ? 7 : 9) : w == 2 ? 11 : -1);
     }
-    __device__ static constexpr int rot_slot(int i) { return kB == 8 ? 55 + i : 12 + i; }
-    static constexpr int kSlotTail = kB == 8 ? 61 : 15;
+    __device__ static constexpr int rot_slot(int i)
+    {
+        return kB == 8 ? 55 + i : kB == 6 ? 28 + i : 12 + i;
+    }
+    static constexpr int kSlotTail = kB == 8 ? 61 : kB == 6 ? 34 : 15;
 
     // lane base w of half kH's reads: slice 1 - kH of the panel at off
     template <int kH, int kW>
@@ -979,9 +985,12 @@ constexpr bool slots_ok()
         ok = ok && Q::rot_slot(i) < Q::kMfmas;
     return ok;
 }
-static_assert(slots_ok<Quad<kBf16, 8>>() && slots_ok<Quad<kBf16, 4>>(), "bf16 slot plans");
+static_assert(slots_ok<Quad<kBf16, 8>>() && slots_ok<Quad<kBf16, 6>>() &&
+                  slots_ok<Quad<kBf16, 4>>(),
+              "bf16 slot plans");
 static_assert(slots_ok<Quad<kFp8, 8>>() && slots_ok<Quad<kFp8, 4>>(), "e4m3 slot plans");
-static_assert(Quad<kBf16, 8>::read_slot(15) < 64 && Quad<kBf16, 4>::read_slot(7) < 16 &&
+static_assert(Quad<kBf16, 8>::read_slot(15) < 64 && Quad<kBf16, 6>::read_slot(11) < 36 &&
+                  Quad<kBf16, 4>::read_slot(7) < 16 &&
                   Quad<kFp8, 8>::b_read_slot(0, 3) < 32 && Quad<kFp8, 4>::b_read_slot(0, 1) < 8,
               "read slots");
 
@@ -1171,7 +1180,7 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype, kB>::Frags &f,
 // the chip).  The wave layout, swizzles, schedule and K order are the same;
 // each wave owns a (kT/2) x (kT/2) quarter, kB = kT/32 blocks a side.
 template <int kDtype, int kT>
-__global__ __launch_bounds__(256, kT == 256 ? 1 : 2) void gemm4_kernel(const GemmParams p)
+__global__ __launch_bounds__(256, kT == 128 ? 2 : 1) void gemm4_kernel(const GemmParams p)
 {
     constexpr int kB = kT / 32;
     constexpr int kP = kT * kRowBytes;   // one panel: kT rows x one K step
@@ -1365,6 +1374,11 @@ hipError_t launch_gemm(Dtype dt, Schedule s, const GemmParams &p, hipStream_t st
             hipLaunchKernelGGL((gemm4_kernel<kBf16, 128>), grid, dim3(256), 0, stream, p);
         else
             hipLaunchKernelGGL((gemm4_kernel<kFp8, 128>), grid, dim3(256), 0, stream, p);
+    } else if (s == kInterleave192) {
+        if (dt == kBf16)
+            hipLaunchKernelGGL((gemm4_kernel<kBf16, 192>), grid, dim3(256), 0, stream, p);
+        else
+            return hipErrorInvalidValue;
     } else if (dt == kBf16) {
         if (s == kPingPong)
             hipLaunchKernelGGL((gemm_kernel<kBf16, kPingPong>), grid, block, 0, stream, p);

@@ -100,15 +100,25 @@ int validate(int64_t M, int64_t N, int64_t K, int64_t kalign, int64_t elem, cons
 }
 
 // Output tile edge of a schedule's kernel.
-int64_t tile_edge(hkg::Schedule s) { return s == hkg::kInterleave128 ? 128 : kTile; }
+int64_t tile_edge(hkg::Schedule s)
+{
+    return s == hkg::kInterleave128 ? 128 : s == hkg::kInterleave192 ? 192 : kTile;
+}
 
 // The default schedule: the 4-wave kernel on 256 x 256 tiles, or on 128 x 128
 // tiles when the 256 x 256 grid would leave more than half of the 256 CUs
 // idle (at most 128 tiles; 128 x 128 tiles give four times as many, two per
-// CU).  Square sizes: 1024^3 and 2048^3 run 1.8-2.6x faster on 128 x 128
-// tiles, 3072^3 (144 tiles of 256) 10-15 % slower.
-hkg::Schedule default_schedule(int64_t M, int64_t N)
+// CU).  bf16 also has 192 x 192 tiles, taken when they fit one round on the
+// 256 CUs (at most 256 tiles) while 128 x 128 ones would not (more than 256,
+// so some CU runs two): each CU then runs one 192-tile instead of two
+// 128-tiles or a single 256-tile.  Square bf16 sizes: 1024^3 .. 2048^3 run
+// 1.8-2.6x faster on 128 x 128 tiles than on 256 x 256; 2304^3 .. 3072^3
+// 8-24 % faster on 192 x 192 tiles than on either other tile.
+hkg::Schedule default_schedule(hkg::Dtype dt, int64_t M, int64_t N)
 {
+    if (dt == hkg::kBf16 && ceil_div(M, 192) * ceil_div(N, 192) <= 256 &&
+        ceil_div(M, 128) * ceil_div(N, 128) > 256)
+        return hkg::kInterleave192;
     const bool small = ceil_div(M, kTile) * ceil_div(N, kTile) <= 128;
     return small ? hkg::kInterleave128 : hkg::kInterleave;
 }
@@ -140,10 +150,10 @@ int64_t split_rows(int64_t M, int64_t N)
 
 // Schedule, tile grid (Gm x Gn tiles of the schedule's edge) and grid order
 // of a call; M, N > 0.
-int resolve_opts(const hkg_gemm_opts *opts, int64_t M, int64_t N, int64_t row_bytes,
+int resolve_opts(hkg::Dtype dt, const hkg_gemm_opts *opts, int64_t M, int64_t N, int64_t row_bytes,
                  int64_t *Gm, int64_t *Gn, int32_t *W, int32_t *C, hkg::Schedule *sched)
 {
-    *sched = default_schedule(M, N);
+    *sched = default_schedule(dt, M, N);
     if (opts) {
         switch (opts->schedule) {
         case HKG_SCHED_DEFAULT:
@@ -159,6 +169,9 @@ int resolve_opts(const hkg_gemm_opts *opts, int64_t M, int64_t N, int64_t row_by
             break;
         case HKG_SCHED_INTERLEAVE_128:
             *sched = hkg::kInterleave128;
+            break;
+        case HKG_SCHED_INTERLEAVE_192:
+            *sched = hkg::kInterleave192;
             break;
         default:
             return HKG_ERR_OPTS;
@@ -198,14 +211,19 @@ int resolve_opts(const hkg_gemm_opts *opts, int64_t M, int64_t N, int64_t row_by
 bool opts_in_range(const hkg_gemm_opts *opts)
 {
     return !opts || (opts->remap >= 0 && opts->remap <= 2 && opts->schedule >= 0 &&
-                     opts->schedule <= 4);
+                     opts->schedule <= 5);
 }
 
-// only the 4-wave kernel (either tile) has the block-scaled MFMA path
+// Only the 4-wave kernel on 256 x 256 and 128 x 128 tiles has the
+// block-scaled MFMA path; 192 x 192 tiles exist for bf16 only.
 bool schedule_supported(hkg::Dtype dt, const hkg_gemm_opts *opts)
 {
-    return dt != hkg::kMx || !opts || opts->schedule == HKG_SCHED_DEFAULT ||
-           opts->schedule == HKG_SCHED_INTERLEAVE || opts->schedule == HKG_SCHED_INTERLEAVE_128;
+    if (!opts || opts->schedule == HKG_SCHED_DEFAULT)
+        return true;
+    if (opts->schedule == HKG_SCHED_INTERLEAVE_192)
+        return dt == hkg::kBf16;
+    return dt != hkg::kMx || opts->schedule == HKG_SCHED_INTERLEAVE ||
+           opts->schedule == HKG_SCHED_INTERLEAVE_128;
 }
 
 // What one call launches: one or two GEMMs over consecutive row ranges of C
@@ -225,7 +243,7 @@ int plan_gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const hkg_gemm_opt
     const int64_t row_bytes = K * (dt == hkg::kBf16 ? 2 : 1);
     pl->launches = 1;
     pl->rows[0] = M;
-    int rc = resolve_opts(opts, M, N, row_bytes, &pl->Gm[0], &pl->Gn[0], &pl->W[0], &pl->C[0],
+    int rc = resolve_opts(dt, opts, M, N, row_bytes, &pl->Gm[0], &pl->Gn[0], &pl->W[0], &pl->C[0],
                           &pl->sched[0]);
     if (rc != HKG_OK)
         return rc;
@@ -439,7 +457,7 @@ int hkg_launch_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, const hkg_ge
     plan->launches = pl.launches;
     for (int i = 0; i < pl.launches; ++i) {
         static const int32_t kSched[] = {HKG_SCHED_PINGPONG, HKG_SCHED_LOCKSTEP, HKG_SCHED_INTERLEAVE,
-                                         HKG_SCHED_INTERLEAVE_128};
+                                         HKG_SCHED_INTERLEAVE_128, HKG_SCHED_INTERLEAVE_192};
         plan->schedule[i] = kSched[pl.sched[i]];
         plan->tile[i] = static_cast<int32_t>(tile_edge(pl.sched[i]));
         plan->rows[i] = pl.rows[i];

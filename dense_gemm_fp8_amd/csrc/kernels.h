@@ -25,8 +25,15 @@ struct GemmParams {
 };
 
 enum Dtype { kBf16 = 0, kFp8 = 1, kMx = 2 };
-// kInterleave128: the 4-wave kernel on 128 x 128 tiles (Gm, Gn count those)
-enum Schedule { kPingPong = 0, kLockstep = 1, kInterleave = 2, kInterleave128 = 3 };
+// kInterleave128 / kInterleave192: the 4-wave kernel on 128 x 128 / 192 x 192
+// tiles (Gm, Gn count those)
+enum Schedule {
+    kPingPong = 0,
+    kLockstep = 1,
+    kInterleave = 2,
+    kInterleave128 = 3,
+    kInterleave192 = 4
+};
 
 hipError_t launch_gemm(Dtype dt, Schedule s, const GemmParams &p, hipStream_t stream);
 hipError_t launch_remap_tiles(int Gm, int Gn, int W, int C, int32_t *out, hipStream_t stream);

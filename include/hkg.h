@@ -68,6 +68,11 @@ enum {
                                HKG_SCHED_INTERLEAVE_128 when
                                ceil(M/256) * ceil(N/256) <= 128, i.e. when 256 x 256
                                tiles would leave over half of the 256 CUs idle.
+                               bf16: HKG_SCHED_INTERLEAVE_192 instead when
+                               ceil(M/192) * ceil(N/192) <= 256 while
+                               ceil(M/128) * ceil(N/128) > 256 (one 192 x 192 tile
+                               per CU in one round, where 128 x 128 ones would not
+                               fit one round).
                                With the default order, a 256 x 256
                                grid whose last round is partial may run as two
                                launches on `stream`: the tile rows of the whole
@@ -79,10 +84,14 @@ enum {
     HKG_SCHED_INTERLEAVE = 3,/* 4 waves (one per SIMD), each 128 x 128 of the tile,
                                loads and LDS reads slotted between its own MFMAs
                                (the note's section 9.1 4-wave interleave)            */
-    HKG_SCHED_INTERLEAVE_128 = 4 /* the same schedule on 128 x 128 output tiles (each
+    HKG_SCHED_INTERLEAVE_128 = 4, /* the same schedule on 128 x 128 output tiles (each
                                wave 64 x 64; 80 KiB of LDS, two workgroups per CU):
                                four times the tiles, for grids too small to fill the
                                GPU with 256 x 256 ones                              */
+    HKG_SCHED_INTERLEAVE_192 = 5  /* the same schedule on 192 x 192 output tiles (each
+                               wave 96 x 96; 120 KiB of LDS, one workgroup per CU),
+                               for grids that fit one round of 256 CUs in 192 x 192
+                               tiles but not in 128 x 128 ones; bf16 only            */
 };
 
 typedef struct {

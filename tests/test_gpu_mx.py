@@ -222,10 +222,12 @@ def test_no_stray_writes(M, N, K, sched):
     assert (buf[:pad] == 12345).all() and (buf[pad + M * N:] == 12345).all()
 
 
-@pytest.mark.parametrize("sched", [hkg.HKG_SCHED_PINGPONG, hkg.HKG_SCHED_LOCKSTEP],
-                         ids=["pingpong", "lockstep"])
+@pytest.mark.parametrize("sched", [hkg.HKG_SCHED_PINGPONG, hkg.HKG_SCHED_LOCKSTEP,
+                                   hkg.HKG_SCHED_INTERLEAVE_192],
+                         ids=["pingpong", "lockstep", "interleave192"])
 def test_unsupported_schedules_rejected(sched):
-    """Only the 4-wave kernel (either tile) has the block-scaled path."""
+    """Only the 4-wave kernel on 256 x 256 or 128 x 128 tiles has the
+    block-scaled path."""
     _say("mx rejected schedule %d" % sched)
     A, SA = synth.small_int_mx(9390, 256, 64)
     pa = hkg.mx_pack_scales(_dev(SA), hkg.HKG_MX_OPERAND_A)
