@@ -324,7 +324,7 @@ def size_sweep(sizes, dtype: str, warmup: int, vendor: bool = False) -> None:
     stream = torch.cuda.current_stream(dev)
     scheds = [("interleave", hkg.HKG_SCHED_INTERLEAVE), ("pingpong", hkg.HKG_SCHED_PINGPONG),
               ("interleave128", hkg.HKG_SCHED_INTERLEAVE_128), ("default", hkg.HKG_SCHED_DEFAULT)]
-    if dtype == "bf16":      # 192 x 192 tiles exist for bf16
+    if dtype != "mxfp8":     # 192 x 192 tiles exist for bf16 and e4m3
         scheds.insert(3, ("interleave192", hkg.HKG_SCHED_INTERLEAVE_192))
     if dtype == "mxfp8":     # the block-scaled path exists in the 4-wave kernel only
         scheds = [sc for sc in scheds if sc[0] != "pingpong"]

@@ -872,23 +872,31 @@ struct QuadF8 {
     static constexpr int kHalfCols = kB / 2;
     static constexpr int kMfmas = kB * kHalfCols;   // per half
     // kB = 4 (8 MFMAs a half, each 32 cycles): half 1 loads on even gaps so
-    // that its tail gap (7) follows the last one
+    // that its tail gap (7) follows the last one.  kB = 6 (18 MFMAs a half):
+    // loads after MFMA 3 v + 1, reads and A-fragment reads after 3 r + 2.
     __device__ static constexpr int dma_slot(int h, int v)
     {
-        return kB == 8 ? 4 * v + 1 : (h == 0 ? 2 * v + 1 : 2 * v);
+        return kB == 8 ? 4 * v + 1 : kB == 6 ? 3 * v + 1 : (h == 0 ? 2 * v + 1 : 2 * v);
     }
     // B fragment kB/2 + r (half 0) or r (half 1)
-    __device__ static constexpr int b_read_slot(int h, int r) { return h == 0 ? 4 * r + 2 : r; }
+    __device__ static constexpr int b_read_slot(int h, int r)
+    {
+        return h == 0 ? (kB == 6 ? 3 * r + 2 : 4 * r + 2) : r;
+    }
     // bookkeeping gaps, as for bf16 (kB = 8: no load or read there in either
     // half; lane bases w = A chunk 0, A chunk 1, B chunk 0, B chunk 1; no slot
     // just before a load slot, whose address arithmetic tends to move up a gap)
     __device__ static constexpr int base_slot(int h, int w)
     {
-        return kB == 8 ? (h == 0 ? 18 : 6) + 4 * w
-                       : (h == 0 ? 2 * w : (w < 2 ? -1 : 2 * w - 1));
+        return kB == 8   ? (h == 0 ? 18 : 6) + 4 * w
+               : kB == 6 ? (h == 0 ? (w < 2 ? 11 + 3 * w : 17) : 3 + 3 * w)
+                         : (h == 0 ? 2 * w : (w < 2 ? -1 : 2 * w - 1));
     }
-    __device__ static constexpr int rot_slot(int i) { return kB == 8 ? 20 + 4 * i : 2 + 2 * i; }
-    static constexpr int kSlotTail = kB == 8 ? 30 : 7;
+    __device__ static constexpr int rot_slot(int i)
+    {
+        return kB == 8 ? 20 + 4 * i : kB == 6 ? (i < 2 ? 3 + 3 * i : 15) : 2 + 2 * i;
+    }
+    static constexpr int kSlotTail = kB == 8 ? 30 : kB == 6 ? 17 : 7;
     // MXFP8 only: half 0 forms step t+2's masked A load offset after MFMA
     // kSlotMaskA; half 1 forms step t+3's B offset after MFMA kSlotMaskB and
     // (kB = 8) moves the next scales of B blocks 0..3 (last used in half 0)
@@ -988,10 +996,13 @@ constexpr bool slots_ok()
 static_assert(slots_ok<Quad<kBf16, 8>>() && slots_ok<Quad<kBf16, 6>>() &&
                   slots_ok<Quad<kBf16, 4>>(),
               "bf16 slot plans");
-static_assert(slots_ok<Quad<kFp8, 8>>() && slots_ok<Quad<kFp8, 4>>(), "e4m3 slot plans");
+static_assert(slots_ok<Quad<kFp8, 8>>() && slots_ok<Quad<kFp8, 6>>() &&
+                  slots_ok<Quad<kFp8, 4>>(),
+              "e4m3 slot plans");
 static_assert(Quad<kBf16, 8>::read_slot(15) < 64 && Quad<kBf16, 6>::read_slot(11) < 36 &&
                   Quad<kBf16, 4>::read_slot(7) < 16 &&
-                  Quad<kFp8, 8>::b_read_slot(0, 3) < 32 && Quad<kFp8, 4>::b_read_slot(0, 1) < 8,
+                  Quad<kFp8, 8>::b_read_slot(0, 3) < 32 && Quad<kFp8, 6>::b_read_slot(0, 2) < 18 &&
+                  Quad<kFp8, 4>::b_read_slot(0, 1) < 8,
               "read slots");
 
 // What the 4-wave loop of one workgroup works on.
@@ -1378,7 +1389,7 @@ hipError_t launch_gemm(Dtype dt, Schedule s, const GemmParams &p, hipStream_t st
         if (dt == kBf16)
             hipLaunchKernelGGL((gemm4_kernel<kBf16, 192>), grid, dim3(256), 0, stream, p);
         else
-            return hipErrorInvalidValue;
+            hipLaunchKernelGGL((gemm4_kernel<kFp8, 192>), grid, dim3(256), 0, stream, p);
     } else if (dt == kBf16) {
         if (s == kPingPong)
             hipLaunchKernelGGL((gemm_kernel<kBf16, kPingPong>), grid, block, 0, stream, p);

@@ -108,15 +108,15 @@ int64_t tile_edge(hkg::Schedule s)
 // The default schedule: the 4-wave kernel on 256 x 256 tiles, or on 128 x 128
 // tiles when the 256 x 256 grid would leave more than half of the 256 CUs
 // idle (at most 128 tiles; 128 x 128 tiles give four times as many, two per
-// CU).  bf16 also has 192 x 192 tiles, taken when they fit one round on the
-// 256 CUs (at most 256 tiles) while 128 x 128 ones would not (more than 256,
-// so some CU runs two): each CU then runs one 192-tile instead of two
-// 128-tiles or a single 256-tile.  Square bf16 sizes: 1024^3 .. 2048^3 run
-// 1.8-2.6x faster on 128 x 128 tiles than on 256 x 256; 2304^3 .. 3072^3
-// 8-24 % faster on 192 x 192 tiles than on either other tile.
+// CU).  bf16 and e4m3 also have 192 x 192 tiles, taken when they fit one
+// round on the 256 CUs (at most 256 tiles) while 128 x 128 ones would not
+// (more than 256, so some CU runs two): each CU then runs one 192-tile
+// instead of two 128-tiles or a single 256-tile.  Square sizes: 1024^3 ..
+// 2048^3 run 1.8-2.6x faster on 128 x 128 tiles than on 256 x 256; 2304^3
+// .. 3072^3 3-32 % faster on 192 x 192 tiles than on either other tile.
 hkg::Schedule default_schedule(hkg::Dtype dt, int64_t M, int64_t N)
 {
-    if (dt == hkg::kBf16 && ceil_div(M, 192) * ceil_div(N, 192) <= 256 &&
+    if (dt != hkg::kMx && ceil_div(M, 192) * ceil_div(N, 192) <= 256 &&
         ceil_div(M, 128) * ceil_div(N, 128) > 256)
         return hkg::kInterleave192;
     const bool small = ceil_div(M, kTile) * ceil_div(N, kTile) <= 128;
@@ -215,15 +215,11 @@ bool opts_in_range(const hkg_gemm_opts *opts)
 }
 
 // Only the 4-wave kernel on 256 x 256 and 128 x 128 tiles has the
-// block-scaled MFMA path; 192 x 192 tiles exist for bf16 only.
+// block-scaled MFMA path (its packed scales follow 128-row groups).
 bool schedule_supported(hkg::Dtype dt, const hkg_gemm_opts *opts)
 {
-    if (!opts || opts->schedule == HKG_SCHED_DEFAULT)
-        return true;
-    if (opts->schedule == HKG_SCHED_INTERLEAVE_192)
-        return dt == hkg::kBf16;
-    return dt != hkg::kMx || opts->schedule == HKG_SCHED_INTERLEAVE ||
-           opts->schedule == HKG_SCHED_INTERLEAVE_128;
+    return dt != hkg::kMx || !opts || opts->schedule == HKG_SCHED_DEFAULT ||
+           opts->schedule == HKG_SCHED_INTERLEAVE || opts->schedule == HKG_SCHED_INTERLEAVE_128;
 }
 
 // What one call launches: one or two GEMMs over consecutive row ranges of C

@@ -68,7 +68,7 @@ enum {
                                HKG_SCHED_INTERLEAVE_128 when
                                ceil(M/256) * ceil(N/256) <= 128, i.e. when 256 x 256
                                tiles would leave over half of the 256 CUs idle.
-                               bf16: HKG_SCHED_INTERLEAVE_192 instead when
+                               bf16 and e4m3: HKG_SCHED_INTERLEAVE_192 instead when
                                ceil(M/192) * ceil(N/192) <= 256 while
                                ceil(M/128) * ceil(N/128) > 256 (one 192 x 192 tile
                                per CU in one round, where 128 x 128 ones would not
@@ -91,7 +91,7 @@ enum {
     HKG_SCHED_INTERLEAVE_192 = 5  /* the same schedule on 192 x 192 output tiles (each
                                wave 96 x 96; 120 KiB of LDS, one workgroup per CU),
                                for grids that fit one round of 256 CUs in 192 x 192
-                               tiles but not in 128 x 128 ones; bf16 only            */
+                               tiles but not in 128 x 128 ones; bf16 and e4m3        */
 };
 
 typedef struct {

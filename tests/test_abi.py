@@ -205,10 +205,10 @@ def test_launch_plan_small_grid_uses_128_tiles():
     assert _plan(2048, 2048, 2048) == [(S128, 128, 2048, 256, 8, 32)]
     assert _plan(256, 256, 256) == [(S128, 128, 256, 4, 2, 1)]
     assert _plan(2048, 2048, 2048, 2) == [(S128, 128, 2048, 256, 8, 32)]    # MXFP8 too
-    assert _plan(3072, 3072, 3072, 1) == [(S4, 256, 3072, 144, 8, 19)]      # e4m3: 144 > 128 tiles
+    assert _plan(3072, 3072, 3072, 2) == [(S4, 256, 3072, 144, 8, 19)]      # MXFP8: 144 > 128 tiles
 
 
-def test_launch_plan_bf16_192_tiles_when_they_fill_one_round():
+def test_launch_plan_192_tiles_when_they_fill_one_round():
     S4, S128, S192 = (hkg.HKG_SCHED_INTERLEAVE, hkg.HKG_SCHED_INTERLEAVE_128,
                       hkg.HKG_SCHED_INTERLEAVE_192)
     # 192-tiles fit one round (<= 256) while 128-tiles would not (> 256)
@@ -220,8 +220,8 @@ def test_launch_plan_bf16_192_tiles_when_they_fill_one_round():
     assert _plan(2048, 2048, 2048)[0][:2] == (S128, 128)
     assert _plan(3328, 3328, 3328)[0][:2] == (S4, 256)
     assert _plan(8192, 8192, 8192)[0][:2] == (S4, 256)
-    # bf16 only: e4m3 and MXFP8 keep their tiles
-    assert _plan(2304, 2304, 2304, 1)[0][:2] == (S128, 128)
+    # e4m3 alike; MXFP8 (scales packed per 128 rows) keeps its tiles
+    assert _plan(2304, 2304, 2304, 1)[0][:2] == (S192, 192)
     assert _plan(2304, 2304, 2304, 2)[0][:2] == (S128, 128)
 
 
@@ -248,11 +248,9 @@ def test_launch_plan_192_tiles_on_request():
     # 3072 / 192 = 16: 256 tiles, one whole round of 256 CUs
     assert _plan(3072, 3072, 3072, 0, o) == [(S192, 192, 3072, 256, 8, 32)]
     assert _plan(1000, 700, 64, 0, o)[0][1:4] == (192, 1000, 6 * 4)          # ragged edges
-    assert hkg.launch_plan(3072, 3072, 3072, 1, o)[0] == hkg.HKG_ERR_OPTS     # bf16 only
-    assert hkg.launch_plan(3072, 3072, 3072, 2, o)[0] == hkg.HKG_ERR_OPTS
-    assert hkg.launch_plan(0, 3072, 3072, 1, o)[0] == hkg.HKG_ERR_OPTS
-    assert hkg.hkg_gemm_fp8_ex(256, 256, 128, FAKE, FAKE, 1.0, 1.0, FAKE, None, None,
-                               o) == hkg.HKG_ERR_OPTS
+    assert _plan(3072, 3072, 3072, 1, o) == [(S192, 192, 3072, 256, 8, 32)]  # e4m3 too
+    assert hkg.launch_plan(3072, 3072, 3072, 2, o)[0] == hkg.HKG_ERR_OPTS     # not MXFP8
+    assert hkg.launch_plan(0, 3072, 3072, 2, o)[0] == hkg.HKG_ERR_OPTS
 
 
 def test_launch_plan_errors_match_entry_points():
