@@ -108,19 +108,28 @@ int64_t tile_edge(hkg::Schedule s)
 // The default schedule: the 4-wave kernel on 256 x 256 tiles, or on 128 x 128
 // tiles when the 256 x 256 grid would leave more than half of the 256 CUs
 // idle (at most 128 tiles; 128 x 128 tiles give four times as many, two per
-// CU).  bf16 and e4m3 also have 192 x 192 tiles, taken when they fit one
-// round on the 256 CUs (at most 256 tiles) while 128 x 128 ones would not
-// (more than 256, so some CU runs two): each CU then runs one 192-tile
-// instead of two 128-tiles or a single 256-tile.  Square sizes: 1024^3 ..
-// 2048^3 run 1.8-2.6x faster on 128 x 128 tiles than on 256 x 256; 2304^3
-// .. 3072^3 3-32 % faster on 192 x 192 tiles than on either other tile.
+// CU).  bf16 and e4m3 also have 192 x 192 tiles, taken
+//  - when they fit one round on the 256 CUs (at most 256 tiles) while
+//    128 x 128 ones would not (more than 256, so some CU runs two): each CU
+//    then runs one 192-tile instead of two 128-tiles or a single 256-tile;
+//  - when they fill whole rounds while the 256 x 256 grid ends in a round at
+//    least a quarter full (a smaller remainder costs the split launch less).
+// Square sizes: 1024^3 .. 2048^3 run 1.9-2.6x faster on 128 x 128 tiles than
+// on 256 x 256; 2304^3 .. 3072^3 4-36 % faster on 192 x 192 tiles than on
+// either other tile, 6144^3 3-8 % faster than 256 x 256 tiles with the split
+// (9216^3, whose 256 x 256 remainder is 16 tiles, 5 % slower).
 hkg::Schedule default_schedule(hkg::Dtype dt, int64_t M, int64_t N)
 {
-    if (dt != hkg::kMx && ceil_div(M, 192) * ceil_div(N, 192) <= 256 &&
-        ceil_div(M, 128) * ceil_div(N, 128) > 256)
-        return hkg::kInterleave192;
-    const bool small = ceil_div(M, kTile) * ceil_div(N, kTile) <= 128;
-    return small ? hkg::kInterleave128 : hkg::kInterleave;
+    const int64_t g256 = ceil_div(M, kTile) * ceil_div(N, kTile);
+    const int64_t g192 = ceil_div(M, 192) * ceil_div(N, 192);
+    const int64_t g128 = ceil_div(M, 128) * ceil_div(N, 128);
+    if (dt != hkg::kMx) {
+        if (g192 <= 256 && g128 > 256)
+            return hkg::kInterleave192;
+        if (g256 > 256 && g192 % 256 == 0 && g256 % 256 >= 64)
+            return hkg::kInterleave192;
+    }
+    return g256 <= 128 ? hkg::kInterleave128 : hkg::kInterleave;
 }
 
 // Rows of a default 256 x 256 launch to keep when the rest goes to a second

@@ -72,7 +72,9 @@ enum {
                                ceil(M/192) * ceil(N/192) <= 256 while
                                ceil(M/128) * ceil(N/128) > 256 (one 192 x 192 tile
                                per CU in one round, where 128 x 128 ones would not
-                               fit one round).
+                               fit one round), or when the 192 x 192 tiles fill
+                               whole rounds of 256 while the 256 x 256 grid ends
+                               in a round at least a quarter full.
                                With the default order, a 256 x 256
                                grid whose last round is partial may run as two
                                launches on `stream`: the tile rows of the whole

@@ -220,6 +220,11 @@ def test_launch_plan_192_tiles_when_they_fill_one_round():
     assert _plan(2048, 2048, 2048)[0][:2] == (S128, 128)
     assert _plan(3328, 3328, 3328)[0][:2] == (S4, 256)
     assert _plan(8192, 8192, 8192)[0][:2] == (S4, 256)
+    # whole rounds of 192-tiles against a 256 x 256 grid ending a quarter full
+    assert _plan(6144, 6144, 6144) == [(S192, 192, 6144, 1024, 8, 32)]     # 576 = 2 x 256 + 64
+    assert _plan(3072, 12288, 4096)[0][:4] == (S192, 192, 3072, 1024)
+    assert len(_plan(9216, 9216, 9216)) == 2                               # 1296 = 5 x 256 + 16: split
+    assert _plan(12288, 12288, 12288)[0][:2] == (S4, 256)                  # 2304 = 9 x 256
     # e4m3 alike; MXFP8 (scales packed per 128 rows) keeps its tiles
     assert _plan(2304, 2304, 2304, 1)[0][:2] == (S192, 192)
     assert _plan(2304, 2304, 2304, 2)[0][:2] == (S128, 128)
@@ -227,13 +232,12 @@ def test_launch_plan_192_tiles_when_they_fill_one_round():
 
 def test_launch_plan_splits_partial_last_round():
     S4, S128 = hkg.HKG_SCHED_INTERLEAVE, hkg.HKG_SCHED_INTERLEAVE_128
-    # 6144^3: 24 x 24 = 576 tiles = 2 rounds + 64; 21 tile rows (504 tiles) stay on 256,
-    # the last 768 rows run as 6 x 48 tiles of 128
-    assert _plan(6144, 6144, 6144) == [(S4, 256, 5376, 504, 8, 32), (S128, 128, 768, 288, 6, 32)]
+    # 6144^3 MXFP8 (no 192 tile): 24 x 24 = 576 tiles = 2 rounds + 64; 21 tile rows
+    # (504 tiles) stay on 256, the last 768 rows run as 6 x 48 tiles of 128
+    assert _plan(6144, 6144, 6144, 2) == [(S4, 256, 5376, 504, 8, 32), (S128, 128, 768, 288, 6, 32)]
     p = _plan(4500, 4400, 136)
     assert len(p) == 2 and p[0][2] + p[1][2] == 4500 and p[0][2] % 256 == 0
     assert len(_plan(16448, 16448, 16448)) == 1        # 3 % idle: not worth a second launch
-    assert len(_plan(6144, 6144, 6144, 2)) == 2        # MXFP8 splits like the others
     # an explicit schedule or order is one launch of what was asked for
     one = _plan(6144, 6144, 6144, 0, hkg.make_opts(schedule=hkg.HKG_SCHED_INTERLEAVE))
     assert one == [(S4, 256, 6144, 576, 8, 32)]

@@ -503,13 +503,15 @@ def _split_rows(M, N):
 
 
 @pytest.mark.parametrize("dtype,M,N,K", [("bf16", 4352, 4352, 256), ("bf16", 4500, 4400, 136),
-                                         ("fp8", 4352, 4352, 256), ("fp8", 6144, 6144, 144)])
+                                         ("fp8", 4352, 4352, 256), ("fp8", 4500, 4400, 144)])
 def test_split_default_launch_identical_to_single_launch(dtype, M, N, K):
     """A default call whose 256 x 256 grid ends in a partial round runs the
     rows of the whole rounds on 256 x 256 tiles and the rest as a second
     launch on 128 x 128 tiles; the result equals one 256 x 256 launch bit for
     bit, and nothing past row M is written."""
-    assert _split_rows(M, N) > 0
+    keep = _split_rows(M, N)
+    plan = hkg.launch_plan(M, N, K, 0 if dtype == "bf16" else 1)[1]
+    assert keep > 0 and [(d["tile"], d["rows"]) for d in plan] == [(256, keep), (128, M - keep)]
     _say("split launch %s %dx%dx%d" % (dtype, M, N, K))
     pad = 16
     if dtype == "bf16":
@@ -536,7 +538,7 @@ def test_split_default_launch_identical_to_single_launch(dtype, M, N, K):
 
 def test_split_default_launch_small_integers_exact():
     M, N, K = 4500, 4400, 128
-    assert _split_rows(M, N) > 0
+    assert _split_rows(M, N) > 0 and len(hkg.launch_plan(M, N, K, 0)[1]) == 2
     _say("split launch ints %dx%dx%d" % (M, N, K))
     A = synth.small_int_bf16(9990, M, K)
     B = synth.small_int_bf16(9991, N, K)
