@@ -15,9 +15,11 @@ and the CPU oracle timed on a bounded sample as a baseline.
   python bench.py --sizes "1024 2048 ..." [--dtype bf16|fp8|mxfp8] [--vendor]
         square-size sweep: each schedule (4-wave 256 and 128 tiles, ping-pong) per
         size, one JSON line each
-  python bench.py --sweep "1,1 8,32 5,25 ..." [--workload N | --shape M,N,K --dtype bf16|fp8]
+  python bench.py --sweep "1,1 8,32 5,25 8,32,i192 ..." [--workload N | --shape M,N,K --dtype bf16|fp8]
         grid-order sweep: one JSON line per (W, C) on the same resident inputs
-        ("1,1" is row-major order); used to choose the library's default (W, C)
+        ("1,1" is row-major order; a third field picks the kernel: i = 4-wave on
+        256x256 tiles (default), i128 / i192 = on 128x128 / 192x192 tiles, p =
+        ping-pong, l = lockstep); used to choose the library's default (W, C)
 """
 from __future__ import annotations
 
@@ -274,7 +276,8 @@ def sweep(w: synth.Workload, pairs, steps: int, warmup: int) -> None:
     rc, dW, dC = hkg.hkg_default_remap(w.M, w.N, w.K, 0 if w.dtype == "bf16" else 1)
 
     scheds = {"p": hkg.HKG_SCHED_PINGPONG, "l": hkg.HKG_SCHED_LOCKSTEP,
-              "i": hkg.HKG_SCHED_INTERLEAVE}
+              "i": hkg.HKG_SCHED_INTERLEAVE, "i128": hkg.HKG_SCHED_INTERLEAVE_128,
+              "i192": hkg.HKG_SCHED_INTERLEAVE_192}
 
     def run(W, Cc, n, sc="i"):
         opts = hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=W, C=Cc, schedule=scheds[sc])
