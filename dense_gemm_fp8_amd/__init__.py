@@ -30,6 +30,7 @@ HKG_ERR_SIZE = -4
 HKG_ERR_OPTS = -5
 HKG_ERR_DEVICE = -6
 HKG_ERR_LAUNCH = -7
+HKG_ERR_OVERLAP = -8
 
 HKG_REMAP_DEFAULT = 0
 HKG_REMAP_ROW_MAJOR = 1

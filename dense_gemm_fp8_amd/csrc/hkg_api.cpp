@@ -83,6 +83,14 @@ bool sizes_fit(int64_t M, int64_t N, int64_t K, int64_t elem)
            N < (int64_t(1) << 31) && ceil_div(M, kTile) * ceil_div(N, kTile) < (int64_t(1) << 30);
 }
 
+// Whether byte ranges [p, p + pb) and [q, q + qb) share a byte.
+bool overlaps(const void *p, int64_t pb, const void *q, int64_t qb)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return p && q && pb > 0 && qb > 0 && a < b + static_cast<uintptr_t>(qb) &&
+           b < a + static_cast<uintptr_t>(pb);
+}
+
 int validate(int64_t M, int64_t N, int64_t K, int64_t kalign, int64_t elem, const void *A,
              const void *B, const void *C, const float *C_f32)
 {
@@ -96,7 +104,16 @@ int validate(int64_t M, int64_t N, int64_t K, int64_t kalign, int64_t elem, cons
         return HKG_ERR_NULL;
     if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (C_f32 && !aligned16(C_f32)))
         return HKG_ERR_ALIGN;
-    return sizes_fit(M, N, K, elem) ? HKG_OK : HKG_ERR_SIZE;
+    if (!sizes_fit(M, N, K, elem))
+        return HKG_ERR_SIZE;
+    // Tiles read operand panels while other tiles write C: an output that
+    // shares a byte with an input, or the two outputs with each other, would
+    // give a wrong result.  (A and B may alias: both are only read.)
+    const int64_t ab = M * K * elem, bb = N * K * elem, cb = M * N * 2, fb = M * N * 4;
+    if (overlaps(C, cb, A, ab) || overlaps(C, cb, B, bb) || overlaps(C_f32, fb, A, ab) ||
+        overlaps(C_f32, fb, B, bb) || overlaps(C_f32, fb, C, cb))
+        return HKG_ERR_OVERLAP;
+    return HKG_OK;
 }
 
 // Output tile edge of a schedule's kernel.
@@ -292,6 +309,10 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
         // the packed scales are read through 32-bit buffer ranges
         if (mx_packed_bytes(M, K) >= (int64_t(1) << 31) || mx_packed_bytes(N, K) >= (int64_t(1) << 31))
             return HKG_ERR_SIZE;
+        const int64_t sab = mx_packed_bytes(M, K), sbb = mx_packed_bytes(N, K);
+        if (overlaps(C, M * N * 2, SA, sab) || overlaps(C, M * N * 2, SB, sbb) ||
+            overlaps(C_f32, M * N * 4, SA, sab) || overlaps(C_f32, M * N * 4, SB, sbb))
+            return HKG_ERR_OVERLAP;
     }
     if (M == 0 || N == 0)
         return opts_in_range(opts) && schedule_supported(dt, opts) ? HKG_OK : HKG_ERR_OPTS;
@@ -411,6 +432,8 @@ int hkg_mx_pack_scales(int32_t operand, int64_t rows, int64_t K, const void *sca
     if (rows >= (int64_t(1) << 31) || kTile * K >= (int64_t(1) << 31) ||
         mx_packed_bytes(rows, K) >= (int64_t(1) << 31))
         return HKG_ERR_SIZE;
+    if (overlaps(packed, mx_packed_bytes(rows, K), scales, rows * (K / kKAlignMx)))
+        return HKG_ERR_OVERLAP;
     hipError_t e = hkg::launch_mx_pack(
         operand, static_cast<int>(rows), static_cast<int>(K / kKAlignMx),
         static_cast<int>(ceil_div(K, kKStepFp8)), static_cast<int>(ceil_div(rows, kMxGroupRows)),
@@ -524,6 +547,7 @@ const char *hkg_status_string(int status)
     case HKG_ERR_OPTS: return "invalid hkg_gemm_opts";
     case HKG_ERR_DEVICE: return "device query failed";
     case HKG_ERR_LAUNCH: return "kernel launch failed";
+    case HKG_ERR_OVERLAP: return "an output overlaps an input or the other output";
     default: return "unknown status";
     }
 }

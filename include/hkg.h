@@ -52,7 +52,9 @@ typedef enum {
     HKG_ERR_SIZE = -4,    /* a per-tile operand panel exceeds the 32-bit buffer range */
     HKG_ERR_OPTS = -5,    /* invalid hkg_gemm_opts                                   */
     HKG_ERR_DEVICE = -6,  /* the current device is not gfx950 or cannot be queried   */
-    HKG_ERR_LAUNCH = -7   /* the kernel launch failed; see hkg_last_hip_error()      */
+    HKG_ERR_LAUNCH = -7,  /* the kernel launch failed; see hkg_last_hip_error()      */
+    HKG_ERR_OVERLAP = -8  /* C or C_f32 shares bytes with A, B, the packed MXFP8
+                             scales or the other output (A and B may alias)          */
 } hkg_status;
 
 /* Grid order (the remap of the HipKittens L2 note, section 2 Pillar 3 / section 7 Algorithm 1). */
@@ -114,7 +116,7 @@ typedef struct {
  * Shapes: any M, N >= 0; K >= 0 with K % 8 == 0 so operand rows stay 16-byte
  * aligned (K == 0 writes zeros; M == 0 or N == 0 is a no-op).  Edge tiles
  * (M or N not multiples of 256, K not a multiple of 64) are handled inside the
- * kernels.  C must not overlap A or B.
+ * kernels.  C must not overlap A or B (HKG_ERR_OVERLAP).
  */
 int hkg_gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                   void *C, float *C_f32, void *stream);
@@ -175,7 +177,7 @@ int64_t hkg_mx_packed_scale_bytes(int64_t rows, int64_t K);
  * Rearrange one operand's E8M0 scales into the order the GEMM kernel reads.
  *   scales  [rows][K/32] bytes, row-major, device (no alignment needed)
  *   packed  device, 16-byte aligned, hkg_mx_packed_scale_bytes(rows, K) bytes,
- *           caller-owned; must not overlap `scales`
+ *           caller-owned; must not overlap `scales` (HKG_ERR_OVERLAP)
  * Layout: byte e (0..7) of lane l (0..63) of K step t of 128-row group g, at
  * offset ((g * ceil(K/128) + t) * 64 + l) * 8 + e, is the scale of row
  * 128 g + rho(e, l) and k block 4 t + l / 16, where with x = l % 16

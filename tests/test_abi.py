@@ -34,6 +34,7 @@ def test_status_strings():
 
 
 FAKE = 1 << 20          # aligned, never dereferenced: every call below fails validation
+FB, FC = FAKE + (64 << 20), FAKE + (128 << 20)   # distinct fake B and C (no overlap)
 
 
 @pytest.mark.parametrize("M,N,K", [(-256, 256, 64), (256, -1, 64), (256, 256, -8), (256, 256, 63),
@@ -70,11 +71,33 @@ def test_launch_plan_sizes_like_the_entry_points():
     assert hkg.hkg_gemm_bf16(0, 256, 1 << 22, FAKE, FAKE, FAKE, None, None) == hkg.HKG_OK
 
 
+def test_overlapping_outputs_rejected():
+    # an output sharing a byte with an input (or with the other output) is refused
+    # before any launch; inputs may alias each other
+    M, N, K = 256, 256, 64
+    a, b = FAKE, FAKE + (64 << 20)
+    c = FAKE + (128 << 20)
+    assert hkg.hkg_gemm_bf16(M, N, K, a, b, a, None, None) == hkg.HKG_ERR_OVERLAP
+    assert hkg.hkg_gemm_bf16(M, N, K, a, b, a + M * K * 2 - 16, None, None) == hkg.HKG_ERR_OVERLAP
+    assert hkg.hkg_gemm_bf16(M, N, K, a, b, b - M * N * 2 + 16, None, None) == hkg.HKG_ERR_OVERLAP
+    assert hkg.hkg_gemm_bf16(M, N, K, a, b, c, c + M * N * 2 - 16, None) == hkg.HKG_ERR_OVERLAP
+    assert hkg.hkg_gemm_bf16(M, N, K, a, b, c, b, None) == hkg.HKG_ERR_OVERLAP
+    assert hkg.hkg_gemm_fp8(M, N, 128, a, b, 1.0, 1.0, b + 4096, None, None) == hkg.HKG_ERR_OVERLAP
+    sa, sb = FAKE + (192 << 20), FAKE + (200 << 20)
+    assert hkg.hkg_gemm_mxfp8(M, N, 128, a, b, sa, sb, sa, None, None) == hkg.HKG_ERR_OVERLAP
+    assert hkg.hkg_mx_pack_scales(0, M, 128, FAKE, FAKE + 16, None) == hkg.HKG_ERR_OVERLAP
+    # adjacent (touching, not sharing) buffers and A == B pass validation: any
+    # other status (no device here) is not an overlap
+    assert hkg.hkg_gemm_bf16(M, N, K, a, b, a + M * K * 2, None, None) != hkg.HKG_ERR_OVERLAP
+    assert hkg.hkg_gemm_bf16(M, N, K, a, a, c, None, None) != hkg.HKG_ERR_OVERLAP
+    assert "overlap" in hkg.hkg_status_string(hkg.HKG_ERR_OVERLAP)
+
+
 def test_bad_opts_rejected():
     bad = [hkg.make_opts(remap=7), hkg.make_opts(schedule=9), hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=0, C=4),
            hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=4, C=0)]
     for o in bad:
-        assert hkg.hkg_gemm_bf16_ex(256, 256, 64, FAKE, FAKE, FAKE, None, None, o) == hkg.HKG_ERR_OPTS
+        assert hkg.hkg_gemm_bf16_ex(256, 256, 64, FAKE, FB, FC, None, None, o) == hkg.HKG_ERR_OPTS
 
 
 def test_empty_output_is_a_noop():
@@ -175,12 +198,13 @@ def test_mxfp8_validation():
     g = hkg.hkg_gemm_mxfp8
     for K in (16, 48, 100):
         assert g(256, 256, K, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == hkg.HKG_ERR_SHAPE
-    assert g(256, 256, 64, FAKE, FAKE, None, FAKE, FAKE, None, None) == hkg.HKG_ERR_NULL
-    assert g(256, 256, 64, FAKE, FAKE, FAKE, FAKE + 8, FAKE, None, None) == hkg.HKG_ERR_ALIGN
+    SA, SB = FAKE + (192 << 20), FAKE + (200 << 20)
+    assert g(256, 256, 64, FAKE, FB, None, SB, FC, None, None) == hkg.HKG_ERR_NULL
+    assert g(256, 256, 64, FAKE, FB, SA, SB + 8, FC, None, None) == hkg.HKG_ERR_ALIGN
     assert g(0, 256, 64, None, None, None, None, None, None, None) == hkg.HKG_OK
     for sched in (hkg.HKG_SCHED_PINGPONG, hkg.HKG_SCHED_LOCKSTEP):
         o = hkg.make_opts(schedule=sched)
-        assert hkg.hkg_gemm_mxfp8_ex(256, 256, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+        assert hkg.hkg_gemm_mxfp8_ex(256, 256, 64, FAKE, FB, SA, SB, FC, None, None,
                                      o) == hkg.HKG_ERR_OPTS
 
 

@@ -305,6 +305,47 @@ def test_rejected_call_leaves_output_untouched():
     assert (C.float() == 3.0).all()
 
 
+def test_shared_operand_and_overlapping_output():
+    """A passed as both operands (A*A^T) is a valid call; an output placed over an
+    input, or over the other output, is refused and nothing is written."""
+    _say("A*A^T and overlap rejection")
+    M, K = 512, 320
+    A = synth.small_int_bf16(9950, M, K)
+    dA = _dev_bf16(A)
+    C = hkg.gemm_bf16(dA, dA)
+    torch.cuda.synchronize()
+    a = bf16_to_f64(A).astype(np.int64)
+    np.testing.assert_array_equal(_host_bits(C), oracle.bf16_round((a @ a.T).astype(np.float64)))
+    A8 = synth.small_int_e4m3(9951, M, K)
+    d8 = _dev_u8(A8)
+    C8 = hkg.gemm_fp8(d8, d8, 1.0, 1.0)
+    torch.cuda.synchronize()
+    a8 = oracle.e4m3_table()[A8].astype(np.int64)
+    np.testing.assert_array_equal(_host_bits(C8), oracle.bf16_round((a8 @ a8.T).astype(np.float64)))
+
+    # one buffer: [A (M*K bf16) | C (M*M bf16) | C_f32 (M*M fp32)], each region 16-byte aligned
+    buf = torch.full((M * K + M * M + 2 * M * M,), 777, dtype=torch.int16, device="cuda")
+    buf[:M * K].copy_(dA.view(torch.int16).reshape(-1))
+    snap = buf.clone()
+    pa = buf.data_ptr()
+    pc = pa + M * K * 2
+    pf = pc + M * M * 2
+    s = torch.cuda.current_stream().cuda_stream
+    bad = [(pa + 64 * K * 2, None),           # C starts inside A (row 64)
+           (pc, pc + M * M * 2 - 16),         # C_f32 starts inside C
+           (pc, pa + 16)]                     # C_f32 over A
+    for c_, f_ in bad:
+        assert hkg.hkg_gemm_bf16(M, M, K, pa, pa, c_, f_, s) == hkg.HKG_ERR_OVERLAP
+    torch.cuda.synchronize()
+    assert torch.equal(buf, snap)
+    # the non-overlapping layout of the same buffer is accepted and gives A*A^T
+    assert hkg.hkg_gemm_bf16(M, M, K, pa, pa, pc, pf, s) == hkg.HKG_OK
+    torch.cuda.synchronize()
+    got = buf[M * K:M * K + M * M].view(torch.bfloat16).view(M, M)
+    assert torch.equal(got.view(torch.int16), C.view(torch.int16))
+    assert torch.equal(buf[:M * K], snap[:M * K])
+
+
 # ---------------------------------------------------------------- full sizes -------
 
 @pytest.mark.parametrize("idx", [2, 3, 4, 5])
