@@ -116,7 +116,8 @@ typedef struct {
  * Shapes: any M, N >= 0; K >= 0 with K % 8 == 0 so operand rows stay 16-byte
  * aligned (K == 0 writes zeros; M == 0 or N == 0 is a no-op).  Edge tiles
  * (M or N not multiples of 256, K not a multiple of 64) are handled inside the
- * kernels.  C must not overlap A or B (HKG_ERR_OVERLAP).
+ * kernels.  C and C_f32 must not share a byte with A, B or each other
+ * (HKG_ERR_OVERLAP); A and B may be the same buffer.
  */
 int hkg_gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                   void *C, float *C_f32, void *stream);
