@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import dense_gemm_fp8_amd as hkg
@@ -252,6 +253,35 @@ def test_launch_plan_192_tiles_when_they_fill_one_round():
     # e4m3 alike; MXFP8 (scales packed per 128 rows) keeps its tiles
     assert _plan(2304, 2304, 2304, 1)[0][:2] == (S192, 192)
     assert _plan(2304, 2304, 2304, 2)[0][:2] == (S128, 128)
+
+
+def test_launch_plan_invariants_over_random_shapes():
+    # whatever the shape, the launches cover the M rows exactly, each grid is its
+    # row block in tiles of its edge, and a split keeps whole 256-rows first
+    rng = np.random.default_rng(4242)
+    edge = {hkg.HKG_SCHED_INTERLEAVE: 256, hkg.HKG_SCHED_INTERLEAVE_128: 128,
+            hkg.HKG_SCHED_INTERLEAVE_192: 192}
+    for _ in range(400):
+        M, N = (int(v) for v in rng.integers(1, 20000, 2))
+        dt = int(rng.integers(0, 3))
+        K = 32 * int(rng.integers(1, 200))
+        rc, L = hkg.launch_plan(M, N, K, dt)
+        assert rc == hkg.HKG_OK, (M, N, K, dt)
+        assert 1 <= len(L) <= 2
+        assert sum(d["rows"] for d in L) == M
+        for d in L:
+            t = edge[d["schedule"]]
+            assert d["tile"] == t
+            gm, gn = -(-d["rows"] // t), -(-N // t)
+            assert d["grid"] == gm * gn
+            assert 1 <= d["W"] <= gm and d["C"] >= 1
+            if dt == 2:
+                assert t != 192                      # MXFP8 has no 192 x 192 kernel
+        if len(L) == 2:
+            assert L[0]["tile"] == 256 and L[0]["rows"] % 256 == 0
+            assert L[1]["tile"] == 128 and L[1]["grid"] <= 512
+            G = -(-M // 256) * -(-N // 256)          # the single-launch 256 x 256 grid
+            assert L[0]["grid"] <= 256 * (G // 256)  # the first launch fits its whole rounds
 
 
 def test_launch_plan_splits_partial_last_round():
