@@ -346,6 +346,39 @@ def test_shared_operand_and_overlapping_output():
     assert torch.equal(buf[:M * K], snap[:M * K])
 
 
+def test_random_shapes_default_launch_exact():
+    """16 seeded shapes (M, N up to 4700, ragged; K a multiple of 16 up to 512),
+    alternating bf16 / e4m3, each through the default launch (every tile edge and
+    a split launch among them): small-integer operands make the exact product the
+    oracle's fp64 one, so C_f32 and C must match bit for bit."""
+    rng = np.random.default_rng(7709)
+    tiles, splits = set(), 0
+    tab = oracle.e4m3_table()
+    for i in range(16):
+        M, N = (int(v) for v in rng.integers(1, 4700, 2))
+        K = 16 * int(rng.integers(1, 33))
+        dt = i % 2
+        rc, plan = hkg.launch_plan(M, N, K, dt)
+        assert rc == hkg.HKG_OK
+        tiles |= {d["tile"] for d in plan}
+        splits += len(plan) == 2
+        _say("random shape %d: %s %dx%dx%d plan %s" % (i, ("bf16", "e4m3")[dt], M, N, K,
+                                                     [(d["tile"], d["rows"]) for d in plan]))
+        if dt == 0:
+            A = synth.small_int_bf16(7000 + i, M, K)
+            B = synth.small_int_bf16(7100 + i, N, K)
+            cb, cf = run_bf16(A, B)
+            want = bf16_to_f64(A) @ bf16_to_f64(B).T
+        else:
+            A = synth.small_int_e4m3(7000 + i, M, K)
+            B = synth.small_int_e4m3(7100 + i, N, K)
+            cb, cf = run_fp8(A, B, 1.0, 1.0)
+            want = tab[A] @ tab[B].T
+        np.testing.assert_array_equal(cf.astype(np.float64), want)
+        np.testing.assert_array_equal(cb, oracle.bf16_round(want))
+    assert tiles == {128, 192, 256} and splits >= 1
+
+
 # ---------------------------------------------------------------- full sizes -------
 
 @pytest.mark.parametrize("idx", [2, 3, 4, 5])
