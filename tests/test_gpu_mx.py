@@ -253,3 +253,27 @@ def test_split_default_launch_identical_to_single_launch():
     one = run_mx(A, SA, B, SB, opts=hkg.make_opts(schedule=hkg.HKG_SCHED_INTERLEAVE))
     np.testing.assert_array_equal(split[1].view(np.uint32), one[1].view(np.uint32))
     np.testing.assert_array_equal(split[0], one[0])
+
+
+def test_random_shapes_default_launch_exact():
+    """10 seeded ragged shapes (M, N up to 4700, K = 32, 64 or 96)
+    through the default MXFP8 launch, which among them takes both tile edges and
+    a split launch; small-integer blocks make every sum exact."""
+    rng = np.random.default_rng(7879)
+    tiles, splits = set(), 0
+    for i in range(10):
+        M, N = (int(v) for v in rng.integers(1, 4700, 2))
+        K = 32 * int(rng.integers(1, 4))
+        rc, plan = hkg.launch_plan(M, N, K, 2)
+        assert rc == hkg.HKG_OK
+        tiles |= {d["tile"] for d in plan}
+        splits += len(plan) == 2
+        _say("mx random shape %d: %dx%dx%d plan %s" % (i, M, N, K,
+                                                     [(d["tile"], d["rows"]) for d in plan]))
+        A, SA = synth.small_int_mx(7200 + i, M, K)
+        B, SB = synth.small_int_mx(7300 + i, N, K)
+        cb, cf = run_mx(A, SA, B, SB)
+        want = oracle.gemm_mxfp8(A, B, SA, SB)
+        np.testing.assert_array_equal(cf.astype(np.float64), want)
+        np.testing.assert_array_equal(cb, oracle.bf16_round(want))
+    assert tiles == {128, 256} and splits >= 1
