@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(0, -8, -1):
+    for s in range(0, -9, -1):
         assert hkg.hkg_status_string(s) != "unknown status"
     assert hkg.hkg_status_string(5) == "unknown status"
 
