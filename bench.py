@@ -318,9 +318,9 @@ def sweep(w: synth.Workload, pairs, steps: int, warmup: int) -> None:
 
 
 def size_sweep(sizes, dtype: str, warmup: int, vendor: bool = False) -> None:
-    """Square sizes n x n x n (any n: edge tiles are masked): both in-CU
-    schedules on the same inputs, each timed for ~0.2 s twice (forward and
-    reverse order); one JSON line per (size, schedule)."""
+    """Sizes given as n (n x n x n) or "MxNxK" (any extents: edge tiles are
+    masked): every schedule on the same inputs, each timed for ~0.2 s twice
+    (forward and reverse order); one JSON line per (size, schedule)."""
     import torch
     import dense_gemm_fp8_amd as hkg
 
@@ -337,7 +337,8 @@ def size_sweep(sizes, dtype: str, warmup: int, vendor: bool = False) -> None:
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     for n in sizes:
-        w = custom_workload("%d,%d,%d" % (n, n, n), dtype)
+        M, N, K = (int(v) for v in n.split("x")) if "x" in n else (int(n),) * 3
+        w = custom_workload("%d,%d,%d" % (M, N, K), dtype)
         A, B, sa, sb = synth.make_inputs(w)
         if dtype == "bf16":
             dA = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -348,7 +349,7 @@ def size_sweep(sizes, dtype: str, warmup: int, vendor: bool = False) -> None:
                 pSA = hkg.mx_pack_scales(torch.from_numpy(sa).to(dev), hkg.HKG_MX_OPERAND_A)
                 pSB = hkg.mx_pack_scales(torch.from_numpy(sb).to(dev), hkg.HKG_MX_OPERAND_B)
         del A, B
-        C = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
 
         def run(sc, k):
             if sc == "vendor":
@@ -392,7 +393,7 @@ def size_sweep(sizes, dtype: str, warmup: int, vendor: bool = False) -> None:
         for name, _ in scheds:
             ms = float(np.mean(times[name]))
             tf = w.flops / (ms * 1e-3) / 1e12
-            rec = {"size_sweep": dtype, "n": n, "schedule": name, "steps": steps,
+            rec = {"size_sweep": dtype, "n": int(n) if "x" not in n else n, "schedule": name, "steps": steps,
                    "ms": round(ms, 5), "TFLOPS": round(tf, 1), "frac_of_peak": round(tf / peak, 4)}
             if name == "vendor":
                 rec["context_only"] = True
@@ -419,7 +420,7 @@ def main(argv=None) -> int:
     ap.add_argument("--dtype", choices=["bf16", "fp8", "mxfp8"], default="bf16")
     ap.add_argument("--sweep", type=str, default=None, help='"W,C W,C ..." grid orders to time')
     ap.add_argument("--sizes", type=str, default=None,
-                    help='"n n ..." square sizes: every schedule per size (with --dtype)')
+                    help='"n n ..." square sizes or "MxNxK ...": every schedule per size (with --dtype)')
     ap.add_argument("--vendor", action="store_true",
                     help="with --sizes: also time the vendor library on the same inputs (context)")
     args = ap.parse_args(argv)
@@ -445,7 +446,7 @@ def main(argv=None) -> int:
         opts = hkg.make_opts(schedule=sched)
 
     if args.sizes:
-        size_sweep([int(v) for v in args.sizes.split()], args.dtype, args.warmup, args.vendor)
+        size_sweep(args.sizes.split(), args.dtype, args.warmup, args.vendor)
         return 0
     if args.sweep:
         w = custom_workload(args.shape, args.dtype) if args.shape else synth.workload(args.workload)
