@@ -52,7 +52,9 @@ typedef enum {
     HKG_ERR_SIZE = -4,    /* a per-tile operand panel exceeds the 32-bit buffer range */
     HKG_ERR_OPTS = -5,    /* invalid hkg_gemm_opts                                   */
     HKG_ERR_DEVICE = -6,  /* the current device is not gfx950 or cannot be queried   */
-    HKG_ERR_LAUNCH = -7,  /* the kernel launch failed; see hkg_last_hip_error()      */
+    HKG_ERR_LAUNCH = -7,  /* a kernel launch failed; see hkg_last_hip_error().  When
+                             the call was split into two launches (hkg_launch_plan),
+                             the rows of the first may already be written         */
     HKG_ERR_OVERLAP = -8  /* C or C_f32 shares bytes with A, B, the packed MXFP8
                              scales or the other output (A and B may alias)          */
 } hkg_status;
