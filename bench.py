@@ -39,6 +39,11 @@ if ROOT not in sys.path:
 from dense_gemm_fp8_amd import synth  # noqa: E402
 
 METRIC = "GEMM TFLOPS at 8192³ bf16 (fraction of 2.5 PF peak); L2/LLC hit %"
+# Eq. 1 of the HipKittens L2 note (section 4), BW = LLC_BW * LLC_hit + L2_BW * L2_hit, with
+# the constants that reproduce every "Mem BW" entry of its Table 4 (section 5) by least
+# squares (the fit is re-derived in tests/test_oracle_schedule.py), in TB/s
+EQ1_L2_BW_TBS = 17.05
+EQ1_LLC_BW_TBS = 5.99
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0}   # MI355X dense MFMA peaks
 # HipKittens 8-wave 0P/8C bf16 GEMM at 8192^3 on MI355X (HipKittens L2 note, Table 2 / Q3)
 PAGES_BF16_8192_TFLOPS = 1610.0
@@ -95,6 +100,63 @@ def load_profile_facts(workload: str) -> dict:
     return facts
 
 
+def wait_event(ev, deadline_s: float, what: str) -> None:
+    """Poll a recorded event until the GPU passes it.  A GPU that has not passed
+    it after deadline_s seconds is reported as a hang (one JSON line with
+    "status": "HANG") and the process exits with status 3 at once, without
+    waiting for the GPU."""
+    t0 = time.perf_counter()
+    while not ev.query():
+        waited = time.perf_counter() - t0
+        if waited > deadline_s:
+            print(json.dumps({"status": "HANG", "where": what, "waited_s": round(waited, 1),
+                              "deadline_s": deadline_s}), flush=True)
+            os._exit(3)
+        time.sleep(0.0002)
+
+
+def gpu_identity() -> dict:
+    """Which box and GPU a line was measured on: host name, and the GPU's serial
+    number and power cap as amdsmi reports them (null where unavailable)."""
+    import socket
+    out = {"host": socket.gethostname(), "gpu_serial": None, "power_cap_w": None}
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+        out["gpu_serial"] = amdsmi.amdsmi_get_gpu_asic_info(h).get("asic_serial")
+        cap = amdsmi.amdsmi_get_power_cap_info(h).get("power_cap")
+        out["power_cap_w"] = round(cap / 1e6) if isinstance(cap, (int, float)) else None
+    except Exception as e:  # pragma: no cover - no amdsmi / no device
+        out["note"] = "amdsmi unavailable: %s" % e
+    return out
+
+
+def clock_from_trace(rec: np.ndarray, launches: int) -> dict:
+    """Clock and per-tile timing from the kernels' own time record (hkg_gemm_opts
+    trace: per workgroup the 100 MHz real-time and shader-clock counters at its
+    start, K-loop end and last store, and its XCD), over the timed launches.
+    rec: uint64 [launches, workgroups, 8]."""
+    rec = rec.reshape(launches, -1, 8).astype(np.int64)
+    rt0, rt1, rt2 = rec[..., 0], rec[..., 1], rec[..., 2]
+    mt0, mt1 = rec[..., 3], rec[..., 4]
+    xcd = rec[..., 6] & 0xF
+    ok = (rt1 > rt0) & (rt2 >= rt1)
+    mhz = np.where(ok, (mt1 - mt0) / np.maximum(rt1 - rt0, 1) * 100.0, np.nan)
+    per_xcd = [round(float(np.nanmean(mhz[xcd == x])), 1) if np.any(xcd == x) else None
+               for x in range(8)]
+    span = (rt2.max(axis=1) - rt0.min(axis=1)) / 100.0          # us per launch
+    return {"source": "per-workgroup shader-clock / 100 MHz real-time counters (s_memtime, "
+                      "s_memrealtime) written by the kernel on every timed launch",
+            "mhz_mean": round(float(np.nanmean(mhz)), 1),
+            "mhz_per_xcd": per_xcd,
+            "tile_us_mean": round(float(np.mean(rt2 - rt0)) / 100.0, 2),
+            "kloop_us_mean": round(float(np.mean(rt1 - rt0)) / 100.0, 2),
+            "epilogue_us_mean": round(float(np.mean(rt2 - rt1)) / 100.0, 2),
+            "launch_span_us_mean": round(float(span.mean()), 2),
+            "workgroups_per_launch": int(rec.shape[1])}
+
+
 def cpu_baseline(w: synth.Workload, A, B, sa, sb, target_s: float = 12.0) -> dict:
     """The oracle as it stands, timed on this host on a sample of whole output rows."""
     import oracle
@@ -119,6 +181,7 @@ def cpu_baseline(w: synth.Workload, A, B, sa, sb, target_s: float = 12.0) -> dic
     rows = int(min(w.M, max(probe_rows, round(target_s * rate / flops_per_row))))
     dt = run(rows)
     return {"value": rows * flops_per_row / dt / 1e12, "unit": "TFLOPS", "cores": threads,
+            "cores_in_affinity_mask": oracle.affinity_cores(),
             "kind": "oracle",
             "sample": "%d full output rows (x %d columns, K=%d) of %s, fp64, %.1f s wall"
                       % (rows, w.N, w.K, w.name, dt)}
@@ -136,7 +199,7 @@ def launch_plan(w: synth.Workload, opts) -> list:
 
 
 def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
-              with_cpu: bool) -> dict:
+              with_cpu: bool, deadline_s: float = 120.0) -> dict:
     import torch
     import dense_gemm_fp8_amd as hkg
 
@@ -158,24 +221,38 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
         pSA = hkg.mx_pack_scales(dSA, hkg.HKG_MX_OPERAND_A, stream=stream)
         pSB = hkg.mx_pack_scales(dSB, hkg.HKG_MX_OPERAND_B, stream=stream)
 
-    def step(e0=None, e1=None):
+    # the kernels' own time record on every timed launch (8 words per workgroup)
+    plan = launch_plan(w, opts)
+    wgs = sum(d["workgroups"] for d in plan)
+    trace = torch.zeros((steps, wgs, 8), dtype=torch.int64, device=dev)
+    base = opts if opts is not None else hkg.make_opts()
+
+    def traced(i):
+        return hkg.make_opts(remap=base.remap, W=base.W, C=base.C, schedule=base.schedule,
+                             trace=trace[i].data_ptr())
+
+    def step(e0=None, e1=None, o=None):
         """One pass of the path; e0/e1 bracket the GEMM kernel launch."""
         if w.dtype == "mxfp8":
             hkg.mx_pack_scales(dSA, hkg.HKG_MX_OPERAND_A, pSA, stream=stream)
             hkg.mx_pack_scales(dSB, hkg.HKG_MX_OPERAND_B, pSB, stream=stream)
         if e0 is not None:
             e0.record(stream)
+        o = opts if o is None else o
         if w.dtype == "bf16":
-            hkg.gemm_bf16(dA, dB, C, opts=opts, stream=stream)
+            hkg.gemm_bf16(dA, dB, C, opts=o, stream=stream)
         elif w.dtype == "mxfp8":
-            hkg.gemm_mxfp8(dA, dB, pSA, pSB, C, opts=opts, stream=stream)
+            hkg.gemm_mxfp8(dA, dB, pSA, pSB, C, opts=o, stream=stream)
         else:
-            hkg.gemm_fp8(dA, dB, sa, sb, C, opts=opts, stream=stream)
+            hkg.gemm_fp8(dA, dB, sa, sb, C, opts=o, stream=stream)
         if e1 is not None:
             e1.record(stream)
 
     for _ in range(warmup):
         step()
+    mark = torch.cuda.Event()
+    mark.record(stream)
+    wait_event(mark, deadline_s, "warm-up")
     torch.cuda.synchronize()
 
     # timed region: every GEMM launch bracketed by HIP events on the launch stream
@@ -183,14 +260,16 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
           for _ in range(steps)]
     outer0 = torch.cuda.Event(enable_timing=True)
     outer1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    topts = [traced(i) for i in range(steps)]
     t0 = time.perf_counter()
     outer0.record(stream)
-    for s, e in ev:
-        step(s, e)
+    for i, (s, e) in enumerate(ev):
+        step(s, e, topts[i])
     outer1.record(stream)
+    wait_event(outer1, deadline_s, "timed region")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock_info = clock_from_trace(trace.cpu().numpy(), steps)
     per_launch_ms = np.array([s.elapsed_time(e) for s, e in ev])
     region_ms = outer0.elapsed_time(outer1)
     ms_per_step = region_ms / steps
@@ -199,7 +278,6 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
     achieved = w.flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
 
-    plan = launch_plan(w, opts)
     # the committed counters were taken on the default launch of this workload
     facts = load_profile_facts(w.name) if opts is None else {}
     res = {
@@ -239,18 +317,44 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
             "kernel_ms_min": round(float(per_launch_ms.min()), 5),
             "kernel_ms_median": round(float(np.median(per_launch_ms)), 5),
         },
-        "cache": {"l2_hit_pct": facts.get("l2_hit_pct"), "llc_hit_pct": facts.get("llc_hit_pct"),
-                  "source": facts.get("source")},
+        "cache": cache_fields(facts),
+        "counters": counter_fields(facts),
+        "clock": clock_info,
         "wall_s_timed_region": round(wall, 4),
         "kernel_source_hash": kernel_source_hash(),
         "gpu": torch.cuda.get_device_name(dev),
+        "box": gpu_identity(),
     }
     del dA, dB, C
     if with_cpu:
         res["cpu_baseline"] = cpu_baseline(w, A, B, sa, sb)
+        res["vs_cpu_baseline"] = round(tflops / res["cpu_baseline"]["value"], 1)
     else:
         res["cpu_baseline"] = None
     return res
+
+
+def cache_fields(facts: dict) -> dict:
+    """L2 / LLC hit rates from the committed counter run of this kernel source,
+    and the L2 term of the pages' Eq. 1 that the measured L2 hit rate implies.
+    The LLC term needs an LLC hit rate, which this ROCm does not expose."""
+    l2 = facts.get("l2_hit_pct")
+    out = {"l2_hit_pct": l2, "llc_hit_pct": facts.get("llc_hit_pct"),
+           "llc_note": facts.get("llc_note"), "source": facts.get("source")}
+    out["eq1"] = {"l2_bw_tbs": EQ1_L2_BW_TBS, "llc_bw_tbs": EQ1_LLC_BW_TBS,
+                  "l2_term_tbs": None if l2 is None else round(EQ1_L2_BW_TBS * l2 / 100.0, 2),
+                  "llc_term_tbs": None}
+    return out
+
+
+def counter_fields(facts: dict) -> dict:
+    """MFMA busy and LDS bank conflicts from the committed counter run of this
+    kernel source (rocprofv3 --pmc in a separate process; null when the
+    kernel source has changed since)."""
+    keys = ("mfma_busy_pct", "lds_bank_conflict_cycles", "wait_any_pct", "counter_clock_ghz")
+    out = {k: facts.get(k) for k in keys}
+    out["source"] = facts.get("source")
+    return out
 
 
 def custom_workload(shape: str, dtype: str) -> synth.Workload:
@@ -416,6 +520,9 @@ def main(argv=None) -> int:
                                            "interleave192"],
                     default="interleave", help="in-CU schedule (default: the library's, interleave)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--deadline", type=float, default=120.0,
+                    help="seconds to wait for the GPU to finish the warm-up or the timed "
+                         "region before reporting a hang (exit status 3)")
     ap.add_argument("--shape", type=str, default=None, help="M,N,K (custom size)")
     ap.add_argument("--dtype", choices=["bf16", "fp8", "mxfp8"], default="bf16")
     ap.add_argument("--sweep", type=str, default=None, help='"W,C W,C ..." grid orders to time')
@@ -459,7 +566,7 @@ def main(argv=None) -> int:
         w = synth.workload(i) if not args.shape else custom_workload(args.shape, args.dtype)
         steps = args.steps
         res = bench_one(w, steps, args.warmup, opts, args.schedule,
-                        with_cpu=(not args.no_cpu_baseline))
+                        with_cpu=(not args.no_cpu_baseline), deadline_s=args.deadline)
         print(json.dumps(res), flush=True)
     return 0
 

@@ -60,6 +60,7 @@ EXPORTS = (
     "hkg_launch_plan",
     "hkg_remap_tile",
     "hkg_remap_tiles_device",
+    "hkg_probe_xcd",
     "hkg_status_string",
     "hkg_last_hip_error",
 )
@@ -67,7 +68,7 @@ EXPORTS = (
 
 class hkg_gemm_opts(ctypes.Structure):
     _fields_ = [("remap", ctypes.c_int32), ("W", ctypes.c_int32), ("C", ctypes.c_int32),
-                ("schedule", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32), ("trace", ctypes.c_void_p)]
 
 
 class hkg_launch_plan_t(ctypes.Structure):
@@ -121,6 +122,7 @@ def load() -> ctypes.CDLL:
                             ctypes.POINTER(hkg_launch_plan_t)],
         "hkg_remap_tile": [i64, i64, i32, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)],
         "hkg_remap_tiles_device": [i64, i64, i32, i32, p, p],
+        "hkg_probe_xcd": [i64, i32, i32, p, p],
         "hkg_status_string": [ctypes.c_int],
         "hkg_last_hip_error": [],
     }
@@ -199,6 +201,10 @@ def hkg_remap_tiles_device(Gm, Gn, W, C, out, stream) -> int:
     return load().hkg_remap_tiles_device(Gm, Gn, W, C, out, stream)
 
 
+def hkg_probe_xcd(workgroups, full_lds, spin_cycles, out, stream) -> int:
+    return load().hkg_probe_xcd(workgroups, full_lds, spin_cycles, out, stream)
+
+
 def hkg_status_string(status: int) -> str:
     return load().hkg_status_string(status).decode()
 
@@ -212,8 +218,13 @@ status_string = hkg_status_string
 
 # ---- torch marshalling helpers ------------------------------------------------------
 
-def make_opts(remap=HKG_REMAP_DEFAULT, W=0, C=0, schedule=HKG_SCHED_DEFAULT) -> hkg_gemm_opts:
-    return hkg_gemm_opts(remap, W, C, schedule)
+def make_opts(remap=HKG_REMAP_DEFAULT, W=0, C=0, schedule=HKG_SCHED_DEFAULT,
+              trace=None) -> hkg_gemm_opts:
+    """Options of the _ex entry points; trace: None or a device pointer (int) /
+    uint64 GPU tensor for the per-workgroup time record."""
+    if trace is not None and not isinstance(trace, int):
+        trace = _dev_ptr(trace, "trace")
+    return hkg_gemm_opts(remap, W, C, schedule, trace)
 
 
 def _stream_handle(stream) -> int:
@@ -337,4 +348,16 @@ def remap_tiles_device(Gm, Gn, W, C, stream=None):
     rc = hkg_remap_tiles_device(Gm, Gn, W, C, out.data_ptr(), _stream_handle(stream))
     if rc != HKG_OK:
         raise HkgError(rc, "hkg_remap_tiles_device")
+    return out
+
+
+def probe_xcd(workgroups, full_lds=True, spin_cycles=0, stream=None):
+    """Where each workgroup of a launch ran (hkg_probe_xcd) -> int32 GPU tensor
+    [workgroups, 2] of (XCC_ID register, HW_ID register)."""
+    import torch
+    out = torch.empty((workgroups, 2), dtype=torch.int32, device="cuda")
+    rc = hkg_probe_xcd(workgroups, int(bool(full_lds)), spin_cycles, out.data_ptr(),
+                       _stream_handle(stream))
+    if rc != HKG_OK:
+        raise HkgError(rc, "hkg_probe_xcd")
     return out

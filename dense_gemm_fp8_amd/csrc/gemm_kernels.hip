@@ -53,16 +53,20 @@
 // 4a + b -> tile column 8a + b + 4 (j & 1) + 32 (j >> 1)) so that blocks j = 0,1
 // give a lane 8 consecutive bf16 (one 16-byte store) and j = 2,3 another 8.
 //
-// Schedules (HipKittens L2 note, section 2 Pillar 2; sections 9.1 and 9.2):
+// Schedules (HipKittens L2 note, section 2 Pillar 2; the ping-pong in
+// sections 9.1 and 9.2, the 4-wave interleave in section 4 "% peak
+// derivation" and section 5, GEMM, Figure 6 right):
 //   kPingPong  8-wave ping-pong.  Group 0 (waves 0-3, one per SIMD) and group
 //              1 (waves 4-7) run one barrier apart: while one group issues its
 //              MFMA cluster at s_setprio 3 the other issues the next K steps'
 //              HBM->LDS loads and reads the first half of its own next
 //              cluster's fragments from LDS into registers, so a cluster
 //              starts with MFMAs instead of waiting for LDS.  Group 1 starts
-//              with a memory phase, which staggers it one phase behind group 0
-//              (the role of the "if (warpId < 4) barrier" of the listing
-//              description); s_barrier is the only synchronisation.
+//              with a memory phase, which staggers it one phase behind group 0:
+//              the conditional extra barrier wait that the pages' GEMM entry
+//              gives one wave group (HipKittens L2 note, section 7 code
+//              citation 1 and section 9.1) does the same there; s_barrier is
+//              the only synchronisation.
 //   kLockstep  all 8 waves compute the same K step and share the loads
 //              (no ping-pong; kept as an ablation).
 #include <hip/hip_runtime.h>
@@ -383,6 +387,38 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, int tm, int tn, 
     }
 }
 
+// Counters for callers that ask for a per-workgroup time record
+// (GemmParams::trace): the 100 MHz real-time counter and the shader-clock
+// counter.  Workgroup b writes 8 words at trace + 8 b from lane 0 of wave 0:
+// real time at entry, at the end of its K loop and after its last store was
+// issued; the shader clock at the same three points; the XCC_ID register;
+// (tile_m << 32) | tile_n.
+struct Stamp {
+    uint64_t rt, mt;
+};
+__device__ __forceinline__ Stamp stamp()
+{
+    return Stamp{__builtin_amdgcn_s_memrealtime(), __builtin_amdgcn_s_memtime()};
+}
+__device__ __forceinline__ void write_trace(const GemmParams &p, const Stamp &s0, const Stamp &s1,
+                                            int tm, int tn)
+{
+    if (!p.trace || threadIdx.x != 0)
+        return;
+    const Stamp s2 = stamp();
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    uint64_t *t = p.trace + 8 * (uint64_t)blockIdx.x;
+    t[0] = s0.rt;
+    t[1] = s1.rt;
+    t[2] = s2.rt;
+    t[3] = s0.mt;
+    t[4] = s1.mt;
+    t[5] = s2.mt;
+    t[6] = xcc;
+    t[7] = ((uint64_t)(uint32_t)tm << 32) | (uint32_t)tn;
+}
+
 template <int kDtype, int kSched>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
 {
@@ -393,6 +429,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
     const int g = wave >> 2;     // ping-pong group, also the 128-row half of the tile
     const int wn = wave & 3;     // 64-column quarter of the tile
     const int w4 = wave & 3;
+    const Stamp s0 = stamp();
 
     int tm, tn;
     remap_tile(blockIdx.x, p.Gm, p.Gn, p.W, p.Cc, tm, tn);
@@ -573,12 +610,16 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
             }
         }
     }
+    const Stamp s1 = stamp();
     store_tile<8, 4, kTile>(p, tm, tn, 128 * g, 64 * wn, lane, acc);
+    write_trace(p, s0, s1, tm, tn);
 }
 
 // ---- 4-wave interleave (one wave per SIMD) --------------------------------
-// HipKittens L2 note, section 9.1 / summary page "4-wave interleave": each
-// wave issues its own loads and LDS reads between its MFMAs.  Wave w owns the
+// HipKittens L2 note, section 2 (Q2, Pillar 2), section 4 ("% peak
+// derivation", FP8 line) and section 5 (GEMM, Figure 6 right), and the
+// summary page's "4-wave interleave": each wave issues its own loads and LDS
+// reads between its MFMAs.  Wave w owns the
 // 128 x 128 quarter (wm, wn) = (w >> 1, w & 1) of the tile: 8 x 8 blocks of
 // 16 x 16, i.e. 256 fp32 accumulators per lane, which fit next to the
 // fragments only because a single wave per SIMD has the whole register file.
@@ -596,7 +637,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
 // Each memory instruction is slotted after a given MFMA (sched_barrier after
 // every slot), so the matrix core is fed by one MFMA after another while the
 // loads and reads issue in its shadow.  The loop body is the same for every
-// t: loads of K steps >= nk are out of range and write zeros into panels no
+// t: the loads of K steps >= nk fetch bytes no MFMA uses -- in-range bytes of
+// the panel's next rows, or zeros past the panel's last row -- into panels no
 // one reads any more, and the reads of "step nk" in the last half are unused.
 // ---- 4-wave layout ----------------------------------------------------------
 // The A and B panels of the 4-wave kernel use one XOR swizzle each instead of
@@ -1204,6 +1246,7 @@ __global__ __launch_bounds__(256, kT == 128 ? 2 : 1) void gemm4_kernel(const Gem
     c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     c.a_rows = (kT / 2) * (c.wave >> 1) * kRowBytes;           // tile rows kT/2 (w >> 1) ..
     c.b_rows = kRing + (kT / 2) * (c.wave & 1) * kRowBytes;    // tile columns kT/2 (w & 1) ..
+    const Stamp s0 = stamp();
 
     int tm, tn;
     remap_tile(blockIdx.x, p.Gm, p.Gn, p.W, p.Cc, tm, tn);
@@ -1297,8 +1340,10 @@ __global__ __launch_bounds__(256, kT == 128 ? 2 : 1) void gemm4_kernel(const Gem
             quad_step<kDtype, kMasked, kB>(f, acc, sc, c, ldk, t, lane, rg, bs0);
         wait_vmcnt<0>();
     }
+    const Stamp s1 = stamp();
     store_tile<kB, kB, kT>(p, tm, tn, c.a_rows / kRowBytes, (c.b_rows - kRing) / kRowBytes, lane,
                            acc);
+    write_trace(p, s0, s1, tm, tn);
 }
 
 // MXFP8 scale packing: entry e (0..7) of lane l at K step t of 128-row group
@@ -1362,6 +1407,32 @@ __global__ void remap_tiles_kernel(int Gm, int Gn, int W, int C, int32_t *out)
     }
 }
 
+// Which XCD (accelerator complex die) and which compute unit each workgroup
+// of a launch runs on: out[2 b] = the XCC_ID hardware register (bits 3:0 the
+// die), out[2 b + 1] = the HW_ID register (wave slot, SIMD, CU, shader array
+// and engine ids).  kFull: the workgroup declares the whole 160 KiB of LDS,
+// as the 256 x 256 GEMM kernels do, so at most one runs per CU.  Workgroup b
+// first waits ((b * 37) % 64) * spin / 64 shader cycles (a bounded wait on the
+// cycle counter), so that workgroups finish out of order.
+template <bool kFull>
+__global__ __launch_bounds__(256) void xcd_probe_kernel(int spin, int32_t *out)
+{
+    __shared__ char lds[kFull ? kLdsBytes : 256];
+    lds[threadIdx.x] = (char)threadIdx.x;
+    __syncthreads();
+    if (threadIdx.x != 0)
+        return;
+    const uint64_t wait = (uint64_t)((blockIdx.x * 37u) % 64u) * (uint64_t)spin / 64u;
+    const uint64_t t0 = __builtin_readcyclecounter();
+    while (__builtin_readcyclecounter() - t0 < wait) {
+    }
+    uint32_t xcc, hw;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    out[2 * blockIdx.x] = (int32_t)xcc + (lds[1] - 1);    // lds[1] == 1: keeps the array live
+    out[2 * blockIdx.x + 1] = (int32_t)hw;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(Dtype dt, Schedule s, const GemmParams &p, hipStream_t stream)
@@ -1412,6 +1483,16 @@ hipError_t launch_mx_pack(int operand, int rows, int nblk, int nk, int groups,
     const dim3 grid((unsigned)groups, (unsigned)((nk + kPackSteps - 1) / kPackSteps));
     hipLaunchKernelGGL(mx_pack_kernel, grid, dim3(256), 0, stream, operand, rows, nblk, nk, src,
                        reinterpret_cast<uint64_t *>(dst));
+    return hipGetLastError();
+}
+
+hipError_t launch_xcd_probe(int workgroups, bool full_lds, int spin, int32_t *out,
+                            hipStream_t stream)
+{
+    if (full_lds)
+        hipLaunchKernelGGL(xcd_probe_kernel<true>, dim3(workgroups), dim3(256), 0, stream, spin, out);
+    else
+        hipLaunchKernelGGL(xcd_probe_kernel<false>, dim3(workgroups), dim3(256), 0, stream, spin, out);
     return hipGetLastError();
 }
 

@@ -5,6 +5,9 @@
 // nothing and leaves C untouched.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
+
+#include <atomic>
 
 #include "../../include/hkg.h"
 #include "kernels.h"
@@ -13,6 +16,50 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// Whether a device is a gfx950, cached per device ordinal (0 = not yet
+// asked, 1 = gfx950, -1 = another architecture).  The kernels are built for
+// gfx950 only.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_arch[kMaxDevices];
+
+// The device work on `stream` runs on (NULL: the calling thread's current
+// device) must be a gfx950.  Called after argument validation, right before
+// the first launch of a call; a device query, no launch.
+int check_device(void *stream)
+{
+    int dev = -1;
+    hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
+                          : hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0) {
+        g_last_hip_error = static_cast<int>(e);
+        return HKG_ERR_DEVICE;
+    }
+    int known = dev < kMaxDevices ? g_device_arch[dev].load(std::memory_order_relaxed) : 0;
+    if (known == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) {
+            g_last_hip_error = static_cast<int>(e);
+            return HKG_ERR_DEVICE;
+        }
+        known = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        if (dev < kMaxDevices)
+            g_device_arch[dev].store(known, std::memory_order_relaxed);
+    }
+    return known == 1 ? HKG_OK : HKG_ERR_DEVICE;
+}
+
+// Device check, then clear any error an earlier, unrelated HIP call left
+// pending, so that the hipGetLastError() read after a launch reports that
+// launch only.
+int prepare_launch(void *stream)
+{
+    const int rc = check_device(stream);
+    if (rc == HKG_OK)
+        (void)hipGetLastError();
+    return rc;
+}
 
 constexpr int64_t kTile = 256;
 constexpr int64_t kKStepBf16 = 64;     // K elements per step (one 128-byte LDS row)
@@ -320,6 +367,23 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
     rc = plan_gemm(dt, M, N, K, opts, &pl);
     if (rc != HKG_OK)
         return rc;
+    uint64_t *trace = opts ? opts->trace : nullptr;
+    if (trace) {
+        // 8 words per workgroup of every launch of the call
+        int64_t wgs = 0;
+        for (int i = 0; i < pl.launches; ++i)
+            wgs += pl.Gm[i] * pl.Gn[i];
+        const int64_t tb = 64 * wgs, ab = M * K * elem, bb = N * K * elem;
+        if ((reinterpret_cast<uintptr_t>(trace) & 7u) != 0)
+            return HKG_ERR_ALIGN;
+        if (overlaps(trace, tb, A, ab) || overlaps(trace, tb, B, bb) ||
+            overlaps(trace, tb, C, M * N * 2) || overlaps(trace, tb, C_f32, M * N * 4))
+            return HKG_ERR_OVERLAP;
+    }
+
+    rc = prepare_launch(stream);
+    if (rc != HKG_OK)
+        return rc;
 
     hkg::GemmParams p;
     p.B = B;
@@ -350,12 +414,15 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
         p.Gn = static_cast<int>(pl.Gn[i]);
         p.W = pl.W[i];
         p.Cc = pl.C[i];
+        p.trace = trace;
         const hipError_t e = hkg::launch_gemm(dt, pl.sched[i], p, static_cast<hipStream_t>(stream));
         if (e != hipSuccess) {
             g_last_hip_error = static_cast<int>(e);
             return HKG_ERR_LAUNCH;
         }
         row += pl.rows[i];
+        if (trace)
+            trace += 8 * pl.Gm[i] * pl.Gn[i];
     }
     return HKG_OK;
 }
@@ -434,6 +501,9 @@ int hkg_mx_pack_scales(int32_t operand, int64_t rows, int64_t K, const void *sca
         return HKG_ERR_SIZE;
     if (overlaps(packed, mx_packed_bytes(rows, K), scales, rows * (K / kKAlignMx)))
         return HKG_ERR_OVERLAP;
+    const int rc = prepare_launch(stream);
+    if (rc != HKG_OK)
+        return rc;
     hipError_t e = hkg::launch_mx_pack(
         operand, static_cast<int>(rows), static_cast<int>(K / kKAlignMx),
         static_cast<int>(ceil_div(K, kKStepFp8)), static_cast<int>(ceil_div(rows, kMxGroupRows)),
@@ -525,9 +595,34 @@ int hkg_remap_tiles_device(int64_t Gm, int64_t Gn, int32_t W, int32_t C, int32_t
         return HKG_ERR_ALIGN;
     int64_t w = W, c = C;
     clamp_remap(Gm, Gn, &w, &c);
+    const int rc = prepare_launch(stream);
+    if (rc != HKG_OK)
+        return rc;
     hipError_t e = hkg::launch_remap_tiles(static_cast<int>(Gm), static_cast<int>(Gn),
                                            static_cast<int>(w), static_cast<int>(c), out,
                                            static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        g_last_hip_error = static_cast<int>(e);
+        return HKG_ERR_LAUNCH;
+    }
+    return HKG_OK;
+}
+
+int hkg_probe_xcd(int64_t workgroups, int32_t full_lds, int32_t spin_cycles, int32_t *out,
+                  void *stream)
+{
+    if (!out)
+        return HKG_ERR_NULL;
+    if (workgroups < 1 || workgroups > (int64_t(1) << 24) || spin_cycles < 0 ||
+        spin_cycles > (1 << 24) || (full_lds != 0 && full_lds != 1))
+        return HKG_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(out) & 3u) != 0)
+        return HKG_ERR_ALIGN;
+    const int rc = prepare_launch(stream);
+    if (rc != HKG_OK)
+        return rc;
+    hipError_t e = hkg::launch_xcd_probe(static_cast<int>(workgroups), full_lds != 0, spin_cycles,
+                                         out, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         g_last_hip_error = static_cast<int>(e);
         return HKG_ERR_LAUNCH;
@@ -545,7 +640,7 @@ const char *hkg_status_string(int status)
     case HKG_ERR_ALIGN: return "pointer not 16-byte aligned";
     case HKG_ERR_SIZE: return "operand panel exceeds the 32-bit buffer range";
     case HKG_ERR_OPTS: return "invalid hkg_gemm_opts";
-    case HKG_ERR_DEVICE: return "device query failed";
+    case HKG_ERR_DEVICE: return "the stream's device is not a gfx950, or could not be queried";
     case HKG_ERR_LAUNCH: return "kernel launch failed";
     case HKG_ERR_OVERLAP: return "an output overlaps an input or the other output";
     default: return "unknown status";

@@ -22,6 +22,7 @@ struct GemmParams {
     const void *SB;     // MXFP8: packed E8M0 scales of B
     int sa_bytes;       // sizes of the packed scale buffers
     int sb_bytes;
+    uint64_t *trace;    // nullptr, or 8 words per workgroup of timestamps (hkg_gemm_opts::trace)
 };
 
 enum Dtype { kBf16 = 0, kFp8 = 1, kMx = 2 };
@@ -37,6 +38,9 @@ enum Schedule {
 
 hipError_t launch_gemm(Dtype dt, Schedule s, const GemmParams &p, hipStream_t stream);
 hipError_t launch_remap_tiles(int Gm, int Gn, int W, int C, int32_t *out, hipStream_t stream);
+// Diagnostic: the XCD and HW_ID of each of `workgroups` workgroups (out: 2 ints each).
+hipError_t launch_xcd_probe(int workgroups, bool full_lds, int spin, int32_t *out,
+                            hipStream_t stream);
 // MXFP8 scale packing: src [rows][nblk] E8M0 bytes -> dst, groups x nk x 64 lanes x 8 bytes.
 hipError_t launch_mx_pack(int operand, int rows, int nblk, int nk, int groups,
                           const uint8_t *src, uint8_t *dst, hipStream_t stream);

@@ -31,8 +31,13 @@
  *    nothing is launched and C is untouched (a launch failure of the second
  *    of two default launches can leave the rows of the first written).
  *  - Return value: HKG_OK (0) or a negative hkg_status.
+ *  - After validation and before its first launch, a call checks (once per
+ *    device, then from a cache) that the device of `stream` is a gfx950
+ *    (HKG_ERR_DEVICE otherwise) and clears any HIP error an earlier call left
+ *    pending, so HKG_ERR_LAUNCH always names this call's own launch.
  *  - The library holds no mutable state apart from a thread-local copy of the
- *    last HIP error; it is safe to call from several host threads.
+ *    last HIP error and that per-device architecture cache; it is safe to call
+ *    from several host threads.
  */
 #ifndef HKG_H
 #define HKG_H
@@ -51,7 +56,8 @@ typedef enum {
     HKG_ERR_ALIGN = -3,   /* a pointer is not 16-byte aligned                        */
     HKG_ERR_SIZE = -4,    /* a per-tile operand panel exceeds the 32-bit buffer range */
     HKG_ERR_OPTS = -5,    /* invalid hkg_gemm_opts                                   */
-    HKG_ERR_DEVICE = -6,  /* the current device is not gfx950 or cannot be queried   */
+    HKG_ERR_DEVICE = -6,  /* the device of `stream` (NULL: the current device) is not
+                             a gfx950, or could not be queried; nothing launched  */
     HKG_ERR_LAUNCH = -7,  /* a kernel launch failed; see hkg_last_hip_error().  When
                              the call was split into two launches (hkg_launch_plan),
                              the rows of the first may already be written         */
@@ -89,7 +95,8 @@ enum {
     HKG_SCHED_LOCKSTEP = 2, /* all 8 waves compute the same K step (ablation only)   */
     HKG_SCHED_INTERLEAVE = 3,/* 4 waves (one per SIMD), each 128 x 128 of the tile,
                                loads and LDS reads slotted between its own MFMAs
-                               (the note's section 9.1 4-wave interleave)            */
+                               (the note's 4-wave interleave: section 2 Pillar 2,
+                               section 5 GEMM, Figure 6 right)                       */
     HKG_SCHED_INTERLEAVE_128 = 4, /* the same schedule on 128 x 128 output tiles (each
                                wave 64 x 64; 80 KiB of LDS, two workgroups per CU):
                                four times the tiles, for grids too small to fill the
@@ -105,7 +112,23 @@ typedef struct {
     int32_t W;         /* window height in tile rows (HKG_REMAP_XCD)   */
     int32_t C;         /* consecutive tiles per XCD (HKG_REMAP_XCD)    */
     int32_t schedule;  /* HKG_SCHED_*                                  */
+    uint64_t *trace;   /* NULL, or a per-workgroup time record (below) */
 } hkg_gemm_opts;
+
+/*
+ * Time record (hkg_gemm_opts.trace): a device buffer, 8-byte aligned, of
+ * 8 uint64 per workgroup of the call (the sum of grid[i] over its launches,
+ * see hkg_launch_plan; launch i's workgroups follow those of launches < i).
+ * Workgroup b writes, from one lane, words 8b .. 8b+7:
+ *   0, 1, 2  the 100 MHz real-time counter at its start, at the end of its K
+ *            loop and after its last store was issued (one wave's view)
+ *   3, 4, 5  the shader-clock counter at the same three points, so that
+ *            (w4 - w3) / (w1 - w0) * 100 MHz is the clock the K loop ran at
+ *   6        the XCC_ID hardware register (bits 3:0: the XCD it ran on)
+ *   7        (tile_m << 32) | tile_n, the output tile it computed
+ * The buffer must not overlap A, B, C or C_f32 (HKG_ERR_OVERLAP).  Writing the
+ * record costs one 64-byte store per workgroup; the arithmetic is unchanged.
+ */
 
 /*
  * bf16 GEMM.
@@ -131,6 +154,15 @@ int hkg_gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
  *   C [M][N] bfloat16 = RNE(fp32(scale_a*scale_b) * fp32 accumulator)
  *   C_f32: NULL or the scaled fp32 value before rounding
  * Shapes: any M, N >= 0; K >= 0 with K % 16 == 0.  Otherwise as above.
+ * Accuracy: K is consumed in steps of 128 (a partial step first when K is not
+ * a multiple of 128).  The gfx950 e4m3 matrix instruction sums the 128
+ * products of a step with about 13 bits below the largest of them before
+ * adding the fp32 accumulator, so for any inputs
+ *   |C_f32 - exact| <= sa*sb * ( 2^-6 * sum_steps max_k |a_k b_k|
+ *                                + steps * 2^-24 * sum_k |a_k b_k| ),
+ * and sums whose products all lie within that window (e.g. small integers)
+ * are exact.  For per-tensor-quantised N(0,1) data the error is far smaller
+ * (8192^3: max 0.006 against 1e-3 * sqrt(K) = 0.09).
  */
 int hkg_gemm_fp8(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                  float scale_a, float scale_b, void *C, float *C_f32, void *stream);
@@ -213,7 +245,7 @@ int hkg_default_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *W
  * default split of a partial last round, see HKG_SCHED_DEFAULT).
  *   launches     0 (M == 0 or N == 0), 1 or 2
  *   schedule[i]  HKG_SCHED_* that launch i runs (never HKG_SCHED_DEFAULT)
- *   tile[i]      its output tile edge, 256 or 128
+ *   tile[i]      its output tile edge, 256, 192 or 128
  *   rows[i]      output rows it covers; launch 1 starts at row rows[0]
  *   grid[i]      its workgroups (tiles)
  *   W[i], C[i]   its grid order
@@ -250,6 +282,25 @@ int hkg_remap_tile(int64_t Gm, int64_t Gn, int32_t W, int32_t C, int64_t b,
  */
 int hkg_remap_tiles_device(int64_t Gm, int64_t Gn, int32_t W, int32_t C, int32_t *out,
                            void *stream);
+
+/*
+ * Diagnostic of the premise behind the grid remap: the remap (HipKittens L2
+ * note, section 2 Pillar 3 and section 7 code citation 5, Algorithm 1's
+ * "de-interleave round-robin" step) assumes that the hardware hands
+ * workgroup b of a launch to XCD b mod 8.  This launches `workgroups`
+ * workgroups of 256 threads; each records where it ran:
+ *   out[2*b]     the XCC_ID hardware register (bits 3:0: the XCD)
+ *   out[2*b + 1] the HW_ID hardware register (wave slot, SIMD, CU, shader
+ *                array and engine ids)
+ * full_lds = 1: each workgroup declares the whole 160 KiB of LDS, as the
+ * 256 x 256 GEMM kernels do (at most one per CU); 0: 256 bytes.  Workgroup b
+ * first waits ((b*37) % 64) * spin_cycles / 64 shader clock cycles (a bounded
+ * wait), so that workgroups finish out of order.
+ *   out: device int32[2*workgroups], caller-owned, 4-byte aligned.
+ * 1 <= workgroups <= 2^24 and 0 <= spin_cycles <= 2^24, else HKG_ERR_SHAPE.
+ */
+int hkg_probe_xcd(int64_t workgroups, int32_t full_lds, int32_t spin_cycles, int32_t *out,
+                  void *stream);
 
 /* Static description of a status code. */
 const char *hkg_status_string(int status);

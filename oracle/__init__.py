@@ -7,6 +7,8 @@ it, and it imports nothing from the GPU library.
 Contents
   liboracle.so (oracle.c)  plain fp64 CPU GEMM C = A * B^T for bf16 and OCP e4m3
                            inputs, exact decoders, one-step bf16 rounding
+  dense.py                 the same GEMM definition evaluated with exact fp64 decoding
+                           and the BLAS fp64 matrix product, for full-size grids
   remap.py                 the chiplet-aware grid remap, written from the pages
   eq1.py                   the L2/LLC bandwidth model and its fit to Table 4
 """
@@ -71,12 +73,23 @@ def _load():
     return _lib
 
 
-def default_threads() -> int:
+def affinity_cores() -> int:
+    """Host cores this process may run on."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        return os.cpu_count() or 1
+
+
+def default_threads() -> int:
+    """Worker threads: every core in the affinity mask, capped by OMP_NUM_THREADS
+    when the environment sets it (a host that shares its cores between GPUs
+    gives each GPU's processes that many)."""
+    n = affinity_cores()
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 def _ptr(a: np.ndarray) -> int:

@@ -22,7 +22,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = hkg.load()
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 15
     assert sorted(hkg.EXPORTS) == names
     for n in names:
         assert getattr(lib, n) is not None
@@ -321,3 +321,37 @@ def test_launch_plan_errors_match_entry_points():
     assert hkg.launch_plan(256, 256, 64, 2, bad)[0] == hkg.HKG_ERR_OPTS      # MXFP8
     assert hkg.launch_plan(0, 256, 64, 2, bad)[0] == hkg.HKG_ERR_OPTS
     assert hkg.launch_plan(256, 256, 64, 0, hkg.make_opts(schedule=9))[0] == hkg.HKG_ERR_OPTS
+
+
+def test_probe_xcd_rejects_bad_arguments():
+    assert hkg.hkg_probe_xcd(8, 1, 0, None, None) == hkg.HKG_ERR_NULL
+    assert hkg.hkg_probe_xcd(0, 1, 0, FAKE, None) == hkg.HKG_ERR_SHAPE
+    assert hkg.hkg_probe_xcd((1 << 24) + 1, 1, 0, FAKE, None) == hkg.HKG_ERR_SHAPE
+    assert hkg.hkg_probe_xcd(8, 2, 0, FAKE, None) == hkg.HKG_ERR_SHAPE
+    assert hkg.hkg_probe_xcd(8, 1, -1, FAKE, None) == hkg.HKG_ERR_SHAPE
+    assert hkg.hkg_probe_xcd(8, 0, 0, FAKE + 2, None) == hkg.HKG_ERR_ALIGN
+
+
+def test_valid_call_without_a_gfx950_is_a_device_error():
+    """A call that passes validation checks the stream's device before its
+    first launch; on a host without a gfx950 (this CPU-only run) every entry
+    point returns HKG_ERR_DEVICE and launches nothing."""
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    M, N, K = 256, 256, 64
+    assert hkg.hkg_gemm_bf16(M, N, K, FAKE, FB, FC, None, None) == hkg.HKG_ERR_DEVICE
+    assert hkg.hkg_gemm_fp8(M, N, 128, FAKE, FB, 1.0, 1.0, FC, None, None) == hkg.HKG_ERR_DEVICE
+    assert hkg.hkg_probe_xcd(8, 1, 0, FAKE, None) == hkg.HKG_ERR_DEVICE
+    assert hkg.hkg_remap_tiles_device(4, 4, 1, 1, FAKE, None) == hkg.HKG_ERR_DEVICE
+
+
+def test_trace_buffer_validated_before_launch():
+    M, N, K = 256, 256, 64
+    o = hkg.make_opts(trace=FC + (64 << 20) + 4)            # not 8-byte aligned
+    assert hkg.hkg_gemm_bf16_ex(M, N, K, FAKE, FB, FC, None, None, o) == hkg.HKG_ERR_ALIGN
+    o = hkg.make_opts(trace=FC + 64)                         # inside C
+    assert hkg.hkg_gemm_bf16_ex(M, N, K, FAKE, FB, FC, None, None, o) == hkg.HKG_ERR_OVERLAP
+    o = hkg.make_opts(trace=FAKE)                            # over A
+    assert hkg.hkg_gemm_fp8_ex(M, N, 128, FAKE, FB, 1.0, 1.0, FC, None, None, o) == hkg.HKG_ERR_OVERLAP
+    assert ctypes.sizeof(hkg.hkg_gemm_opts) == 24

@@ -2,7 +2,7 @@
 
 Exactness cases (small integers, all-ones, identity, zeros) are compared bit for
 bit; random N(0,1) cases use the (i)-(iii) acceptance of tests/_parity.py;
-full-size workloads are compared on sampled outputs that touch every tile.
+full-size workloads are compared entry by entry (default launch and ping-pong).
 Every launch goes through dense_gemm_fp8_amd's marshalling of the C entry
 points; nothing here falls back to a host computation."""
 import sys
@@ -81,6 +81,28 @@ def test_device_remap_matches_oracle(Gm, Gn, W, C):
     np.testing.assert_array_equal(got, want)
 
 
+@pytest.mark.parametrize("full_lds,spin", [(True, 0), (True, 20000), (False, 0)])
+def test_workgroup_b_runs_on_xcd_b_mod_8(full_lds, spin):
+    """The premise of the grid remap's de-interleave step: workgroup b of a
+    launch runs on XCD b mod 8 (HipKittens L2 note, section 7 code citation 5).
+    What the remap needs is that the workgroups of one residue b mod 8 share one
+    XCD and the 8 residues cover the 8 XCDs; the test also requires the plain
+    b mod 8 numbering that the library's comments state.  Checked for 16 rounds
+    of one workgroup per CU (the GEMM's LDS footprint), with workgroups that
+    finish out of order, and for small workgroups that pack several per CU."""
+    G = 4096
+    _say("xcd probe G=%d full_lds=%s spin=%d" % (G, full_lds, spin))
+    got = hkg.probe_xcd(G, full_lds, spin).cpu().numpy()
+    xcd = got[:, 0] & 0xF
+    b = np.arange(G)
+    per_residue = [set(xcd[b % 8 == r].tolist()) for r in range(8)]
+    _say("xcd of residues 0..7: %s; distinct HW_ID values: %d"
+         % ([sorted(x) for x in per_residue], len(set(got[:, 1].tolist()))))
+    assert all(len(x) == 1 for x in per_residue), per_residue
+    assert sorted(x.pop() for x in per_residue) == list(range(8))
+    np.testing.assert_array_equal(xcd, b % 8)
+
+
 # ---------------------------------------------------------------- exactness --------
 
 @pytest.mark.parametrize("sched", SCHEDULES, ids=SCHED_IDS)
@@ -153,6 +175,56 @@ def test_fp8_mixed_magnitudes_exact():
     B = np.full((N, K), 0x38, dtype=np.uint8)
     cb, cf = run_fp8(A, B, 1.0, 1.0)
     np.testing.assert_array_equal(cf.astype(np.float64), oracle.gemm_fp8(A, B, 1.0, 1.0))
+
+
+def _fp8_window_bound(A, B, sa, sb):
+    """Error bound of the e4m3 path for inputs of any dynamic range.  One
+    16x16x128 e4m3 MFMA sums the 128 products of a K step with about 13 bits
+    below the largest of them (the accumulator is added afterwards, in fp32),
+    so a step's sum is off by at most 128 * 2^-13 = 2^-6 of its largest product
+    magnitude; the K/128 fp32 accumulations add at most 2^-24 of the running
+    magnitude each.  (K a multiple of 128, so the steps are k = 128 t ...)"""
+    from oracle import dense
+    a, b = dense.decode_e4m3(A), dense.decode_e4m3(B)
+    K = a.shape[1]
+    steps = K // 128
+    step_max = np.zeros((a.shape[0], b.shape[0]))
+    for t in range(steps):
+        sl = slice(128 * t, 128 * (t + 1))
+        step_max += np.abs(a[:, None, sl] * b[None, :, sl]).max(axis=2)
+    mag = np.abs(a) @ np.abs(b).T
+    return (2.0 ** -6 * step_max + steps * 2.0 ** -24 * mag) * (float(sa) * float(sb))
+
+
+@pytest.mark.parametrize("case", ["all_codes", "scaled_normals", "row_magnitudes"])
+def test_fp8_wide_dynamic_range_within_stated_bound(case):
+    """Per-tensor e4m3 inputs whose products span many binades in one K step:
+    the GPU's fp32 result stays within the bound stated for hkg_gemm_fp8 in
+    include/hkg.h (see _fp8_window_bound).  all_codes: every non-NaN code,
+    uniformly, scale 1; scaled_normals: N(0,1) times 2^U(-8..8) per element,
+    quantised per tensor; row_magnitudes: rows scaled by 2^-8 .. 2^7."""
+    _say("fp8 wide range %s" % case)
+    M, N, K = 256, 256, 1024
+    g = np.random.Generator(np.random.PCG64(9520))
+    if case == "all_codes":
+        codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+        A = codes[g.integers(0, codes.size, (M, K))]
+        B = codes[g.integers(0, codes.size, (N, K))]
+        sa = sb = np.float32(1.0)
+    elif case == "scaled_normals":
+        x = synth.normal_f32(9521, M, K) * np.exp2(g.integers(-8, 9, (M, K))).astype(np.float32)
+        y = synth.normal_f32(9522, N, K) * np.exp2(g.integers(-8, 9, (N, K))).astype(np.float32)
+        (A, sa), (B, sb) = synth.e4m3_quantize(x), synth.e4m3_quantize(y)
+    else:
+        x = synth.normal_f32(9523, M, K) * np.exp2(np.arange(M) % 16 - 8)[:, None].astype(np.float32)
+        (A, sa), (B, sb) = synth.e4m3_quantize(x), synth.e4m3_quantize(synth.normal_f32(9524, N, K))
+    cb, cf = run_fp8(A, B, sa, sb)
+    ref = oracle.gemm_fp8(A, B, sa, sb)
+    err = np.abs(cf.astype(np.float64) - ref)
+    bound = _fp8_window_bound(A, B, sa, sb)
+    _say("fp8 wide range %s: max err %.4g, max err/bound %.4g" % (case, err.max(), (err / bound).max()))
+    assert np.all(err <= bound)
+    np.testing.assert_array_equal(cb, synth.f32_to_bf16_bits(cf))
 
 
 @pytest.mark.parametrize("K", [64, 4096])
@@ -381,14 +453,13 @@ def test_random_shapes_default_launch_exact():
 
 # ---------------------------------------------------------------- full sizes -------
 
-@pytest.mark.parametrize("idx", [2, 3, 4, 5])
-def test_full_size_workload_sampled_parity(idx):
-    """Every full-size workload, sampled outputs (one per tile + uniform extras),
-    in the launch configuration the bench times (default opts) and with the
-    fp32 copy; the two bf16 outputs must be identical."""
-    w = synth.workload(idx)
-    _say("full-size %s: inputs" % w.name)
-    A, B, sa, sb = synth.make_inputs(w)
+FULL_SCHEDULES = [("default", None), ("pingpong", hkg.HKG_SCHED_PINGPONG)]
+
+
+def _full_size_outputs(w, A, B, sa, sb, opts):
+    """One workload through one schedule: the bench's launch (no fp32 copy) and
+    the validation launch (with it); returns host (C bits, C_f32) after
+    checking that the two launches agree and (ii) on every entry, on the device."""
     if w.dtype == "bf16":
         dA, dB = _dev_bf16(A), _dev_bf16(B)
     else:
@@ -396,29 +467,54 @@ def test_full_size_workload_sampled_parity(idx):
     C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
     C2 = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
     Cf = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
-    _say("full-size %s: launch" % w.name)
     if w.dtype == "bf16":
-        hkg.gemm_bf16(dA, dB, C)                 # bench configuration
-        hkg.gemm_bf16(dA, dB, C2, Cf)            # validation launch
+        hkg.gemm_bf16(dA, dB, C, opts=opts)            # bench configuration
+        hkg.gemm_bf16(dA, dB, C2, Cf, opts=opts)       # validation launch
     else:
-        hkg.gemm_fp8(dA, dB, sa, sb, C)
-        hkg.gemm_fp8(dA, dB, sa, sb, C2, Cf)
+        hkg.gemm_fp8(dA, dB, sa, sb, C, opts=opts)
+        hkg.gemm_fp8(dA, dB, sa, sb, C2, Cf, opts=opts)
     torch.cuda.synchronize()
     assert torch.equal(C.view(torch.int16), C2.view(torch.int16))
     # (ii) on every entry, on the device: torch's float->bfloat16 cast is RNE
     assert torch.equal(Cf.to(torch.bfloat16).view(torch.int16), C.view(torch.int16))
-    pm, pn = synth.sample_pairs(7000 + idx, w.M, w.N, 60000)
-    ipm, ipn = torch.from_numpy(pm).cuda(), torch.from_numpy(pn).cuda()
-    cf = Cf[ipm, ipn].cpu().numpy()
-    cb = C.view(torch.int16)[ipm, ipn].cpu().numpy().view(np.uint16)
+    out = (_host_bits(C), Cf.cpu().numpy())
     del dA, dB, C, C2, Cf
-    _say("full-size %s: oracle on %d samples" % (w.name, pm.size))
-    if w.dtype == "bf16":
-        ref = oracle.gemm_bf16_pairs(A, B, pm, pn)
-    else:
-        ref = oracle.gemm_fp8_pairs(A, B, sa, sb, pm, pn)
-    info = check(ref, cf, cb, w.K, w.name)
-    _say("full-size %s: %s" % (w.name, info))
+    torch.cuda.empty_cache()
+    return out
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_full_size_workload_every_entry(idx):
+    """Every full-size workload, EVERY output entry, against the oracle: the
+    default launch (the one the bench times) and the 8-wave ping-pong.  The
+    oracle is the fp64 full-grid route (exact decoding, BLAS fp64 product),
+    evaluated in row blocks; (i)-(iii) of tests/_parity.py apply to each entry.
+    The two schedules sum every 16 x 16 block's K steps in the same order, so
+    their outputs must also agree bit for bit."""
+    from oracle import dense
+    w = synth.workload(idx)
+    _say("full-size %s: inputs" % w.name)
+    A, B, sa, sb = synth.make_inputs(w)
+    outs = {}
+    for name, sched in FULL_SCHEDULES:
+        _say("full-size %s: launch %s" % (w.name, name))
+        outs[name] = _full_size_outputs(w, A, B, sa, sb,
+                                        None if sched is None else hkg.make_opts(schedule=sched))
+    np.testing.assert_array_equal(outs["pingpong"][1].view(np.uint32), outs["default"][1].view(np.uint32))
+    np.testing.assert_array_equal(outs["pingpong"][0], outs["default"][0])
+    ref = dense.DenseReference(w.dtype, A, B, 1.0 if sa is None else sa, 1.0 if sb is None else sb)
+    worst = {name: {"max_abs_err": 0.0, "literal_1ulp_violations": 0, "checked": 0} for name in outs}
+    for r0, r1 in ref.row_blocks():
+        block = ref.rows(r0, r1)
+        for name, (cb, cf) in outs.items():
+            info = check(block, cf[r0:r1], cb[r0:r1], w.K, "%s %s rows %d..%d" % (w.name, name, r0, r1))
+            acc = worst[name]
+            acc["max_abs_err"] = max(acc["max_abs_err"], info["max_abs_err"])
+            acc["literal_1ulp_violations"] += info["literal_1ulp_violations"]
+            acc["checked"] += info["checked"]
+    for name, acc in worst.items():
+        assert acc["checked"] == w.M * w.N
+        _say("full-size %s %s: every entry within tol %.4g: %s" % (w.name, name, w.tol, acc))
 
 
 # ---------------------------------------------------------------- ragged shapes ----
@@ -620,6 +716,48 @@ def test_split_default_launch_small_integers_exact():
     want = bf16_to_f64(A) @ bf16_to_f64(B).T          # small integers: exact in fp64
     np.testing.assert_array_equal(cf.astype(np.float64), want)
     np.testing.assert_array_equal(cb, oracle.bf16_round(want))
+
+
+# ------------------------------------------------------------- time record ---------
+
+@pytest.mark.parametrize("dtype,M,N,K", [("bf16", 4352, 4352, 256), ("fp8", 2048, 1536, 512)])
+def test_time_record(dtype, M, N, K):
+    """hkg_gemm_opts.trace: every workgroup of every launch of a call writes its
+    record (counters ordered, a plausible clock, its XCD, the tile the remap
+    gave it, so the tiles of each launch cover its grid once), and the output is
+    bit-identical to the call without a record."""
+    from oracle import remap
+    rc, plan = hkg.launch_plan(M, N, K, 0 if dtype == "bf16" else 1)
+    wgs = sum(d["grid"] for d in plan)
+    _say("time record %s %dx%dx%d, %d launch(es), %d workgroups" % (dtype, M, N, K, len(plan), wgs))
+    rec = torch.zeros((wgs, 8), dtype=torch.int64, device="cuda")
+    if dtype == "bf16":
+        A = synth.f32_to_bf16_bits(synth.normal_f32(9930, M, K))
+        B = synth.f32_to_bf16_bits(synth.normal_f32(9931, N, K))
+        plain, _ = run_bf16(A, B, want_f32=False)
+        traced, _ = run_bf16(A, B, opts=hkg.make_opts(trace=rec), want_f32=False)
+    else:
+        (A, sa), (B, sb) = (synth.e4m3_quantize(synth.normal_f32(9932, M, K)),
+                            synth.e4m3_quantize(synth.normal_f32(9933, N, K)))
+        plain, _ = run_fp8(A, B, sa, sb, want_f32=False)
+        traced, _ = run_fp8(A, B, sa, sb, opts=hkg.make_opts(trace=rec), want_f32=False)
+    np.testing.assert_array_equal(traced, plain)
+    r = rec.cpu().numpy()
+    assert np.all(r[:, 0] > 0) and np.all(r[:, 1] >= r[:, 0]) and np.all(r[:, 2] >= r[:, 1])
+    assert np.all(r[:, 4] >= r[:, 3]) and np.all(r[:, 5] >= r[:, 4])
+    loop = r[:, 1] - r[:, 0]
+    mhz = (r[:, 4] - r[:, 3])[loop > 50] / loop[loop > 50] * 100.0
+    _say("time record: clock %.0f..%.0f MHz, XCDs %s" % (mhz.min(), mhz.max(), sorted(set((r[:, 6] & 0xF).tolist()))))
+    assert mhz.size > 0 and np.all((mhz > 50) & (mhz < 3000))
+    np.testing.assert_array_equal(r[:, 6] & 0xF, np.concatenate([np.arange(d["grid"]) % 8 for d in plan]))
+    start = 0
+    for d in plan:
+        t = d["tile"]
+        Gm, Gn = -(-d["rows"] // t), -(-N // t)
+        tiles = r[start:start + d["grid"], 7]
+        got = np.stack([tiles >> 32, tiles & 0xFFFFFFFF], axis=1)
+        np.testing.assert_array_equal(got, np.array(remap.remap_table(Gm, Gn, d["W"], d["C"])))
+        start += d["grid"]
 
 
 # ---------------------------------------------------------- graphs and streams ------
