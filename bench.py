@@ -48,7 +48,8 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0}   # MI355X dense 
 # HipKittens 8-wave 0P/8C bf16 GEMM at 8192^3 on MI355X (HipKittens L2 note, Table 2 / Q3)
 PAGES_BF16_8192_TFLOPS = 1610.0
 KERNEL_SOURCES = ("dense_gemm_fp8_amd/csrc/gemm_kernels.hip", "dense_gemm_fp8_amd/csrc/remap.h",
-                  "dense_gemm_fp8_amd/csrc/kernels.h", "dense_gemm_fp8_amd/csrc/hkg_api.cpp")
+                  "dense_gemm_fp8_amd/csrc/kernels.h", "dense_gemm_fp8_amd/csrc/hkg_api.cpp",
+                  "dense_gemm_fp8_amd/csrc/remap_model.h", "dense_gemm_fp8_amd/csrc/remap_model.cpp")
 
 
 def _strip_comments(text: str) -> str:

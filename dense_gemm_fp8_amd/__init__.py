@@ -58,6 +58,7 @@ EXPORTS = (
     "hkg_mx_pack_scales",
     "hkg_default_remap",
     "hkg_launch_plan",
+    "hkg_remap_model",
     "hkg_remap_tile",
     "hkg_remap_tiles_device",
     "hkg_probe_xcd",
@@ -120,6 +121,8 @@ def load() -> ctypes.CDLL:
         "hkg_default_remap": [i64, i64, i64, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)],
         "hkg_launch_plan": [i64, i64, i64, i32, ctypes.POINTER(hkg_gemm_opts),
                             ctypes.POINTER(hkg_launch_plan_t)],
+        "hkg_remap_model": [i64, i64, i32, i32, i64, i32, ctypes.POINTER(ctypes.c_double),
+                            ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
         "hkg_remap_tile": [i64, i64, i32, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)],
         "hkg_remap_tiles_device": [i64, i64, i32, i32, p, p],
         "hkg_probe_xcd": [i64, i32, i32, p, p],
@@ -188,6 +191,14 @@ def launch_plan(M, N, K, dtype, opts=None):
     out = [dict(schedule=pl.schedule[i], tile=pl.tile[i], rows=pl.rows[i], grid=pl.grid[i],
                 W=pl.W[i], C=pl.C[i]) for i in range(pl.launches)] if rc == HKG_OK else []
     return rc, out
+
+
+def hkg_remap_model(Gm, Gn, W, C, panel_bytes, per_xcd=32):
+    """-> (status, l2_hit, llc_hit, eq1_bw_tbs) of the library's cache model."""
+    l2, llc, bw = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    rc = load().hkg_remap_model(Gm, Gn, W, C, panel_bytes, per_xcd, ctypes.byref(l2),
+                                ctypes.byref(llc), ctypes.byref(bw))
+    return rc, l2.value, llc.value, bw.value
 
 
 def hkg_remap_tile(Gm, Gn, W, C, b):

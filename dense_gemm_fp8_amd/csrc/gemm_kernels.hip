@@ -99,16 +99,36 @@ constexpr int kLdsBytes = (kAPanels + kBPanels) * kPanelBytes;   // 160 KiB
 constexpr int kDmaBytes = 64 * 16;                // one wave-wide 16 B/lane load
 constexpr int kDmaRows = kDmaBytes / kRowBytes;   // = 8 rows per load
 
-// Slot permutation of LDS row r (uses bits 0..4 of r).  A 16-lane group of a
-// ds_read_b128 reads one chunk from 16 rows; for conflict-free banking those
-// 16 reads must hit 16 different 16-byte slots of a 256-byte bank line
-// (64 banks x 4 B).  Two rows share a bank line (row bit 0), so for each
-// parity the 8 rows must get 8 different XOR values.  The A fragment reads
-// rows 16i + 0..15 (bits 1,2,3 vary), the interleaved B fragment reads rows
-// with bits 0,1,3,4 varying; (b1, b3, b2 ^ b4) is a bijection in both cases.
-__device__ __forceinline__ int slot_xor(int r)
+// Slot permutations of LDS row r, one per operand.  A 16-lane group of a
+// ds_read_b128 reads one 16-byte chunk from 16 rows; for conflict-free
+// banking those 16 reads must hit 16 different 16-byte slots of a 256-byte
+// bank line (64 banks x 4 B).  Two rows share a bank line (row bit 0), so for
+// each row parity the 8 rows of a group must get 8 different XOR values.  The
+// A fragment reads vary row bits 1,2,3 within a 16-lane group and B's
+// interleaved reads bits 1,3,4, so
+//   A: slot = chunk ^ (b1 | b3 << 1 | b2 << 2)   (independent of row bit 4)
+//   B: slot = chunk ^ (b1 | b3 << 1 | b4 << 2)   (independent of row bit 2)
+// are bank-conflict free, and the two row parities of a fragment pair (A
+// rows 16 apart, B rows 4 apart) lie a constant 2048 / 512 bytes apart, so
+// one lane base per operand and chunk half serves every block.
+__device__ __forceinline__ int slot_xor_a(int r)
 {
-    return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | ((((r >> 2) ^ (r >> 4)) & 1) << 2);
+    return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2);
+}
+__device__ __forceinline__ int slot_xor_b(int r)
+{
+    return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 4) & 1) << 2);
+}
+
+// An empty asm that claims to change x.  Applied to the lane base address of
+// a half, it stops the optimiser from folding a panel's offset into a
+// separate precomputed address per fragment read (one register each, and one
+// vector add each per K step): every read stays one ds_read of
+// (base + constant block offset).
+__device__ __forceinline__ int opaque(int x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
 }
 
 template <int N>
@@ -199,6 +219,28 @@ struct Frag<kFp8> {
     }
 };
 
+// Lane part of a fragment read, chunk half h (chunk 4 h + q): A row x, B row
+// (x & 3) + 8 (x >> 2) of a block pair, x = lane % 16, q = lane / 16.  For
+// bf16 the halves are the two DOT_SLICEs.  For e4m3 this is the 16x16x128
+// MFMA's own k order (lane group q supplies k 16q..16q+15 and 64 + 16q..+15,
+// probed on gfx950); the block-scaled form applies the scale in lane group b
+// to the 32 k of block b, so the MXFP8 scales follow the same order.
+struct QuadLane {
+    int a[2], b[2];
+};
+__device__ __forceinline__ QuadLane quad_lane(int lane)
+{
+    const int x = lane & 15, q = lane >> 4;
+    const int rb = (x & 3) + 8 * (x >> 2);
+    QuadLane l;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        l.a[h] = x * kRowBytes + (((4 * h + q) ^ slot_xor_a(x)) << 4);
+        l.b[h] = rb * kRowBytes + (((4 * h + q) ^ slot_xor_b(rb)) << 4);
+    }
+    return l;
+}
+
 // Per-lane LDS byte offsets of the fragment reads (relative to a 32-row
 // group).  [parity][h]: h selects chunk q (h = 0) or chunk 4 + q (h = 1),
 // i.e. the two DOT_SLICEs of bf16 or the two halves of an e4m3 fragment.
@@ -218,23 +260,15 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int lane)
         const int rb = (x & 3) + 4 * p + 8 * (x >> 2);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            o.a[p][h] = ra * kRowBytes + (((4 * h + q) ^ slot_xor(ra)) << 4);
-            o.b[p][h] = rb * kRowBytes + (((4 * h + q) ^ slot_xor(rb)) << 4);
+            o.a[p][h] = ra * kRowBytes + (((4 * h + q) ^ slot_xor_a(ra)) << 4);
+            o.b[p][h] = rb * kRowBytes + (((4 * h + q) ^ slot_xor_b(rb)) << 4);
         }
     }
     return o;
 }
 
-// Base addresses of a wave's fragments inside an A panel / B panel.
-__device__ __forceinline__ const char *a_frag_base(const char *a_panel, int g)
-{
-    return a_panel + (128 * g) * kRowBytes;
-}
-__device__ __forceinline__ const char *b_frag_base(const char *b_panel, int wn)
-{
-    return b_panel + (64 * wn) * kRowBytes;
-}
-// Offsets of fragment i of A (16-row block) and j of B (32-row half) from those bases.
+// Offsets of fragment i of A (16-row block) and j of B (32-row half) from a
+// wave's first row in a panel (lockstep schedule).
 __device__ __forceinline__ constexpr int a_blk(int i) { return 16 * (i & ~1) * kRowBytes; }
 __device__ __forceinline__ constexpr int b_blk(int j) { return 32 * (j >> 1) * kRowBytes; }
 
@@ -263,11 +297,18 @@ __device__ __forceinline__ void compute_kstep(const char *a_base, const char *b_
 }
 
 // Fragments of one K step for the ping-pong.  A wave reads all of them
-// (24 ds_read_b128, 96 VGPRs per lane) during its memory phase, while its
-// partner runs MFMAs, so the MFMA cluster itself contains no LDS instruction
-// and issues back to back.
-//   bf16: 2 DOT_SLICEs x (8 A + 4 B) fragments of 8 bf16
-//   e4m3: 8 A + 4 B fragments of 32 e4m3 (two 16-byte chunks each)
+// (24 ds_read_b128, 96 VGPRs per lane) in its memory phase, after issuing its
+// loads, while its partner runs MFMAs, so the MFMA cluster itself contains no LDS
+// instruction and issues back to back.  Every read is one ds_read_b128 of a
+// lane base plus an immediate block offset (the per-operand swizzles make
+// one base per operand and chunk half serve every block):
+//   bf16: 2 DOT_SLICEs x (8 A + 4 B) fragments of 8 bf16, slice s from base [s]
+//   e4m3: 8 A + 4 B fragments of 32 e4m3, chunk halves from bases [0], [1]
+// A fragment i: tile rows 16 i + x; B fragment j: rows 32 (j >> 1) + 4 (j & 1)
+// + (x & 3) + 8 (x >> 2) of the wave's 64 (the epilogue's column interleave).
+__device__ __forceinline__ constexpr int qa_blk(int i) { return 16 * i * kRowBytes; }
+__device__ __forceinline__ constexpr int qb_blk(int j) { return (32 * (j >> 1) + 4 * (j & 1)) * kRowBytes; }
+
 template <int kDtype>
 struct Pipe;
 
@@ -277,17 +318,17 @@ struct Pipe<kBf16> {
     struct Frags {
         bf16x8 a[2][8], b[2][4];
     };
-    __device__ __forceinline__ static void read(Frags &f, const char *a_base, const char *b_base,
-                                                const LaneOffsets &o)
+    __device__ __forceinline__ static void read(Frags &f, const char *smem, const int (&ba)[2],
+                                                const int (&bb)[2])
     {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                f.b[s][j] = F::load(b_base + b_blk(j), o.b[j & 1][0], o.b[j & 1][1], s);
+                f.b[s][j] = *reinterpret_cast<const bf16x8 *>(smem + qb_blk(j) + bb[s]);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                f.a[s][i] = F::load(a_base + a_blk(i), o.a[i & 1][0], o.a[i & 1][1], s);
+                f.a[s][i] = *reinterpret_cast<const bf16x8 *>(smem + qa_blk(i) + ba[s]);
         }
     }
     __device__ __forceinline__ static void cluster(const Frags &f, f32x4 (&acc)[8][4])
@@ -308,15 +349,21 @@ struct Pipe<kFp8> {
     struct Frags {
         i32x8 a[8], b[4];
     };
-    __device__ __forceinline__ static void read(Frags &f, const char *a_base, const char *b_base,
-                                                const LaneOffsets &o)
+    __device__ __forceinline__ static i32x8 frag(const char *smem, int blk, int base0, int base1)
+    {
+        const i32x4 lo = *reinterpret_cast<const i32x4 *>(smem + blk + base0);
+        const i32x4 hi = *reinterpret_cast<const i32x4 *>(smem + blk + base1);
+        return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    __device__ __forceinline__ static void read(Frags &f, const char *smem, const int (&ba)[2],
+                                                const int (&bb)[2])
     {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            f.b[j] = F::load(b_base + b_blk(j), o.b[j & 1][0], o.b[j & 1][1], 0);
+            f.b[j] = frag(smem, qb_blk(j), bb[0], bb[1]);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            f.a[i] = F::load(a_base + a_blk(i), o.a[i & 1][0], o.a[i & 1][1], 0);
+            f.a[i] = frag(smem, qa_blk(i), ba[0], ba[1]);
     }
     __device__ __forceinline__ static void cluster(const Frags &f, f32x4 (&acc)[8][4])
     {
@@ -342,7 +389,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 // only rows < M and columns < N (element by element when N % 8 != 0).
 // kRB x kCB blocks of 16 x 16 of a kT x kT output tile (tile (tm, tn)), the
 // wave's part starting at (row_off, col_off) inside it.
-template <int kRB, int kCB, int kT>
+// The fp32 values of output blocks (i, 2h) and (i, 2h + 1), scaled by p.scale
+// if kScale (per-tensor e4m3; bf16 and MXFP8 have scale 1 and skip the
+// multiply).  kAgpr: the accumulators live in AGPRs; an empty asm keeps each
+// pair there until this point, so the epilogue copies 8 values at a time
+// into VGPRs instead of all of them at once (which spills).
+template <bool kScale, bool kAgpr, int kRB, int kCB>
+__device__ __forceinline__ void block_pair(f32x4 (&acc)[kRB][kCB], int i, int h, float sc,
+                                           f32x4 &lo, f32x4 &hi)
+{
+    if (kAgpr)
+        asm volatile("" : "+a"(acc[i][2 * h]), "+a"(acc[i][2 * h + 1]));
+    lo = kScale ? acc[i][2 * h] * sc : acc[i][2 * h];
+    hi = kScale ? acc[i][2 * h + 1] * sc : acc[i][2 * h + 1];
+}
+// The same for a whole 16-row block i (kCB of 6 or 8 blocks): one pin for
+// the row, so that its conversions and stores can overlap.
+template <int kRB, int kCB>
+__device__ __forceinline__ void pin_row(f32x4 (&acc)[kRB][kCB], int i)
+{
+    static_assert(kCB == 6 || kCB == 8, "row pin for the AGPR tiles");
+    if constexpr (kCB == 8)
+        asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]),
+                          "+a"(acc[i][4]), "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+    else
+        asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]),
+                          "+a"(acc[i][4]), "+a"(acc[i][5]));
+}
+
+template <int kRB, int kCB, int kT, bool kScale, bool kAgpr>
 __device__ __forceinline__ void store_tile(const GemmParams &p, int tm, int tn, int row_off,
                                            int col_off, int lane, f32x4 (&acc)[kRB][kCB])
 {
@@ -353,6 +428,32 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, int tm, int tn, 
     uint16_t *C = static_cast<uint16_t *>(p.C);
     const bool vec = (p.N & 7) == 0;
     const bool inside = (tm + 1) * kT <= p.M && (tn + 1) * kT <= p.N && vec;
+    // Whole tiles without the fp32 copy (every timed launch): one buffer
+    // resource over the wave's 16 kRB rows of C, a lane offset fixed for the
+    // whole epilogue, a scalar offset per 16-row block and the 32-column group
+    // in the instruction's immediate offset -- no per-store address
+    // arithmetic and no branches.  The resource's 32-bit range bounds N.
+    if (inside && !p.C_f32 && (uint64_t)32 * kRB * (uint64_t)p.N < (uint64_t(1) << 32)) {
+        const int64_t origin = ((int64_t)tm * kT + row_off) * p.N + (int64_t)tn * kT + col_off;
+        const __amdgpu_buffer_rsrc_t rc =
+            make_rsrc(C + origin, (uint32_t)(32 * kRB) * (uint32_t)p.N);
+        const int voff = ((lane & 15) * p.N + 8 * q) * 2;
+#pragma unroll
+        for (int i = 0; i < kRB; ++i) {
+            const int soff = __builtin_amdgcn_readfirstlane((int)((uint32_t)(32 * i) * (uint32_t)p.N));
+            if constexpr (kAgpr)
+                pin_row(acc, i);
+#pragma unroll
+            for (int h = 0; h < kCB / 2; ++h) {
+                f32x4 lo, hi;
+                block_pair<kScale, false>(acc, i, h, sc, lo, hi);
+                const u32x4 packed = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                                      pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
+                __builtin_amdgcn_raw_buffer_store_b128(packed, rc, voff + 64 * h, soff, 0);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < kRB; ++i) {
         const int64_t m = row0 + 16 * i;
@@ -360,8 +461,8 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, int tm, int tn, 
             continue;
 #pragma unroll
         for (int h = 0; h < kCB / 2; ++h) {
-            const f32x4 lo = acc[i][2 * h] * sc;
-            const f32x4 hi = acc[i][2 * h + 1] * sc;
+            f32x4 lo, hi;
+            block_pair<kScale, kAgpr>(acc, i, h, sc, lo, hi);
             const int64_t n0 = col0 + 32 * h;
             const int64_t off = m * p.N + n0;
             u32x4 packed = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
@@ -443,20 +544,23 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
     const __amdgpu_buffer_rsrc_t rb =
         make_rsrc(static_cast<const char *>(p.B) + (int64_t)tn * kTile * ldk, rows_b * ldk);
 
-    // This lane's source offset inside a row group: row 8u + lane/8, slot
-    // lane%8; row bits 3,4 equal (u & 3) == w4 for every load this wave issues.
+    // This lane's source offsets inside a row group: row 8u + lane/8, slot
+    // lane%8; row bits 3,4 equal (u & 3) == w4 for every load this wave
+    // issues, so one offset per operand serves all its loads.
     const int r8 = lane >> 3;
-    const int cbytes = ((lane & 7) ^ slot_xor(r8 | (w4 << 3))) << 4;
-    const int voff0 = r8 * ldk + cbytes;
+    const int cb_a = ((lane & 7) ^ slot_xor_a(r8 | (w4 << 3))) << 4;
+    const int cb_b = ((lane & 7) ^ slot_xor_b(r8 | (w4 << 3))) << 4;
     // K step k covers row bytes [128 k - shift, +128): a partial step is step
     // 0, whose lanes with a chunk below byte 0 load zeros, and every later
-    // step is whole (the loads of steps past the end are never issued).
+    // step is whole.  Loads of steps >= nk fetch bytes no MFMA uses (in-range
+    // bytes of the panel's next rows, or zeros past its last row) into panels
+    // no one reads any more.
     const int shift = __builtin_amdgcn_readfirstlane(p.nk * kRowBytes - ldk);
-    const int voff_first = cbytes >= shift ? voff0 - shift : kOutOfRange;
-    auto voff = [&](int k) { return k == 0 ? voff_first : voff0; };
+    const int va = r8 * ldk + cb_a, vb = r8 * ldk + cb_b;
+    const int va_first = cb_a >= shift ? va - shift : kOutOfRange;
+    const int vb_first = cb_b >= shift ? vb - shift : kOutOfRange;
     auto soff = [&](int k) { return k == 0 ? 0 : k * kRowBytes - shift; };
 
-    const LaneOffsets lo = lane_offsets(lane);
     f32x4 acc[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -466,32 +570,40 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
 
     const int nk = p.nk;
     // K step k lives in A panel k % 2 and B panel k % 3 (lockstep: k % 2).
-    auto a_panel = [&](int k) { return smem + (k & 1) * kPanelBytes; };
-    auto b_panel = [&](int k) { return smem + kBRing + (k % kBPanels) * kPanelBytes; };
-    auto b_panel2 = [&](int k) { return smem + kBRing + (k & 1) * kPanelBytes; };
+    auto a_off = [&](int k) { return (k & 1) * kPanelBytes; };
+    auto b_off = [&](int k) { return kBRing + (k % kBPanels) * kPanelBytes; };
+    auto b_off2 = [&](int k) { return kBRing + (k & 1) * kPanelBytes; };
+    // this wave's 4 of the 8-row groups u = base + w4 + 4 v of a K step's panel
+    auto load_a = [&](int k, int off, int base) {
+        dma_panel_part<4>(ra, smem + off, base, w4, k == 0 ? va_first : va, soff(k), ldk);
+    };
+    auto load_b = [&](int k, int off, int base) {
+        dma_panel_part<4>(rb, smem + off, base, w4, k == 0 ? vb_first : vb, soff(k), ldk);
+    };
 
     if (kSched == kLockstep) {
+        const LaneOffsets lo = lane_offsets(lane);
         // Each wave loads its 16 of the 64 row groups of a K step.
         if (nk > 0) {
-            dma_panel_part<4>(ra, a_panel(0), 16 * g, w4, voff(0), soff(0), ldk);
-            dma_panel_part<4>(rb, b_panel2(0), 16 * g, w4, voff(0), soff(0), ldk);
+            load_a(0, a_off(0), 16 * g);
+            load_b(0, b_off2(0), 16 * g);
         }
         if (nk > 1) {
-            dma_panel_part<4>(ra, a_panel(1), 16 * g, w4, voff(1), soff(1), ldk);
-            dma_panel_part<4>(rb, b_panel2(1), 16 * g, w4, voff(1), soff(1), ldk);
+            load_a(1, a_off(1), 16 * g);
+            load_b(1, b_off2(1), 16 * g);
             wait_vmcnt<8>();
         } else {
             wait_vmcnt<0>();
         }
         block_barrier();
         for (int t = 0; t < nk; ++t) {
-            compute_kstep<kDtype>(a_frag_base(a_panel(t), g), b_frag_base(b_panel2(t), wn), lo,
-                                  acc);
+            compute_kstep<kDtype>(smem + a_off(t) + 128 * g * kRowBytes,
+                                  smem + b_off2(t) + 64 * wn * kRowBytes, lo, acc);
             wait_lgkmcnt0();
             block_barrier();                       // every wave is done with K step t
             if (t + 2 < nk) {
-                dma_panel_part<4>(ra, a_panel(t), 16 * g, w4, voff(t + 2), soff(t + 2), ldk);
-                dma_panel_part<4>(rb, b_panel2(t), 16 * g, w4, voff(t + 2), soff(t + 2), ldk);
+                load_a(t + 2, a_off(t), 16 * g);
+                load_b(t + 2, b_off2(t), 16 * g);
                 wait_vmcnt<8>();                   // K step t+1 has landed
             } else {
                 wait_vmcnt<0>();
@@ -503,115 +615,100 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
         // Phases alternate between the groups and end at a barrier:
         //   group 0:  c(0) | m(0) | c(1) | m(1) | ...
         //   group 1:  m(-1)| c(0) | m(0) | c(1) | ...
-        // c(t) is the MFMA cluster of K step t (its fragments already in
-        // registers); m(t) issues HBM->LDS loads for later K steps and reads
-        // all fragments of c(t+1) from LDS.  Loads (k = K step, into A panel k % 2 / B panel k % 3), 32 KiB
-        // per memory phase for either group (the CU's HBM->LDS path, not HBM,
-        // limits how fast they issue, so the two phases carry equal shares):
+        // c(t) is the MFMA cluster of K step t at s_setprio 3, its fragments
+        // already in registers; m(t) issues HBM->LDS loads for later K steps,
+        // then reads all fragments of c(t+1) from LDS (they land while the
+        // partner's cluster runs; reading first measured 4 % more cycles per
+        // K step).  Loads (k = K step, into A panel
+        // k % 2 / B panel k % 3), 32 KiB per memory phase for either group:
         //   A rows   0..127 of k: group 0 in m(k-2), awaited at the end of c(k-1)
         //   B rows   0..127 of k: group 0 in m(k-2), awaited at the end of c(k-1)
         //   A rows 128..255 of k: group 1 in m(k-2), awaited at the end of c(k-1)
         //   B rows 128..255 of k: group 1 in m(k-3), awaited at the end of m(k-2)
         // so every panel is complete and published by a barrier before the
-        // memory phase that reads its fragments, and no load targets a panel that a
-        // phase in flight still reads.  Group 1 ends after c(nk-1); group 0
-        // skips the barriers after its last cluster, keeping the counts equal.
+        // memory phase that reads its fragments, and no load targets a panel
+        // that a phase in flight still reads.  The loop body is the same for
+        // every t (loads of steps >= nk are harmless, see above).  Group 1
+        // ends after c(nk-1); group 0 skips the barriers after its last
+        // cluster, keeping the counts equal.
         using P = Pipe<kDtype>;
         typename P::Frags frags;
+        const QuadLane ql = quad_lane(lane);
+        const int a_rows = 128 * g * kRowBytes, b_rows = 64 * wn * kRowBytes;
+        // fragments of step k: four lane bases (one vector add each), then 24
+        // reads of base + immediate
+        auto read = [&](int k) {
+            const int ao = __builtin_amdgcn_readfirstlane(a_rows + a_off(k));
+            const int bo = __builtin_amdgcn_readfirstlane(b_rows + b_off(k));
+            const int ba[2] = {opaque(ql.a[0] + ao), opaque(ql.a[1] + ao)};
+            const int bb[2] = {opaque(ql.b[0] + bo), opaque(ql.b[1] + bo)};
+            P::read(frags, smem, ba, bb);
+        };
+        auto cluster = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(3);
+            P::cluster(frags, acc);
+            __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_sched_barrier(0);
+        };
         if (nk > 0) {   // K step 0: both groups share every panel
-            dma_panel_part<4>(ra, a_panel(0), 16 * g, w4, voff(0), soff(0), ldk);
-            dma_panel_part<4>(rb, b_panel(0), 16 * g, w4, voff(0), soff(0), ldk);
-        }
-        if (g == 0) {
-            if (nk > 1) {
-                dma_panel_part<4>(ra, a_panel(1), 0, w4, voff(1), soff(1), ldk);
-                dma_panel_part<4>(rb, b_panel(1), 0, w4, voff(1), soff(1), ldk);
+            load_a(0, a_off(0), 16 * g);
+            load_b(0, b_off(0), 16 * g);
+            if (g == 0) {
+                load_a(1, a_off(1), 0);
+                load_b(1, b_off(1), 0);
                 wait_vmcnt<8>();                   // K step 0 landed
             } else {
-                wait_vmcnt<0>();
-            }
-        } else {
-            if (nk > 1) {
-                dma_panel_part<4>(rb, b_panel(1), 16, w4, voff(1), soff(1), ldk);
+                load_b(1, b_off(1), 16);
                 wait_vmcnt<4>();                   // K step 0 landed
-            } else {
-                wait_vmcnt<0>();
             }
-        }
-        block_barrier();
+            block_barrier();
 
-        if (g == 0) {
-            if (nk > 0)
-                P::read(frags, a_frag_base(a_panel(0), 0), b_frag_base(b_panel(0), wn), lo);
-            for (int t = 0; t < nk; ++t) {
-                __builtin_amdgcn_sched_barrier(0);
-                __builtin_amdgcn_s_setprio(3);
-                P::cluster(frags, acc);
-                __builtin_amdgcn_s_setprio(0);
-                __builtin_amdgcn_sched_barrier(0);
-                wait_lgkmcnt0();
-                if (t == nk - 1)
-                    break;
-                wait_vmcnt<0>();                   // rows 0..127 of A and B of t+1 landed
-                block_barrier();                   // end of c(t)
-                if (t + 2 < nk) {
-                    dma_panel_part<4>(ra, a_panel(t + 2), 0, w4, voff(t + 2),
-                                      soff(t + 2), ldk);
-                    dma_panel_part<4>(rb, b_panel(t + 2), 0, w4, voff(t + 2),
-                                      soff(t + 2), ldk);
-                }
-                P::read(frags, a_frag_base(a_panel(t + 1), 0), b_frag_base(b_panel(t + 1), wn), lo);
-                block_barrier();                   // end of m(t)
-            }
-        } else if (nk > 0) {
-            // m(-1)
-            if (nk > 1)
-                dma_panel_part<4>(ra, a_panel(1), 16, w4, voff(1), soff(1), ldk);
-            if (nk > 2)
-                dma_panel_part<4>(rb, b_panel(2), 16, w4, voff(2), soff(2), ldk);
-            P::read(frags, a_frag_base(a_panel(0), 1), b_frag_base(b_panel(0), wn), lo);
-            if (nk > 2)
-                wait_vmcnt<8>();                   // B rows 128..255 of step 1 landed
-            else if (nk > 1)
-                wait_vmcnt<4>();
-            else
-                wait_vmcnt<0>();
-            if (nk > 1)
-                block_barrier();                   // end of m(-1)
-            for (int t = 0; t < nk; ++t) {
-                __builtin_amdgcn_sched_barrier(0);
-                __builtin_amdgcn_s_setprio(3);
-                P::cluster(frags, acc);
-                __builtin_amdgcn_s_setprio(0);
-                __builtin_amdgcn_sched_barrier(0);
-                wait_lgkmcnt0();
-                if (t == nk - 1)
-                    break;
-                if (t + 2 < nk)
-                    wait_vmcnt<4>();               // A rows 128..255 of t+1 landed
-                else
-                    wait_vmcnt<0>();
-                block_barrier();                   // end of c(t)
-                if (t + 2 < nk)
-                    dma_panel_part<4>(ra, a_panel(t + 2), 16, w4, voff(t + 2),
-                                      soff(t + 2), ldk);
-                if (t + 3 < nk)
-                    dma_panel_part<4>(rb, b_panel(t + 3), 16, w4, voff(t + 3),
-                                      soff(t + 3), ldk);
-                P::read(frags, a_frag_base(a_panel(t + 1), 1), b_frag_base(b_panel(t + 1), wn), lo);
-                if (t + 3 < nk)
-                    wait_vmcnt<8>();               // B rows 128..255 of step t+2 landed
-                else if (t + 2 < nk)
-                    wait_vmcnt<4>();
-                else
-                    wait_vmcnt<0>();
-                if (t != nk - 2)
+            if (g == 0) {
+                read(0);
+                for (int t = 0; t < nk; ++t) {
+                    cluster();
+                    wait_lgkmcnt0();
+                    if (t == nk - 1)
+                        break;
+                    wait_vmcnt<0>();               // rows 0..127 of A and B of t+1 landed
+                    block_barrier();               // end of c(t)
+                    load_a(t + 2, a_off(t + 2), 0);
+                    load_b(t + 2, b_off(t + 2), 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    read(t + 1);
                     block_barrier();               // end of m(t)
+                }
+            } else {
+                // m(-1)
+                load_a(1, a_off(1), 16);
+                load_b(2, b_off(2), 16);
+                __builtin_amdgcn_sched_barrier(0);
+                read(0);
+                wait_vmcnt<8>();                   // B rows 128..255 of step 1 landed
+                if (nk > 1)
+                    block_barrier();               // end of m(-1)
+                for (int t = 0; t < nk; ++t) {
+                    cluster();
+                    wait_lgkmcnt0();
+                    if (t == nk - 1)
+                        break;
+                    wait_vmcnt<4>();               // A rows 128..255 of t+1 landed
+                    block_barrier();               // end of c(t)
+                    load_a(t + 2, a_off(t + 2), 16);
+                    load_b(t + 3, b_off(t + 3), 16);
+                    __builtin_amdgcn_sched_barrier(0);
+                    read(t + 1);
+                    wait_vmcnt<8>();               // B rows 128..255 of step t+2 landed
+                    if (t != nk - 2)
+                        block_barrier();           // end of m(t)
+                }
             }
         }
     }
+    wait_vmcnt<0>();                               // no load still writes LDS at exit
     const Stamp s1 = stamp();
-    store_tile<8, 4, kTile>(p, tm, tn, 128 * g, 64 * wn, lane, acc);
+    store_tile<8, 4, kTile, kDtype == kFp8, false>(p, tm, tn, 128 * g, 64 * wn, lane, acc);
     write_trace(p, s0, s1, tm, tn);
 }
 
@@ -640,47 +737,6 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
 // t: the loads of K steps >= nk fetch bytes no MFMA uses -- in-range bytes of
 // the panel's next rows, or zeros past the panel's last row -- into panels no
 // one reads any more, and the reads of "step nk" in the last half are unused.
-// ---- 4-wave layout ----------------------------------------------------------
-// The A and B panels of the 4-wave kernel use one XOR swizzle each instead of
-// the shared slot_xor: the A fragment reads vary row bits 1,2,3 within a
-// 16-lane group and B's interleaved reads bits 1,3,4 (plus the row parity
-// bit 0, which selects the bank half), so
-//   A: slot = chunk ^ (b1 | b3 << 1 | b2 << 2)   (independent of row bit 4)
-//   B: slot = chunk ^ (b1 | b3 << 1 | b4 << 2)   (independent of row bit 2)
-// are bank-conflict free, and the two row parities of a fragment pair (A
-// rows 16 apart, B rows 4 apart) lie a constant 2048 / 512 bytes apart, so
-// one lane base per operand and chunk half serves every block.
-__device__ __forceinline__ int slot_xor_a(int r)
-{
-    return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2);
-}
-__device__ __forceinline__ int slot_xor_b(int r)
-{
-    return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 4) & 1) << 2);
-}
-
-// Lane part of a fragment read, chunk half h (chunk 4 h + q): A row x, B row
-// (x & 3) + 8 (x >> 2) of a block pair, x = lane % 16, q = lane / 16.  For
-// bf16 the halves are the two DOT_SLICEs.  For e4m3 this is the 16x16x128
-// MFMA's own k order (lane group q supplies k 16q..16q+15 and 64 + 16q..+15,
-// probed on gfx950); the block-scaled form applies the scale in lane group b
-// to the 32 k of block b, so the MXFP8 scales follow the same order.
-struct QuadLane {
-    int a[2], b[2];
-};
-__device__ __forceinline__ QuadLane quad_lane(int lane)
-{
-    const int x = lane & 15, q = lane >> 4;
-    const int rb = (x & 3) + 8 * (x >> 2);
-    QuadLane l;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        l.a[h] = x * kRowBytes + (((4 * h + q) ^ slot_xor_a(x)) << 4);
-        l.b[h] = rb * kRowBytes + (((4 * h + q) ^ slot_xor_b(rb)) << 4);
-    }
-    return l;
-}
-
 // MXFP8 scales of one K step for one lane l: byte e of a[e >> 2] is the E8M0
 // scale of A fragment e's row for lane l and k block 4 t + l / 16 (the block
 // the MFMA scales with lane group l / 16's value), b likewise for B fragment
@@ -723,20 +779,20 @@ __device__ __forceinline__ f32x4 mma_mx(const i32x8 &x, const i32x8 &y, const f3
     default: return mma_mx_c<3, 3>(x, y, c, sx, sy);
     }
 }
-// Offsets of A fragment i (rows 16 i ..) and B fragment j (rows 32 (j >> 1)
-// + 4 (j & 1) + interleave) from the lane's base.
-__device__ __forceinline__ constexpr int qa_blk(int i) { return 16 * i * kRowBytes; }
-__device__ __forceinline__ constexpr int qb_blk(int j) { return (32 * (j >> 1) + 4 * (j & 1)) * kRowBytes; }
 
-// An empty asm that claims to change x.  Applied to the lane base address of
-// a half, it stops the optimiser from folding a panel's offset into a
-// separate precomputed address per fragment read (one register each, and one
-// vector add each per K step): every read stays one ds_read of
-// (base + constant block offset).
-__device__ __forceinline__ int opaque(int x)
+
+// The accumulators leave the K loop in the accumulation registers (AGPRs),
+// whatever the epilogue does with them: without this, how the epilogue reads
+// them feeds back into the loop's register assignment, and the allocator
+// then moves accumulators between AGPRs and VGPRs inside the loop.
+template <int kR, int kC>
+__device__ __forceinline__ void pin_acc(f32x4 (&acc)[kR][kC])
 {
-    asm volatile("" : "+v"(x));
-    return x;
+#pragma unroll
+    for (int i = 0; i < kR; ++i)
+#pragma unroll
+        for (int j = 0; j < kC; ++j)
+            asm volatile("" : "+a"(acc[i][j]));
 }
 
 // Scalar counterparts.  Instruction selection orders a whole K step (one
@@ -1341,8 +1397,10 @@ __global__ __launch_bounds__(256, kT == 128 ? 2 : 1) void gemm4_kernel(const Gem
         wait_vmcnt<0>();
     }
     const Stamp s1 = stamp();
-    store_tile<kB, kB, kT>(p, tm, tn, c.a_rows / kRowBytes, (c.b_rows - kRing) / kRowBytes, lane,
-                           acc);
+    if constexpr (kB >= 6)   // accumulators in AGPRs (the 128 x 128 tile keeps them in VGPRs)
+        pin_acc(acc);
+    store_tile<kB, kB, kT, kDtype == kFp8, (kB >= 6)>(p, tm, tn, c.a_rows / kRowBytes,
+                                                      (c.b_rows - kRing) / kRowBytes, lane, acc);
     write_trace(p, s0, s1, tm, tn);
 }
 

@@ -12,6 +12,7 @@
 #include "../../include/hkg.h"
 #include "kernels.h"
 #include "remap.h"
+#include "remap_model.h"
 
 namespace {
 
@@ -80,25 +81,15 @@ int64_t mx_packed_bytes(int64_t rows, int64_t K)
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// W beyond the grid height, and any chunk with 8*C > G (no full cycle: the
-// whole grid is handled by the tail rule), give the same order; clamping keeps
-// the kernel's 32-bit products W*Gn and 8*C in range.
 void clamp_remap(int64_t Gm, int64_t Gn, int64_t *W, int64_t *C)
 {
-    const int64_t G = Gm * Gn;
-    if (*W > Gm)
-        *W = Gm;
-    if (*C > G / hkg::kNumXcd + 1)
-        *C = G / hkg::kNumXcd + 1;
-    if (*W < 1)
-        *W = 1;
-    if (*C < 1)
-        *C = 1;
+    hkg::clamp_order(Gm, Gn, *W, *C);
 }
 
 // (W, C) used when the caller does not choose one; row_bytes = K x element
 // size.  Both choices give each XCD's 32 concurrent tiles a patch that
-// shares 12 operand panels in its L2 (the L2 term of the pages' Eq. 1):
+// shares 12 operand panels in its L2 (the L2 term of the pages' Eq. 1; the
+// cache model of remap_model.h predicts 81 % L2 hits for both):
 //  - (8, 32): chunks of 32 consecutive remapped ids per XCD, an 8 x 4 patch;
 //    the 256 tiles in flight on the chip form an 8 x 32 strip of the grid
 //    (40 panels);
@@ -109,7 +100,10 @@ void clamp_remap(int64_t Gm, int64_t Gn, int64_t *W, int64_t *C)
 // of Eq. 1).  Measured at square sizes: (8, 32) is as good or better while 40
 // panels stay below ~185 MiB (bf16 n <= 9216, e4m3 n <= 12288, K = 4096
 // shapes), and (16, 4) wins above (bf16 10000, 12288, 14592, 16384: +5.4,
-// +1.6, +1.0, +5.1 %).
+// +1.6, +1.0, +5.1 %).  Ranking every candidate by the model's Eq. 1
+// bandwidth agrees at 8192, 12288, 14592 and 16384 bf16 but not at 10000
+// bf16, e4m3 12288 or K = 4096 (its LLC term is too coarse there), so the
+// measured rule stays the default and the model serves as hkg_remap_model.
 constexpr int64_t kLlcPanelBudget = int64_t(185) << 20;
 constexpr int64_t kBigRowBytes = kLlcPanelBudget / (40 * kTile);   // 18944 B (bf16 K > 9472)
 
@@ -563,6 +557,25 @@ int hkg_launch_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, const hkg_ge
         plan->W[i] = pl.W[i];
         plan->C[i] = pl.C[i];
     }
+    return HKG_OK;
+}
+
+int hkg_remap_model(int64_t Gm, int64_t Gn, int32_t W, int32_t C, int64_t panel_bytes,
+                    int32_t per_xcd, double *l2_hit, double *llc_hit, double *eq1_bw_tbs)
+{
+    if (!l2_hit || !llc_hit || !eq1_bw_tbs)
+        return HKG_ERR_NULL;
+    if (Gm < 1 || Gn < 1 || W < 1 || C < 1 || Gm * Gn >= (int64_t(1) << 30) || panel_bytes < 0 ||
+        per_xcd < 1 || per_xcd > 1024)
+        return HKG_ERR_SHAPE;
+    int64_t w = W, c = C;
+    clamp_remap(Gm, Gn, &w, &c);
+    const hkg::RemapModel m =
+        hkg::model_remap(static_cast<int>(Gm), static_cast<int>(Gn), static_cast<int>(w),
+                         static_cast<int>(c), panel_bytes, per_xcd);
+    *l2_hit = m.l2_hit;
+    *llc_hit = m.llc_hit;
+    *eq1_bw_tbs = m.bw_tbs;
     return HKG_OK;
 }
 

@@ -17,6 +17,8 @@
 // so that W*Gn and 8*C stay within 32 bits for G < 2^30.
 #pragma once
 
+#include <stdint.h>
+
 #ifndef __HIPCC__
 #define HKG_HD inline
 #else
@@ -26,6 +28,22 @@
 namespace hkg {
 
 constexpr int kNumXcd = 8;
+
+// W beyond the grid height, and any chunk with 8*C > G (no full cycle: the
+// whole grid is handled by the tail rule), give the same order; clamping keeps
+// the kernel's 32-bit products W*Gn and 8*C in range for G < 2^30.
+inline void clamp_order(int64_t Gm, int64_t Gn, int64_t &W, int64_t &C)
+{
+    const int64_t G = Gm * Gn;
+    if (W > Gm)
+        W = Gm;
+    if (C > G / kNumXcd + 1)
+        C = G / kNumXcd + 1;
+    if (W < 1)
+        W = 1;
+    if (C < 1)
+        C = 1;
+}
 
 HKG_HD void remap_tile(int b, int Gm, int Gn, int W, int C, int &tile_m, int &tile_n)
 {

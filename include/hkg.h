@@ -229,12 +229,14 @@ int hkg_mx_pack_scales(int32_t operand, int64_t rows, int64_t K, const void *sca
  * The (W, C) the library uses for HKG_REMAP_DEFAULT on a shape (host only, no
  * HIP call).  dtype: 0 = bf16, 1 = fp8, 2 = MXFP8.  Returns HKG_ERR_NULL/SHAPE
  * on bad input.  The grid is that of the default call's first launch
- * (hkg_launch_plan: W[0], C[0]; tiles of 256, or of 128 where
- * HKG_SCHED_DEFAULT picks them).  Rule (the L2 and LLC terms
- * of the HipKittens L2 note's section 4 equation): (8, 32) while an operand
- * row holds at most 18944 bytes (K x element size), else (16, 4), whose 256
- * concurrent tiles share fewer operand panels in the last-level cache; both
- * clamped to the grid (W <= tile rows, C <= tiles/8 + 1).
+ * (hkg_launch_plan: W[0], C[0]; tiles of 256, or of 128 / 192 where
+ * HKG_SCHED_DEFAULT picks them).  Rule (the L2 and LLC terms of the
+ * HipKittens L2 note's section 4 equation): (8, 32) while an operand row
+ * holds at most 18944 bytes (K x element size), else (16, 4).  Both keep each
+ * XCD's 32 concurrent tiles on 12 operand panels (the same L2 hit rate); the
+ * second's 256 concurrent tiles share fewer panels (32 instead of 40), which
+ * keeps a round's panels inside the last-level cache for long rows.  Both
+ * are clamped to the grid (W <= tile rows, C <= tiles/8 + 1).
  */
 int hkg_default_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t *W, int32_t *C);
 
@@ -265,6 +267,29 @@ typedef struct {
 
 int hkg_launch_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, const hkg_gemm_opts *opts,
                     hkg_launch_plan_t *plan);
+
+/*
+ * The cache model behind the default grid order (host only, no HIP call):
+ * for a Gm x Gn tile grid walked in order (W, C), with operand panels of
+ * panel_bytes (tile rows x K x element size) and per_xcd workgroups in
+ * flight per XCD (32 CUs x workgroups per CU: 32 for 256 x 256 and 192 x 192
+ * tiles, 64 for 128 x 128), the predicted
+ *   l2_hit      fraction of operand-panel requests served by an XCD's L2
+ *               (its concurrent tiles stream the same K steps together, so a
+ *               panel misses once per round: 1 - distinct panels / requests)
+ *   llc_hit     fraction of L2 misses served by the 256 MiB last-level cache
+ *               (a panel another XCD fetches in the same round, or one used in
+ *               the previous round when that round's panels fit the cache)
+ *   eq1_bw_tbs  5.99 * llc_hit + 17.05 * l2_hit (TB/s; the constants fit every
+ *               row of the note's Table 4, section 5)
+ * Workgroup b is taken to run on XCD b mod 8 (hkg_probe_xcd checks it), and
+ * rounds of 8 * per_xcd workgroups to run together; the first 8 rounds are
+ * simulated.  An analysis aid: the default order (hkg_default_remap) is the
+ * measured rule, which this model's L2 term explains.
+ * Returns HKG_ERR_NULL / HKG_ERR_SHAPE on bad input.
+ */
+int hkg_remap_model(int64_t Gm, int64_t Gn, int32_t W, int32_t C, int64_t panel_bytes,
+                    int32_t per_xcd, double *l2_hit, double *llc_hit, double *eq1_bw_tbs);
 
 /*
  * The grid remap itself (HipKittens L2 note, section 7 Algorithm 1 reading): flat

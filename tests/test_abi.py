@@ -22,7 +22,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = hkg.load()
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 16
     assert sorted(hkg.EXPORTS) == names
     for n in names:
         assert getattr(lib, n) is not None
@@ -355,3 +355,44 @@ def test_trace_buffer_validated_before_launch():
     o = hkg.make_opts(trace=FAKE)                            # over A
     assert hkg.hkg_gemm_fp8_ex(M, N, 128, FAKE, FB, 1.0, 1.0, FC, None, None, o) == hkg.HKG_ERR_OVERLAP
     assert ctypes.sizeof(hkg.hkg_gemm_opts) == 24
+
+
+def _table4():
+    import csv
+    path = os.path.join(ROOT, "tests", "golden", "table4_chiplet_schedule.csv")
+    return list(csv.DictReader(line for line in open(path) if not line.startswith("#")))
+
+
+def test_remap_model_l2_term_tracks_table4():
+    """The cache model's L2 hit rate for the pages' Table 4 orders (HipKittens L2
+    note, section 5): within 6.5 points of the printed value on every row but the
+    9216 row-major one (printed 55 %, modelled 73 %), and the rows of each size in
+    the printed order of Eq. 1 bandwidth (TFLOPS order) at 14592."""
+    got = {}
+    for r in _table4():
+        n = int(r["size"])
+        g = -(-n // 256)
+        rc, l2, llc, bw = hkg.hkg_remap_model(g, g, int(r["W"]), int(r["C"]), 256 * n * 2)
+        assert rc == hkg.HKG_OK and 0 <= l2 <= 1 and 0 <= llc <= 1
+        assert bw == pytest.approx(17.05 * l2 + 5.99 * llc)
+        got[(n, int(r["W"]), int(r["C"]))] = (l2, llc, bw, float(r["l2_pct"]), float(r["tflops"]))
+    for (n, W, C), (l2, llc, bw, page_l2, tf) in got.items():
+        if (n, W, C) != (9216, 1, 1):
+            assert abs(100 * l2 - page_l2) <= 6.5, (n, W, C, l2, page_l2)
+    rows = sorted((v for k, v in got.items() if k[0] == 14592), key=lambda v: v[4])
+    assert [v[2] for v in rows] == sorted(v[2] for v in rows)
+
+
+def test_remap_model_closed_forms():
+    # one XCD round of a grid with a single tile column: every tile of an XCD
+    # shares the one B panel, rows all differ -> L2 hit = 1 - (32 + 1) / 64
+    rc, l2, llc, bw = hkg.hkg_remap_model(256, 1, 1, 1, 1 << 20)
+    assert rc == hkg.HKG_OK and l2 == pytest.approx(1 - 33 / 64)
+    # (8, 32) on a 32 x 32 grid: each XCD's 32 tiles form an 8 x 4 patch: 12 panels
+    rc, l2, llc, bw = hkg.hkg_remap_model(32, 32, 8, 32, 4 << 20)
+    assert l2 == pytest.approx(1 - 12 / 64)
+    # a single tile: both panels miss
+    rc, l2, llc, bw = hkg.hkg_remap_model(1, 1, 1, 1, 1 << 20)
+    assert l2 == 0.0 and llc == 0.0
+    assert hkg.hkg_remap_model(0, 4, 1, 1, 1, 32)[0] == hkg.HKG_ERR_SHAPE
+    assert hkg.hkg_remap_model(4, 4, 0, 1, 1, 32)[0] == hkg.HKG_ERR_SHAPE
