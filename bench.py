@@ -8,10 +8,19 @@ M = N = K = 8192 with seeded N(0,1) inputs.  Prints one JSON line with the
 throughput (TFLOPS), the MFMA roofline of the kernel (live HIP-event timing),
 and the CPU oracle timed on a bounded sample as a baseline.
 
+Timing: W warm-up steps, a barrier, then exactly K timed steps.  This is done
+twice: first right after the inputs are uploaded ("from_idle" in the line),
+then after --settle-ms (200) of untimed steps back to back ("value").  An idle
+MI355X under its power cap takes ~50-100 ms of load before its clock settles
+(it starts near 1.5 GHz, dips, then rises to its steady clock), and a short
+timed region right after an idle gap measures that ramp, not the kernel.
+
   python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload 2]
-                  [--all] [--remap W,C | --row-major]
+                  [--settle-ms 200] [--all] [--remap W,C | --row-major]
                   [--schedule interleave|pingpong|lockstep|interleave128|interleave192]
                   [--no-cpu-baseline]
+  python bench.py --clock-ramp 800 [--workload N | --all]
+        the clock after 2 s of idle, per window of launches (time record)
   python bench.py --sizes "1024 2048 ..." [--dtype bf16|fp8|mxfp8] [--vendor]
         square-size sweep: each schedule (4-wave 256 and 128 tiles, ping-pong) per
         size, one JSON line each
@@ -200,7 +209,7 @@ def launch_plan(w: synth.Workload, opts) -> list:
 
 
 def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
-              with_cpu: bool, deadline_s: float = 120.0) -> dict:
+              with_cpu: bool, deadline_s: float = 120.0, settle_ms: float = 200.0) -> dict:
     import torch
     import dense_gemm_fp8_amd as hkg
 
@@ -249,30 +258,70 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
         if e1 is not None:
             e1.record(stream)
 
-    for _ in range(warmup):
-        step()
-    mark = torch.cuda.Event()
-    mark.record(stream)
-    wait_event(mark, deadline_s, "warm-up")
-    torch.cuda.synchronize()
-
-    # timed region: every GEMM launch bracketed by HIP events on the launch stream
+    # events and per-launch options of a timed region, made before any warm-up so
+    # that nothing but the barrier separates the warm-up from the timed steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     outer0 = torch.cuda.Event(enable_timing=True)
     outer1 = torch.cuda.Event(enable_timing=True)
     topts = [traced(i) for i in range(steps)]
-    t0 = time.perf_counter()
-    outer0.record(stream)
-    for i, (s, e) in enumerate(ev):
-        step(s, e, topts[i])
-    outer1.record(stream)
-    wait_event(outer1, deadline_s, "timed region")
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    clock_info = clock_from_trace(trace.cpu().numpy(), steps)
-    per_launch_ms = np.array([s.elapsed_time(e) for s, e in ev])
-    region_ms = outer0.elapsed_time(outer1)
+
+    def warm_then_time():
+        """W untimed warm-up steps, a barrier, then exactly `steps` timed steps,
+        every GEMM launch bracketed by HIP events on the launch stream."""
+        for _ in range(warmup):
+            step()
+        mark = torch.cuda.Event()
+        mark.record(stream)
+        wait_event(mark, deadline_s, "warm-up")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        outer0.record(stream)
+        for i, (s, e) in enumerate(ev):
+            step(s, e, topts[i])
+        outer1.record(stream)
+        wait_event(outer1, deadline_s, "timed region")
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return (np.array([s.elapsed_time(e) for s, e in ev]), outer0.elapsed_time(outer1), wall,
+                clock_from_trace(trace.cpu().numpy(), steps))
+
+    def settle(ms: float) -> int:
+        """Untimed steps back to back for at least `ms` of wall time (8 to 24 in
+        flight, so the GPU never idles); returns how many ran."""
+        marks, n, t0 = [], 0, time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < ms:
+            for _ in range(8):
+                step()
+            n += 8
+            e = torch.cuda.Event()
+            e.record(stream)
+            marks.append(e)
+            if len(marks) > 2:
+                wait_event(marks.pop(0), deadline_s, "settle")
+        return n
+
+    # 1. as asked: W warm-up steps right after the inputs arrived (the GPU was
+    #    idle while they were drawn), then the K timed steps
+    per_launch_ms, region_ms, wall, clock_info = warm_then_time()
+    from_idle = {"value": round(w.flops / (region_ms / steps * 1e-3) / 1e12, 2),
+                 "ms_per_step": round(region_ms / steps, 5),
+                 "kernel_ms_mean": round(float(per_launch_ms.mean()), 5),
+                 "mhz_mean": clock_info["mhz_mean"]}
+    settle_info = None
+    if settle_ms > 0:
+        # 2. after any idle gap the power controller takes ~50-100 ms of load to
+        #    settle (it starts near 1.5 GHz and dips before it rises to the steady
+        #    clock); `value` is measured at that steady clock: untimed steps for
+        #    settle_ms, then the same W warm-up and K timed steps again
+        t_s = time.perf_counter()
+        n_settle = settle(settle_ms)
+        settle_info = {"ms": round((time.perf_counter() - t_s) * 1e3, 1), "launches": n_settle,
+                       "rule": "untimed steps back to back for at least %g ms before the W warm-up "
+                               "steps, so that the K timed steps run at the steady power-capped "
+                               "clock, not on the clock ramp that follows an idle GPU; from_idle "
+                               "is the same W + K measurement without it" % settle_ms}
+        per_launch_ms, region_ms, wall, clock_info = warm_then_time()
     ms_per_step = region_ms / steps
     tflops = w.flops / (ms_per_step * 1e-3) / 1e12
     kern_ms = float(per_launch_ms.mean())
@@ -321,6 +370,8 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
         "cache": cache_fields(facts),
         "counters": counter_fields(facts),
         "clock": clock_info,
+        "settle": settle_info,
+        "from_idle": from_idle,
         "wall_s_timed_region": round(wall, 4),
         "kernel_source_hash": kernel_source_hash(),
         "gpu": torch.cuda.get_device_name(dev),
@@ -352,7 +403,8 @@ def counter_fields(facts: dict) -> dict:
     """MFMA busy and LDS bank conflicts from the committed counter run of this
     kernel source (rocprofv3 --pmc in a separate process; null when the
     kernel source has changed since)."""
-    keys = ("mfma_busy_pct", "lds_bank_conflict_cycles", "wait_any_pct", "counter_clock_ghz")
+    keys = ("mfma_busy_pct", "lds_bank_conflict_cycles", "wait_any_pct", "wait_inst_lds_pct",
+            "counter_clock_ghz")
     out = {k: facts.get(k) for k in keys}
     out["source"] = facts.get("source")
     return out
@@ -420,6 +472,56 @@ def sweep(w: synth.Workload, pairs, steps: int, warmup: int) -> None:
                           "default": [W, Cc] == [dW, dC],
                           "ms": round(ms, 5), "ms_runs": [round(t, 5) for t in times[key]],
                           "TFLOPS": round(w.flops / (ms * 1e-3) / 1e12, 2)}), flush=True)
+
+
+def clock_ramp(w: synth.Workload, launches: int, idle_s: float) -> None:
+    """The clock after an idle GPU: `launches` default launches back to back
+    after idle_s seconds of idle, each with the kernels' time record; one JSON
+    line with the mean clock and throughput over windows of launches."""
+    import torch
+    import dense_gemm_fp8_amd as hkg
+
+    if w.dtype not in ("bf16", "fp8"):
+        raise ValueError("--clock-ramp runs the bf16 and e4m3 workloads")
+    dev = torch.device("cuda:0")
+    A, B, sa, sb = synth.make_inputs(w)
+    if w.dtype == "bf16":
+        dA = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).to(dev)
+        dB = torch.from_numpy(B.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    del A, B
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    wgs = sum(d["workgroups"] for d in launch_plan(w, None))
+    trace = torch.zeros((launches, wgs, 8), dtype=torch.int64, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    opts = [hkg.make_opts(trace=trace[i].data_ptr()) for i in range(launches)]
+    torch.cuda.synchronize()
+    time.sleep(idle_s)
+    for i in range(launches):
+        ev[i][0].record(stream)
+        if w.dtype == "bf16":
+            hkg.gemm_bf16(dA, dB, C, opts=opts[i], stream=stream)
+        else:
+            hkg.gemm_fp8(dA, dB, sa, sb, C, opts=opts[i], stream=stream)
+        ev[i][1].record(stream)
+    wait_event(ev[-1][1], 120.0, "clock ramp")
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    rec = trace.cpu().numpy()
+    out = {"clock_ramp": w.name, "idle_s": idle_s, "launches": launches, "windows": []}
+    lo = 0
+    for hi in (5, 10, 25, 50, 100, 200, 400, 800, 1600):
+        if hi > launches:
+            break
+        c = clock_from_trace(rec[lo:hi], hi - lo)
+        out["windows"].append({"launches": [lo, hi], "ends_at_ms": round(float(ms[:hi].sum()), 1),
+                               "mhz_mean": c["mhz_mean"],
+                               "tflops": round(w.flops / (float(ms[lo:hi].mean()) * 1e-3) / 1e12, 1)})
+        lo = hi
+    print(json.dumps(out), flush=True)
 
 
 def size_sweep(sizes, dtype: str, warmup: int, vendor: bool = False) -> None:
@@ -521,6 +623,12 @@ def main(argv=None) -> int:
                                            "interleave192"],
                     default="interleave", help="in-CU schedule (default: the library's, interleave)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--clock-ramp", type=int, default=0, metavar="N",
+                    help="time N default launches after 2 s of idle, each with the time record, "
+                         "and print the clock per window of launches")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed steps (ms of wall time) between a first W + K measurement from "
+                         "idle and the W + K measurement reported as value; 0 reports the first")
     ap.add_argument("--deadline", type=float, default=120.0,
                     help="seconds to wait for the GPU to finish the warm-up or the timed "
                          "region before reporting a hang (exit status 3)")
@@ -556,6 +664,10 @@ def main(argv=None) -> int:
     if args.sizes:
         size_sweep(args.sizes.split(), args.dtype, args.warmup, args.vendor)
         return 0
+    if args.clock_ramp:
+        for i in ([2, 5] if args.all else [args.workload]):
+            clock_ramp(synth.workload(i), args.clock_ramp, 2.0)
+        return 0
     if args.sweep:
         w = custom_workload(args.shape, args.dtype) if args.shape else synth.workload(args.workload)
         pairs = [tuple(int(v) if v.isdigit() else v for v in item.split(","))
@@ -567,7 +679,8 @@ def main(argv=None) -> int:
         w = synth.workload(i) if not args.shape else custom_workload(args.shape, args.dtype)
         steps = args.steps
         res = bench_one(w, steps, args.warmup, opts, args.schedule,
-                        with_cpu=(not args.no_cpu_baseline), deadline_s=args.deadline)
+                        with_cpu=(not args.no_cpu_baseline), deadline_s=args.deadline,
+                        settle_ms=args.settle_ms)
         print(json.dumps(res), flush=True)
     return 0
 

@@ -19,7 +19,8 @@
 //   B ring: 3 panels [256 rows][128 B] (K step k in panel k % 3)
 //   one 128-byte row = one K step of one operand row (64 bf16 or 128 e4m3)
 //   row r stores its eight 16-byte chunks permuted: chunk c lives in slot
-//   c ^ slot_xor(r).
+//   c ^ x(r), with x = slot_xor_a for A panels and slot_xor_b for B panels
+//   (defined below; one map per operand).
 // The pages keep a 2-deep LDS double buffer (HipKittens L2 note, section 4 "Pipeline
 // depth"); the third B panel here exists so that the ping-pong below can
 // prefetch register fragments one phase early while the shared B panel still
@@ -36,7 +37,7 @@
 // M0 + 16*l, so one instruction fills 8 consecutive rows (1 KiB).  The lane
 // therefore cannot choose where its bytes land; instead each lane fetches the
 // global chunk that belongs in its fixed slot: lane l -> row 8u + l/8,
-// slot l%8, global chunk (l%8) ^ slot_xor(row).  This is the "swizzle applied
+// slot l%8, global chunk (l%8) ^ x(row).  This is the "swizzle applied
 // to the HBM address" of the HipKittens L2 note (section 2) and summary page.
 //
 // Waves and the output tile (WARPS_M = 2 x WARPS_N = 4):

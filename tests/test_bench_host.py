@@ -1,0 +1,70 @@
+"""Host-side logic of bench.py (no GPU): argument limits, the time-record
+decoder, the counter facts and the Eq. 1 field."""
+import json
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
+
+
+def test_clock_from_trace_decodes_a_known_record():
+    # 2 launches x 16 workgroups; workgroup b on XCD b % 8 at (1500 + 20 x) MHz:
+    # shader-clock ticks = MHz / 100 per real-time tick
+    L, G = 2, 16
+    rec = np.zeros((L, G, 8), dtype=np.int64)
+    for li in range(L):
+        for b in range(G):
+            x = b % 8
+            rt0 = 1_000_000 + 50_000 * li + 10 * b
+            kl, ep = 18_000, 500                     # 180 us K loop, 5 us epilogue
+            mhz = 1500 + 20 * x
+            rec[li, b, :] = [rt0, rt0 + kl, rt0 + kl + ep, 7, 7 + kl * mhz // 100, 0, x,
+                             (b // 4) << 32 | (b % 4)]
+    c = bench.clock_from_trace(rec, L)
+    assert c["mhz_per_xcd"] == [1500.0 + 20 * x for x in range(8)]
+    assert abs(c["mhz_mean"] - 1570.0) < 1e-9
+    assert c["kloop_us_mean"] == 180.0 and c["epilogue_us_mean"] == 5.0
+    assert c["tile_us_mean"] == 185.0
+    assert c["launch_span_us_mean"] == (10 * 15 + kl + ep) / 100.0
+    assert c["workgroups_per_launch"] == G
+
+
+def test_profile_facts_follow_the_kernel_source(tmp_path, monkeypatch):
+    h = bench.kernel_source_hash()
+    facts = {"kernel_source_hash": h, "l2_hit_pct": 80.0}
+    os.makedirs(tmp_path / "profiles")
+    (tmp_path / "profiles" / "counters_x.json").write_text(json.dumps(facts))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: h)
+    assert bench.load_profile_facts("x")["l2_hit_pct"] == 80.0
+    facts["kernel_source_hash"] = "0" * 16
+    (tmp_path / "profiles" / "counters_x.json").write_text(json.dumps(facts))
+    assert bench.load_profile_facts("x") == {}
+    assert bench.load_profile_facts("missing") == {}
+
+
+def test_committed_facts_match_this_source():
+    """Every committed counter file names its kernel source; those of the five
+    workloads must match the current one, or bench.py drops them silently."""
+    for name in ("bf16_8192", "fp8_e4m3_8192", "mxfp8_8192", "bf16_mlp_16384x14336x4096",
+                 "bf16_16384"):
+        facts = bench.load_profile_facts(name)
+        assert facts, name
+        assert 0 < facts["l2_hit_pct"] < 100 and facts["hbm_bytes_per_launch"] > 0
+
+
+def test_eq1_l2_term():
+    c = bench.cache_fields({"l2_hit_pct": 80.0})
+    assert abs(c["eq1"]["l2_term_tbs"] - 0.8 * bench.EQ1_L2_BW_TBS) < 0.006
+    assert c["eq1"]["llc_term_tbs"] is None
+    assert bench.cache_fields({})["eq1"]["l2_term_tbs"] is None
