@@ -16,7 +16,7 @@ MI355X under its power cap takes ~50-100 ms of load before its clock settles
 timed region right after an idle gap measures that ramp, not the kernel.
 
   python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload 2]
-                  [--settle-ms 200] [--all] [--remap W,C | --row-major]
+                  [--settle-ms 200] [--all] [--remap W,C | --row-major | --tune]
                   [--schedule interleave|pingpong|lockstep|interleave128|interleave192]
                   [--no-cpu-baseline]
   python bench.py --clock-ramp 800 [--workload N | --all]
@@ -24,8 +24,9 @@ timed region right after an idle gap measures that ramp, not the kernel.
   python bench.py --sizes "1024 2048 ..." [--dtype bf16|fp8|mxfp8] [--vendor]
         square-size sweep: each schedule (4-wave 256 and 128 tiles, ping-pong) per
         size, one JSON line each
-  python bench.py --sweep "1,1 8,32 5,25 8,32,i192 ..." [--workload N | --shape M,N,K --dtype bf16|fp8]
-        grid-order sweep: one JSON line per (W, C) on the same resident inputs
+  python bench.py --sweep "default 1,1 8,32 5,25 8,32,i192 ..." [--workload N | --shape M,N,K --dtype bf16|fp8]
+        grid-order sweep: one JSON line per (W, C) on the same resident inputs ("default" = the
+        library's default launch, split included)
         ("1,1" is row-major order; a third field picks the kernel: i = 4-wave on
         256x256 tiles (default), i128 / i192 = on 128x128 / 192x192 tiles, p =
         ping-pong, l = lockstep); used to choose the library's default (W, C)
@@ -56,9 +57,10 @@ EQ1_LLC_BW_TBS = 5.99
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0}   # MI355X dense MFMA peaks
 # HipKittens 8-wave 0P/8C bf16 GEMM at 8192^3 on MI355X (HipKittens L2 note, Table 2 / Q3)
 PAGES_BF16_8192_TFLOPS = 1610.0
+# the sources that decide what a default launch runs: the kernels and the
+# launch planning (not the cache model or the autotuner, which only advise)
 KERNEL_SOURCES = ("dense_gemm_fp8_amd/csrc/gemm_kernels.hip", "dense_gemm_fp8_amd/csrc/remap.h",
-                  "dense_gemm_fp8_amd/csrc/kernels.h", "dense_gemm_fp8_amd/csrc/hkg_api.cpp",
-                  "dense_gemm_fp8_amd/csrc/remap_model.h", "dense_gemm_fp8_amd/csrc/remap_model.cpp")
+                  "dense_gemm_fp8_amd/csrc/kernels.h", "dense_gemm_fp8_amd/csrc/hkg_api.cpp")
 
 
 def _strip_comments(text: str) -> str:
@@ -209,7 +211,8 @@ def launch_plan(w: synth.Workload, opts) -> list:
 
 
 def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
-              with_cpu: bool, deadline_s: float = 120.0, settle_ms: float = 200.0) -> dict:
+              with_cpu: bool, deadline_s: float = 120.0, settle_ms: float = 200.0,
+              tune: bool = False) -> dict:
     import torch
     import dense_gemm_fp8_amd as hkg
 
@@ -231,6 +234,15 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
         pSA = hkg.mx_pack_scales(dSA, hkg.HKG_MX_OPERAND_A, stream=stream)
         pSB = hkg.mx_pack_scales(dSB, hkg.HKG_MX_OPERAND_B, stream=stream)
 
+    tuned = None
+    if tune:
+        # the library's autotuner picks the grid order on these buffers first
+        if w.dtype == "mxfp8":
+            raise ValueError("--tune times bf16 and e4m3 (MXFP8 takes the e4m3 order)")
+        opts, tuned_ms, tried = hkg.tune_remap(dA, dB, C, launches=10, stream=stream)
+        tuned = {"remap": opts.remap, "W": opts.W, "C": opts.C, "ms_per_launch": round(tuned_ms, 5),
+                 "tried": [{"remap": o.remap, "W": o.W, "C": o.C, "ms": round(t, 5)}
+                           for o, t in tried]}
     # the kernels' own time record on every timed launch (8 words per workgroup)
     plan = launch_plan(w, opts)
     wgs = sum(d["workgroups"] for d in plan)
@@ -351,6 +363,7 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
                                 " step includes packing both scale arrays)"}[w.dtype],
                    "schedule": sched_name,
                    "remap": ({"remap": opts.remap, "W": opts.W, "C": opts.C} if opts else "default"),
+                   "tuned": tuned,
                    "launches": plan},
         "fraction_of_peak": round(tflops / peak, 4),
         "roofline": {
@@ -438,7 +451,9 @@ def sweep(w: synth.Workload, pairs, steps: int, warmup: int) -> None:
               "i192": hkg.HKG_SCHED_INTERLEAVE_192}
 
     def run(W, Cc, n, sc="i"):
-        opts = hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=W, C=Cc, schedule=scheds[sc])
+        # "default" (W) = the library's default launch, split included
+        opts = None if W == "default" else hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=W, C=Cc,
+                                                         schedule=scheds[sc])
         for _ in range(n):
             if w.dtype == "bf16":
                 hkg.gemm_bf16(dA, dB, C, opts=opts, stream=stream)
@@ -469,7 +484,7 @@ def sweep(w: synth.Workload, pairs, steps: int, warmup: int) -> None:
         ms = float(np.mean(times[key]))
         print(json.dumps({"sweep": w.name, "M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype,
                           "W": W, "C": Cc, "schedule": key[2] if len(key) > 2 else "i",
-                          "default": [W, Cc] == [dW, dC],
+                          "default": W == "default" or [W, Cc] == [dW, dC],
                           "ms": round(ms, 5), "ms_runs": [round(t, 5) for t in times[key]],
                           "TFLOPS": round(w.flops / (ms * 1e-3) / 1e12, 2)}), flush=True)
 
@@ -626,6 +641,8 @@ def main(argv=None) -> int:
     ap.add_argument("--clock-ramp", type=int, default=0, metavar="N",
                     help="time N default launches after 2 s of idle, each with the time record, "
                          "and print the clock per window of launches")
+    ap.add_argument("--tune", action="store_true",
+                    help="pick the grid order with the library's autotuner (hkg_tune_remap) first")
     ap.add_argument("--settle-ms", type=float, default=200.0,
                     help="untimed steps (ms of wall time) between a first W + K measurement from "
                          "idle and the W + K measurement reported as value; 0 reports the first")
@@ -670,7 +687,8 @@ def main(argv=None) -> int:
         return 0
     if args.sweep:
         w = custom_workload(args.shape, args.dtype) if args.shape else synth.workload(args.workload)
-        pairs = [tuple(int(v) if v.isdigit() else v for v in item.split(","))
+        pairs = [("default", 0) if item == "default" else
+                 tuple(int(v) if v.isdigit() else v for v in item.split(","))
                  for item in args.sweep.split()]
         sweep(w, pairs, args.steps, args.warmup)
         return 0
@@ -680,7 +698,7 @@ def main(argv=None) -> int:
         steps = args.steps
         res = bench_one(w, steps, args.warmup, opts, args.schedule,
                         with_cpu=(not args.no_cpu_baseline), deadline_s=args.deadline,
-                        settle_ms=args.settle_ms)
+                        settle_ms=args.settle_ms, tune=args.tune and opts is None)
         print(json.dumps(res), flush=True)
     return 0
 

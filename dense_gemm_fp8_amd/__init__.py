@@ -59,6 +59,8 @@ EXPORTS = (
     "hkg_default_remap",
     "hkg_launch_plan",
     "hkg_remap_model",
+    "hkg_remap_candidates",
+    "hkg_tune_remap",
     "hkg_remap_tile",
     "hkg_remap_tiles_device",
     "hkg_probe_xcd",
@@ -123,6 +125,10 @@ def load() -> ctypes.CDLL:
                             ctypes.POINTER(hkg_launch_plan_t)],
         "hkg_remap_model": [i64, i64, i32, i32, i64, i32, ctypes.POINTER(ctypes.c_double),
                             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
+        "hkg_remap_candidates": [i64, i64, i64, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                 ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)],
+        "hkg_tune_remap": [i64, i64, i64, i32, p, p, p, i32, popts, ctypes.POINTER(f32), popts,
+                           ctypes.POINTER(f32), ctypes.POINTER(i32), p],
         "hkg_remap_tile": [i64, i64, i32, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)],
         "hkg_remap_tiles_device": [i64, i64, i32, i32, p, p],
         "hkg_probe_xcd": [i64, i32, i32, p, p],
@@ -199,6 +205,33 @@ def hkg_remap_model(Gm, Gn, W, C, panel_bytes, per_xcd=32):
     rc = load().hkg_remap_model(Gm, Gn, W, C, panel_bytes, per_xcd, ctypes.byref(l2),
                                 ctypes.byref(llc), ctypes.byref(bw))
     return rc, l2.value, llc.value, bw.value
+
+
+def hkg_remap_candidates(M, N, K, dtype, max_out=48):
+    """-> (status, [(W, C, eq1_bw_tbs), ...] best first, count)."""
+    W = (ctypes.c_int32 * max(max_out, 1))()
+    C = (ctypes.c_int32 * max(max_out, 1))()
+    bw = (ctypes.c_double * max(max_out, 1))()
+    n = ctypes.c_int32()
+    rc = load().hkg_remap_candidates(M, N, K, dtype, max_out, W, C, bw, ctypes.byref(n))
+    got = min(n.value, max_out) if rc == HKG_OK else 0
+    return rc, [(W[i], C[i], bw[i]) for i in range(got)], n.value
+
+
+HKG_TUNE_MAX_CANDIDATES = 8
+
+
+def hkg_tune_remap(M, N, K, dtype, A, B, C, launches, best, stream):
+    """-> (status, best_ms, [(opts, ms) of every configuration timed]); fills
+    the hkg_gemm_opts `best`."""
+    ms = ctypes.c_float()
+    tried = (hkg_gemm_opts * HKG_TUNE_MAX_CANDIDATES)()
+    tried_ms = (ctypes.c_float * HKG_TUNE_MAX_CANDIDATES)()
+    n = ctypes.c_int32()
+    rc = load().hkg_tune_remap(M, N, K, dtype, A, B, C, launches, ctypes.byref(best),
+                               ctypes.byref(ms), tried, tried_ms, ctypes.byref(n), stream)
+    got = n.value if rc == HKG_OK else 0
+    return rc, ms.value, [(tried[i], tried_ms[i]) for i in range(got)]
 
 
 def hkg_remap_tile(Gm, Gn, W, C, b):
@@ -350,6 +383,36 @@ def gemm_mxfp8(A, B, SA_packed, SB_packed, C=None, C_f32=None, opts=None, stream
     if rc != HKG_OK:
         raise HkgError(rc, "hkg_gemm_mxfp8_ex")
     return C
+
+
+def tune_remap(A, B, C=None, launches=10, stream=None):
+    """Time the candidate grid orders of C = A·Bᵀ on these GPU tensors (bf16, or
+    e4m3 bytes timed with unit scales) and return (opts, ms, tried): the fastest
+    as hkg_gemm_opts for gemm_bf16 / gemm_fp8 / gemm_mxfp8, its time per launch,
+    and (opts, ms) of every configuration timed (the default launch first).
+    C (allocated if None) is overwritten with the product."""
+    import torch
+    if A.dtype == torch.bfloat16 and B.dtype == torch.bfloat16:
+        dtype = 0
+    elif A.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)) and \
+            B.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+        dtype = 1
+    else:
+        raise TypeError("A and B must both be bfloat16 or both hold e4m3 bytes")
+    M, K = A.shape
+    N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("A is [M,K] and B is [N,K]")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    if tuple(C.shape) != (M, N) or C.dtype != torch.bfloat16:
+        raise ValueError("C must be a [M,N] bfloat16 tensor")
+    best = hkg_gemm_opts()
+    rc, ms, tried = hkg_tune_remap(M, N, K, dtype, _dev_ptr(A, "A"), _dev_ptr(B, "B"),
+                                   _dev_ptr(C, "C"), launches, best, _stream_handle(stream))
+    if rc != HKG_OK:
+        raise HkgError(rc, "hkg_tune_remap")
+    return best, ms, tried
 
 
 def remap_tiles_device(Gm, Gn, W, C, stream=None):

@@ -10,13 +10,16 @@
 #include <atomic>
 
 #include "../../include/hkg.h"
+#include "api_internal.h"
 #include "kernels.h"
 #include "remap.h"
 #include "remap_model.h"
 
-namespace {
+namespace hkg::api {
 
 thread_local int g_last_hip_error = 0;
+
+void set_last_hip_error(int e) { g_last_hip_error = e; }
 
 // Whether a device is a gfx950, cached per device ordinal (0 = not yet
 // asked, 1 = gfx950, -1 = another architecture).  The kernels are built for
@@ -65,8 +68,6 @@ int prepare_launch(void *stream)
 constexpr int64_t kTile = 256;
 constexpr int64_t kKStepBf16 = 64;     // K elements per step (one 128-byte LDS row)
 constexpr int64_t kKStepFp8 = 128;
-constexpr int64_t kKAlignBf16 = 8;     // K granule: operand rows stay 16-byte aligned
-constexpr int64_t kKAlignFp8 = 16;
 constexpr int64_t kKAlignMx = 32;      // one E8M0 scale per 32 elements along K
 constexpr int64_t kMxGroupRows = 128;  // packed scales: 128-row groups ...
 constexpr int64_t kMxStepBytes = 512;  // ... of 64 lanes x 8 bytes per K step
@@ -421,7 +422,9 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
     return HKG_OK;
 }
 
-}  // namespace
+}  // namespace hkg::api
+
+using namespace hkg::api;
 
 extern "C" {
 

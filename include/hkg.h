@@ -24,7 +24,9 @@
  * Conventions for every entry point:
  *  - Pointers named A, B, C, C_f32 are DEVICE pointers allocated, owned and
  *    freed by the caller; the library never allocates, frees, copies to the
- *    host or synchronises.  Work is enqueued on `stream` (a hipStream_t;
+ *    host or synchronises (the one exception is the autotuner,
+ *    hkg_tune_remap, which creates, waits for and destroys two HIP events).
+ *    Work is enqueued on `stream` (a hipStream_t;
  *    NULL = the default stream) and completes asynchronously; buffers must
  *    stay alive until the stream has passed the kernel.
  *  - All arguments are validated before any HIP call.  On a validation error
@@ -290,6 +292,61 @@ int hkg_launch_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, const hkg_ge
  */
 int hkg_remap_model(int64_t Gm, int64_t Gn, int32_t W, int32_t C, int64_t panel_bytes,
                     int32_t per_xcd, double *l2_hit, double *llc_hit, double *eq1_bw_tbs);
+
+/*
+ * Candidate grid orders of a shape, best first by the cache model's Eq. 1
+ * bandwidth (HipKittens L2 note, section 4 equation; section 5 Table 4 tunes W
+ * and C per shape).  Host only, no HIP call.  The grid is the one the default
+ * schedule picks for the shape (tiles of 256, 192 or 128, one launch); the
+ * candidates are W in {1, 2, 4, 8, 16, 32} x C in {1, 2, 4, 8, 16, 32, 64,
+ * 128}, clamped to the grid as hkg_remap_model clamps them and with duplicates
+ * removed (at most 48), ranked by eq1_bw_tbs of hkg_remap_model (ties keep that
+ * enumeration order).  Writes the first min(max, count) entries to W[i], C[i],
+ * eq1_bw_tbs[i] and the number of candidates to *count (0 for M == 0 or
+ * N == 0).  dtype: 0 = bf16, 1 = e4m3, 2 = MXFP8.  Returns HKG_ERR_NULL for a
+ * NULL pointer (W, C, eq1_bw_tbs may be NULL when max == 0), HKG_ERR_SHAPE as
+ * hkg_launch_plan does, HKG_ERR_SIZE for grids the entry points refuse.
+ */
+int hkg_remap_candidates(int64_t M, int64_t N, int64_t K, int32_t dtype, int32_t max,
+                         int32_t *W, int32_t *C, double *eq1_bw_tbs, int32_t *count);
+
+/*
+ * Grid-order autotuner (HipKittens L2 note, section 5 Table 4: the order is
+ * tuned per shape).  Times, on the caller's buffers and stream, the default
+ * launch of this GEMM and, with the default schedule, the best-ranked order of
+ * hkg_remap_candidates for each window height W that occurs in that list (at
+ * most 6; the model often ties orders that differ only in C) plus row-major
+ * order if it is not among them, and returns the fastest as options for the
+ * _ex entry points.
+ *   dtype     0 = bf16, 1 = e4m3 (MXFP8 moves the same operand bytes as e4m3:
+ *             tune it with dtype 1 on its element arrays)
+ *   A, B, C   as for hkg_gemm_bf16 / hkg_gemm_fp8 (same checks); C is
+ *             overwritten, every time with the product A·Bᵀ (unit scales for e4m3)
+ *   launches  timed launches per candidate and pass, 1 .. 1000
+ *   best      out: {HKG_REMAP_DEFAULT, default W, default C, HKG_SCHED_DEFAULT,
+ *             NULL} when the default launch won, else {HKG_REMAP_ROW_MAJOR or
+ *             HKG_REMAP_XCD, W, C, HKG_SCHED_DEFAULT, NULL}
+ *   best_ms   out (may be NULL): the winner's mean time per launch, ms
+ *   tried, tried_ms, n_tried
+ *             out (all NULL, or arrays of HKG_TUNE_MAX_CANDIDATES entries and
+ *             a count): every configuration timed, the default launch first,
+ *             with its mean time per launch, ms
+ * Procedure: about 100 ms of default launches first (the clock of an idle GPU
+ * takes that long to settle under its power cap), then every candidate is
+ * timed twice, in forward and then reverse order, each time after one untimed
+ * launch, with HIP events on `stream`.  Unlike the GEMM entry points this call
+ * creates two HIP events, waits for them on the host and destroys them; it
+ * returns when its last launch has finished.  M == 0 or N == 0: no launch,
+ * best = the defaults, *best_ms = 0, *n_tried = 0.  Returns the entry points'
+ * status codes, plus HKG_ERR_NULL for best == NULL or for only some of tried,
+ * tried_ms, n_tried given, HKG_ERR_SHAPE for another dtype and
+ * HKG_ERR_OPTS for launches outside 1 .. 1000; on HKG_ERR_LAUNCH (event or
+ * launch failure, see hkg_last_hip_error) `best` is left unchanged.
+ */
+#define HKG_TUNE_MAX_CANDIDATES 8
+int hkg_tune_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A, const void *B,
+                   void *C, int32_t launches, hkg_gemm_opts *best, float *best_ms,
+                   hkg_gemm_opts *tried, float *tried_ms, int32_t *n_tried, void *stream);
 
 /*
  * The grid remap itself (HipKittens L2 note, section 7 Algorithm 1 reading): flat

@@ -22,7 +22,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = hkg.load()
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 18
     assert sorted(hkg.EXPORTS) == names
     for n in names:
         assert getattr(lib, n) is not None
@@ -396,3 +396,76 @@ def test_remap_model_closed_forms():
     assert l2 == 0.0 and llc == 0.0
     assert hkg.hkg_remap_model(0, 4, 1, 1, 1, 32)[0] == hkg.HKG_ERR_SHAPE
     assert hkg.hkg_remap_model(4, 4, 0, 1, 1, 32)[0] == hkg.HKG_ERR_SHAPE
+
+
+def test_remap_candidates_are_the_model_ranked_orders():
+    """hkg_remap_candidates: every clamped, distinct (W, C) of the default
+    schedule's grid, best first by the model's Eq. 1 bandwidth, each entry equal
+    to hkg_remap_model for that order."""
+    for M, N, K, dt, tile, per in ((14592, 14592, 14592, 0, 256, 32), (8192, 8192, 8192, 1, 256, 32),
+                                   (2048, 2048, 2048, 0, 128, 64), (16384, 14336, 4096, 0, 256, 32),
+                                   (3072, 3072, 1024, 0, 192, 32)):
+        rc, L, n = hkg.hkg_remap_candidates(M, N, K, dt)
+        assert rc == hkg.HKG_OK and n == len(L) and 0 < n <= 48
+        assert len(set((w, c) for w, c, _ in L)) == n
+        bws = [b for _, _, b in L]
+        assert bws == sorted(bws, reverse=True)
+        Gm, Gn = -(-M // tile), -(-N // tile)
+        elem = 2 if dt == 0 else 1
+        for w, c, b in L:
+            assert 1 <= w <= Gm and 1 <= c
+            rc, l2, llc, bw = hkg.hkg_remap_model(Gm, Gn, w, c, tile * K * elem, per)
+            assert rc == hkg.HKG_OK and bw == pytest.approx(b)
+        # every enumerated window height, clamped to the grid's tile rows, occurs
+        assert set(min(w, Gm) for w in (1, 2, 4, 8, 16, 32)) == set(w for w, _, _ in L)
+    # at 14592 the top order is the one the measured rule picks there
+    rc, L, n = hkg.hkg_remap_candidates(14592, 14592, 14592, 0)
+    assert L[0][:2] == (16, 4) and hkg.hkg_default_remap(14592, 14592, 14592, 0)[1:] == (16, 4)
+    # truncation, empty shapes, bad input
+    rc, L, n = hkg.hkg_remap_candidates(8192, 8192, 8192, 0, 3)
+    assert rc == hkg.HKG_OK and len(L) == 3 and n > 3
+    assert hkg.hkg_remap_candidates(0, 100, 64, 0)[::2] == (hkg.HKG_OK, 0)
+    assert hkg.hkg_remap_candidates(100, 100, 60, 1)[0] == hkg.HKG_ERR_SHAPE
+    assert hkg.hkg_remap_candidates(100, 100, 64, 3)[0] == hkg.HKG_ERR_SHAPE
+    n = ctypes.c_int32()
+    assert hkg.load().hkg_remap_candidates(100, 100, 64, 0, 4, None, None, None,
+                                           ctypes.byref(n)) == hkg.HKG_ERR_NULL
+    assert hkg.load().hkg_remap_candidates(100, 100, 64, 0, 0, None, None, None,
+                                           ctypes.byref(n)) == hkg.HKG_OK and n.value > 0
+
+
+def test_tune_remap_validates_before_any_hip_call():
+    best = hkg.hkg_gemm_opts()
+    lib = hkg.load()
+    T = lambda *a: hkg.hkg_tune_remap(*a)[0]
+    assert lib.hkg_tune_remap(256, 256, 256, 0, FAKE, FB, FC, 5, None, None, None, None, None,
+                              None) == hkg.HKG_ERR_NULL
+    ms = ctypes.c_float()
+    assert lib.hkg_tune_remap(256, 256, 256, 0, FAKE, FB, FC, 5, ctypes.byref(best), None, None,
+                              ctypes.byref(ms), None, None) == hkg.HKG_ERR_NULL   # partial report
+    assert T(256, 256, 256, 2, FAKE, FB, FC, 5, best, None) == hkg.HKG_ERR_SHAPE   # MXFP8: tune as e4m3
+    assert T(256, 256, 255, 0, FAKE, FB, FC, 5, best, None) == hkg.HKG_ERR_SHAPE
+    assert T(256, 256, 256, 0, None, FB, FC, 5, best, None) == hkg.HKG_ERR_NULL
+    assert T(256, 256, 256, 0, FAKE + 8, FB, FC, 5, best, None) == hkg.HKG_ERR_ALIGN
+    assert T(256, 256, 256, 0, FAKE, FB, FAKE, 5, best, None) == hkg.HKG_ERR_OVERLAP
+    assert T(256, 256, 256, 0, FAKE, FB, FC, 0, best, None) == hkg.HKG_ERR_OPTS
+    assert T(256, 256, 256, 1, FAKE, FB, FC, 1001, best, None) == hkg.HKG_ERR_OPTS
+    # an empty product launches nothing and returns the defaults
+    best.remap = 7
+    rc, ms, tried = hkg.hkg_tune_remap(0, 256, 256, 0, None, None, None, 5, best, None)
+    assert rc == hkg.HKG_OK and ms == 0.0 and best.remap == hkg.HKG_REMAP_DEFAULT and tried == []
+
+
+def test_tune_remap_without_a_gfx950_is_a_device_error():
+    """Valid arguments reach the device check, which fails without a gfx950, and
+    `best` stays as it was."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    best = hkg.make_opts(remap=hkg.HKG_REMAP_XCD, W=3, C=5)
+    rc, ms, tried = hkg.hkg_tune_remap(256, 256, 256, 0, FAKE, FB, FC, 5, best, None)
+    assert rc == hkg.HKG_ERR_DEVICE and tried == []
+    assert (best.remap, best.W, best.C) == (hkg.HKG_REMAP_XCD, 3, 5)

@@ -817,3 +817,50 @@ def test_concurrent_streams_independent():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(_host_bits(C1), want1)
     np.testing.assert_array_equal(_host_bits(C2), want2)
+
+
+# ------------------------------------------------------------- autotuner ------------
+
+@pytest.mark.parametrize("dtype,M,N,K", [("bf16", 4096, 4096, 512), ("fp8", 3000, 5000, 512),
+                                         ("bf16", 4352, 4352, 256)])
+def test_tune_remap_returns_a_timed_order_and_leaves_a_valid_product(dtype, M, N, K):
+    """hkg_tune_remap: returns a default / row-major / XCD order with a positive
+    time, leaves the product A·Bᵀ (unit scales for e4m3) in C, and the order it
+    returns gives the same output, bit for bit, as the default launch.  4352^2
+    takes the default split (two launches), which the tuner times as one
+    candidate."""
+    _say("tune_remap %s %dx%dx%d" % (dtype, M, N, K))
+    rng = np.random.default_rng(9700 + M)
+    x, y = synth.normal_f32(9701 + M, M, K), synth.normal_f32(9702 + N, N, K)
+    if dtype == "bf16":
+        A, B = synth.f32_to_bf16_bits(x), synth.f32_to_bf16_bits(y)
+        dA, dB = _dev_bf16(A), _dev_bf16(B)
+        run = lambda C, o: hkg.gemm_bf16(dA, dB, C, opts=o)
+    else:
+        (A, _), (B, _) = synth.e4m3_quantize(x), synth.e4m3_quantize(y)
+        dA, dB = _dev_u8(A), _dev_u8(B)
+        run = lambda C, o: hkg.gemm_fp8(dA, dB, 1.0, 1.0, C, opts=o)
+    Ct = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    best, ms, tried = hkg.tune_remap(dA, dB, Ct, launches=3)
+    torch.cuda.synchronize()
+    assert ms > 0 and 2 <= len(tried) <= hkg.HKG_TUNE_MAX_CANDIDATES
+    assert tried[0][0].remap == hkg.HKG_REMAP_DEFAULT
+    assert ms == min(t for _, t in tried)
+    assert any((o.remap, o.W, o.C) == (best.remap, best.W, best.C) for o, _ in tried)
+    assert best.schedule == hkg.HKG_SCHED_DEFAULT and not best.trace
+    assert best.remap in (hkg.HKG_REMAP_DEFAULT, hkg.HKG_REMAP_ROW_MAJOR, hkg.HKG_REMAP_XCD)
+    assert best.W >= 1 and best.C >= 1
+    Cd = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    Cb = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    run(Cd, None)
+    run(Cb, best)
+    torch.cuda.synchronize()
+    want = _host_bits(Cd)
+    assert not np.any(np.isnan(bf16_to_f64(want)))
+    assert np.array_equal(_host_bits(Ct), want)
+    assert np.array_equal(_host_bits(Cb), want)
+    if dtype == "bf16":   # and it is the product: sampled entries against the oracle
+        pm, pn = rng.integers(0, M, 2000), rng.integers(0, N, 2000)
+        ref = oracle.gemm_bf16_pairs(A, B, pm, pn)
+        assert np.all(np.abs(bf16_to_f64(want[pm, pn]) - ref) <=
+                      1e-3 * np.sqrt(K) + np.abs(ref) * 2.0 ** -8)
