@@ -212,7 +212,7 @@ def launch_plan(w: synth.Workload, opts) -> list:
 
 def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
               with_cpu: bool, deadline_s: float = 120.0, settle_ms: float = 200.0,
-              tune: bool = False) -> dict:
+              tune: bool = False, pad_k: int = 0) -> dict:
     import torch
     import dense_gemm_fp8_amd as hkg
 
@@ -224,6 +224,14 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
     else:
         dA = torch.from_numpy(A).to(dev)
         dB = torch.from_numpy(B).to(dev)
+    if pad_k:
+        # operand rows pad_k elements longer than K: the GEMM reads views with
+        # that row pitch (lda = ldb = K + pad_k)
+        def padded(t):
+            big = torch.zeros((t.shape[0], t.shape[1] + pad_k), dtype=t.dtype, device=dev)
+            big[:, :t.shape[1]] = t
+            return big[:, :t.shape[1]]
+        dA, dB = padded(dA), padded(dB)
     C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
     if w.dtype == "mxfp8":
@@ -364,6 +372,7 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
                    "schedule": sched_name,
                    "remap": ({"remap": opts.remap, "W": opts.W, "C": opts.C} if opts else "default"),
                    "tuned": tuned,
+                   "operand_row_pitch": w.K + pad_k,
                    "launches": plan},
         "fraction_of_peak": round(tflops / peak, 4),
         "roofline": {
@@ -641,6 +650,8 @@ def main(argv=None) -> int:
     ap.add_argument("--clock-ramp", type=int, default=0, metavar="N",
                     help="time N default launches after 2 s of idle, each with the time record, "
                          "and print the clock per window of launches")
+    ap.add_argument("--pad-k", type=int, default=0,
+                    help="lay A and B out with rows this many elements longer than K (row pitch)")
     ap.add_argument("--tune", action="store_true",
                     help="pick the grid order with the library's autotuner (hkg_tune_remap) first")
     ap.add_argument("--settle-ms", type=float, default=200.0,
@@ -698,7 +709,8 @@ def main(argv=None) -> int:
         steps = args.steps
         res = bench_one(w, steps, args.warmup, opts, args.schedule,
                         with_cpu=(not args.no_cpu_baseline), deadline_s=args.deadline,
-                        settle_ms=args.settle_ms, tune=args.tune and opts is None)
+                        settle_ms=args.settle_ms, tune=args.tune and opts is None,
+                        pad_k=args.pad_k)
         print(json.dumps(res), flush=True)
     return 0
 

@@ -71,7 +71,8 @@ EXPORTS = (
 
 class hkg_gemm_opts(ctypes.Structure):
     _fields_ = [("remap", ctypes.c_int32), ("W", ctypes.c_int32), ("C", ctypes.c_int32),
-                ("schedule", ctypes.c_int32), ("trace", ctypes.c_void_p)]
+                ("schedule", ctypes.c_int32), ("trace", ctypes.c_void_p),
+                ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldc", ctypes.c_int64)]
 
 
 class hkg_launch_plan_t(ctypes.Structure):
@@ -263,12 +264,13 @@ status_string = hkg_status_string
 # ---- torch marshalling helpers ------------------------------------------------------
 
 def make_opts(remap=HKG_REMAP_DEFAULT, W=0, C=0, schedule=HKG_SCHED_DEFAULT,
-              trace=None) -> hkg_gemm_opts:
+              trace=None, lda=0, ldb=0, ldc=0) -> hkg_gemm_opts:
     """Options of the _ex entry points; trace: None or a device pointer (int) /
-    uint64 GPU tensor for the per-workgroup time record."""
+    uint64 GPU tensor for the per-workgroup time record; lda / ldb / ldc: row
+    pitches in elements (0 = dense)."""
     if trace is not None and not isinstance(trace, int):
         trace = _dev_ptr(trace, "trace")
-    return hkg_gemm_opts(remap, W, C, schedule, trace)
+    return hkg_gemm_opts(remap, W, C, schedule, trace, lda, ldb, ldc)
 
 
 def _stream_handle(stream) -> int:
@@ -287,8 +289,58 @@ def _dev_ptr(t, name):
     return t.data_ptr()
 
 
+def _matrix(t, name):
+    """(device pointer, row pitch in elements) of a 2-D GPU tensor whose rows are
+    contiguous (stride 1 along the row); the pitch is its row stride, which may
+    exceed the row length (a view of a wider matrix, or padded rows)."""
+    if t is None:
+        return None, 0
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    rows, cols = t.shape
+    if t.is_contiguous():
+        return t.data_ptr(), cols
+    if t.stride(1) != 1 or t.stride(0) < cols:
+        raise ValueError("%s must have contiguous rows (stride 1 along a row)" % name)
+    return t.data_ptr(), t.stride(0)
+
+
+def _operands(A, B, C, C_f32, opts, M, N, K):
+    """Pointers of A, B, C, C_f32 and the options with their row pitches."""
+    pA, lda = _matrix(A, "A")
+    pB, ldb = _matrix(B, "B")
+    pC, ldc = _matrix(C, "C")
+    pF, ldf = _matrix(C_f32, "C_f32")
+    if C_f32 is not None and ldf != ldc:
+        raise ValueError("C and C_f32 must have the same row pitch")
+    return pA, pB, pC, pF, _with_pitches(opts, lda, ldb, ldc, dict(lda=K, ldb=K, ldc=N))
+
+
+def _with_pitches(opts, lda, ldb, ldc, dense):
+    """opts with the tensors' row pitches filled in where opts leaves them 0;
+    None when every pitch is the dense one and no opts were given."""
+    want = dict(lda=lda, ldb=ldb, ldc=ldc)
+    if opts is None:
+        if all(want[k] == dense[k] for k in want):
+            return None
+        opts = make_opts()
+    out = hkg_gemm_opts(opts.remap, opts.W, opts.C, opts.schedule, opts.trace, opts.lda, opts.ldb,
+                        opts.ldc)
+    for k, v in want.items():
+        given = getattr(out, k)
+        if given == 0:
+            setattr(out, k, v)
+        elif v != dense[k] and given != v:
+            raise ValueError("opts.%s = %d disagrees with the tensor's row stride %d" % (k, given, v))
+    return out
+
+
 def gemm_bf16(A, B, C=None, C_f32=None, opts=None, stream=None):
-    """C[M,N] (bf16) = A[M,K] · B[N,K]ᵀ for bf16 GPU tensors; returns C."""
+    """C[M,N] (bf16) = A[M,K] · B[N,K]ᵀ for bf16 GPU tensors; returns C.  Each
+    2-D tensor needs contiguous rows; a row stride beyond the row length (a view
+    of a wider matrix, or padded rows) is passed as its pitch (lda / ldb / ldc)."""
     import torch
     if A.dtype != torch.bfloat16 or B.dtype != torch.bfloat16:
         raise TypeError("A and B must be torch.bfloat16")
@@ -302,8 +354,8 @@ def gemm_bf16(A, B, C=None, C_f32=None, opts=None, stream=None):
         raise ValueError("C must be a [M,N] bfloat16 tensor")
     if C_f32 is not None and (tuple(C_f32.shape) != (M, N) or C_f32.dtype != torch.float32):
         raise ValueError("C_f32 must be a [M,N] float32 tensor")
-    rc = hkg_gemm_bf16_ex(M, N, K, _dev_ptr(A, "A"), _dev_ptr(B, "B"), _dev_ptr(C, "C"),
-                          _dev_ptr(C_f32, "C_f32"), _stream_handle(stream), opts)
+    pA, pB, pC, pF, opts = _operands(A, B, C, C_f32, opts, M, N, K)
+    rc = hkg_gemm_bf16_ex(M, N, K, pA, pB, pC, pF, _stream_handle(stream), opts)
     if rc != HKG_OK:
         raise HkgError(rc, "hkg_gemm_bf16_ex")
     return C
@@ -311,7 +363,8 @@ def gemm_bf16(A, B, C=None, C_f32=None, opts=None, stream=None):
 
 def gemm_fp8(A, B, scale_a, scale_b, C=None, C_f32=None, opts=None, stream=None):
     """C[M,N] (bf16) = bf16(sa·sb · A[M,K] · B[N,K]ᵀ) for e4m3 code tensors
-    (torch.uint8 or torch.float8_e4m3fn) on the GPU; returns C."""
+    (torch.uint8 or torch.float8_e4m3fn) on the GPU; returns C.  Row strides
+    become pitches as in gemm_bf16."""
     import torch
     ok = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
     if A.dtype not in ok or B.dtype not in ok:
@@ -326,8 +379,8 @@ def gemm_fp8(A, B, scale_a, scale_b, C=None, C_f32=None, opts=None, stream=None)
         raise ValueError("C must be a [M,N] bfloat16 tensor")
     if C_f32 is not None and (tuple(C_f32.shape) != (M, N) or C_f32.dtype != torch.float32):
         raise ValueError("C_f32 must be a [M,N] float32 tensor")
-    rc = hkg_gemm_fp8_ex(M, N, K, _dev_ptr(A, "A"), _dev_ptr(B, "B"), float(scale_a),
-                         float(scale_b), _dev_ptr(C, "C"), _dev_ptr(C_f32, "C_f32"),
+    pA, pB, pC, pF, opts = _operands(A, B, C, C_f32, opts, M, N, K)
+    rc = hkg_gemm_fp8_ex(M, N, K, pA, pB, float(scale_a), float(scale_b), pC, pF,
                          _stream_handle(stream), opts)
     if rc != HKG_OK:
         raise HkgError(rc, "hkg_gemm_fp8_ex")
@@ -377,9 +430,9 @@ def gemm_mxfp8(A, B, SA_packed, SB_packed, C=None, C_f32=None, opts=None, stream
         raise ValueError("C must be a [M,N] bfloat16 tensor")
     if C_f32 is not None and (tuple(C_f32.shape) != (M, N) or C_f32.dtype != torch.float32):
         raise ValueError("C_f32 must be a [M,N] float32 tensor")
-    rc = hkg_gemm_mxfp8_ex(M, N, K, _dev_ptr(A, "A"), _dev_ptr(B, "B"),
-                           _dev_ptr(SA_packed, "SA_packed"), _dev_ptr(SB_packed, "SB_packed"),
-                           _dev_ptr(C, "C"), _dev_ptr(C_f32, "C_f32"), _stream_handle(stream), opts)
+    pA, pB, pC, pF, opts = _operands(A, B, C, C_f32, opts, M, N, K)
+    rc = hkg_gemm_mxfp8_ex(M, N, K, pA, pB, _dev_ptr(SA_packed, "SA_packed"),
+                           _dev_ptr(SB_packed, "SB_packed"), pC, pF, _stream_handle(stream), opts)
     if rc != HKG_OK:
         raise HkgError(rc, "hkg_gemm_mxfp8_ex")
     return C

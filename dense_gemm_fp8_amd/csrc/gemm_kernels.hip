@@ -160,19 +160,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 
 constexpr int kOutOfRange = int(0x80000000u);   // voffset past any panel's range
 
-// voffset for K step k: the lane's own offset, or out of range if its chunk
-// (at byte cbytes of the K step) lies past the row's ldk bytes.
-__device__ __forceinline__ int kstep_voff(int voff, int cbytes, int k, int ldk)
+// Byte range of a panel of `rows` operand rows `pitch` bytes apart, each
+// holding kb bytes of K: it ends with the last row's K bytes, so loads past
+// them (a partial K step's lanes, or the padding after the last row) read
+// zeros.
+__device__ __forceinline__ uint32_t panel_bytes(int rows, int pitch, int kb)
 {
-    return k * kRowBytes + cbytes < ldk ? voff : kOutOfRange;
+    return rows > 0 ? (uint32_t)(rows - 1) * (uint32_t)pitch + (uint32_t)kb : 0u;
 }
 
-// One wave-wide HBM->LDS load of 8 panel rows (u = row group, 0..31).
+// voffset for K step k: the lane's own offset, or out of range if its chunk
+// (at byte cbytes of the K step) lies past the row's kb bytes of K.
+__device__ __forceinline__ int kstep_voff(int voff, int cbytes, int k, int kb)
+{
+    return k * kRowBytes + cbytes < kb ? voff : kOutOfRange;
+}
+
+// One wave-wide HBM->LDS load of 8 panel rows (u = row group, 0..31) of an
+// operand whose rows are `pitch` bytes apart.
 __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, char *panel, int u, int voff,
-                                         int soff_kstep, int ldk)
+                                         int soff_kstep, int pitch)
 {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(panel + u * kDmaBytes), 16, voff,
-                                             soff_kstep + u * kDmaRows * ldk, 0, 0);
+                                             soff_kstep + u * kDmaRows * pitch, 0, 0);
 }
 
 // Row groups u = base + (wave & 3) + 4 v, v < count: every lane of a wave
@@ -180,11 +190,11 @@ __device__ __forceinline__ void dma_rows(__amdgpu_buffer_rsrc_t rs, char *panel,
 // offset serves all its loads.
 template <int kCount>
 __device__ __forceinline__ void dma_panel_part(__amdgpu_buffer_rsrc_t rs, char *panel, int base,
-                                               int w4, int voff, int soff_kstep, int ldk)
+                                               int w4, int voff, int soff_kstep, int pitch)
 {
 #pragma unroll
     for (int v = 0; v < kCount; ++v)
-        dma_rows(rs, panel, base + w4 + 4 * v, voff, soff_kstep, ldk);
+        dma_rows(rs, panel, base + w4 + 4 * v, voff, soff_kstep, pitch);
 }
 
 template <int kDtype>
@@ -427,21 +437,22 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, int tm, int tn, 
     const int64_t col0 = (int64_t)tn * kT + col_off + 8 * q;
     const float sc = p.scale;
     uint16_t *C = static_cast<uint16_t *>(p.C);
-    const bool vec = (p.N & 7) == 0;
+    const int64_t ldc = p.ldc;
+    const bool vec = ((p.N | p.ldc) & 7) == 0;   // 16-byte stores of 8 columns
     const bool inside = (tm + 1) * kT <= p.M && (tn + 1) * kT <= p.N && vec;
     // Whole tiles without the fp32 copy (every timed launch): one buffer
     // resource over the wave's 16 kRB rows of C, a lane offset fixed for the
     // whole epilogue, a scalar offset per 16-row block and the 32-column group
     // in the instruction's immediate offset -- no per-store address
     // arithmetic and no branches.  The resource's 32-bit range bounds N.
-    if (inside && !p.C_f32 && (uint64_t)32 * kRB * (uint64_t)p.N < (uint64_t(1) << 32)) {
-        const int64_t origin = ((int64_t)tm * kT + row_off) * p.N + (int64_t)tn * kT + col_off;
+    if (inside && !p.C_f32 && (uint64_t)32 * kRB * (uint64_t)p.ldc < (uint64_t(1) << 32)) {
+        const int64_t origin = ((int64_t)tm * kT + row_off) * ldc + (int64_t)tn * kT + col_off;
         const __amdgpu_buffer_rsrc_t rc =
-            make_rsrc(C + origin, (uint32_t)(32 * kRB) * (uint32_t)p.N);
-        const int voff = ((lane & 15) * p.N + 8 * q) * 2;
+            make_rsrc(C + origin, (uint32_t)(32 * kRB) * (uint32_t)p.ldc);
+        const int voff = ((lane & 15) * p.ldc + 8 * q) * 2;
 #pragma unroll
         for (int i = 0; i < kRB; ++i) {
-            const int soff = __builtin_amdgcn_readfirstlane((int)((uint32_t)(32 * i) * (uint32_t)p.N));
+            const int soff = __builtin_amdgcn_readfirstlane((int)((uint32_t)(32 * i) * (uint32_t)p.ldc));
             if constexpr (kAgpr)
                 pin_row(acc, i);
 #pragma unroll
@@ -465,7 +476,7 @@ __device__ __forceinline__ void store_tile(const GemmParams &p, int tm, int tn, 
             f32x4 lo, hi;
             block_pair<kScale, kAgpr>(acc, i, h, sc, lo, hi);
             const int64_t n0 = col0 + 32 * h;
-            const int64_t off = m * p.N + n0;
+            const int64_t off = m * ldc + n0;
             u32x4 packed = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
                             pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
             if (inside || (vec && n0 < p.N)) {
@@ -537,13 +548,14 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
     remap_tile(blockIdx.x, p.Gm, p.Gn, p.W, p.Cc, tm, tn);
 
     constexpr int kElem = kDtype == kBf16 ? 2 : 1;
-    const int ldk = p.K * kElem;                          // bytes per operand row
+    const int kb = p.K * kElem;                           // bytes of K per operand row
+    const int pa = p.lda * kElem, pb = p.ldb * kElem;     // row pitches in bytes
     const int rows_a = min(kTile, p.M - tm * kTile);      // valid rows of this tile's panels
     const int rows_b = min(kTile, p.N - tn * kTile);
-    const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(static_cast<const char *>(p.A) + (int64_t)tm * kTile * ldk, rows_a * ldk);
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(static_cast<const char *>(p.B) + (int64_t)tn * kTile * ldk, rows_b * ldk);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(
+        static_cast<const char *>(p.A) + (int64_t)tm * kTile * pa, panel_bytes(rows_a, pa, kb));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(
+        static_cast<const char *>(p.B) + (int64_t)tn * kTile * pb, panel_bytes(rows_b, pb, kb));
 
     // This lane's source offsets inside a row group: row 8u + lane/8, slot
     // lane%8; row bits 3,4 equal (u & 3) == w4 for every load this wave
@@ -556,8 +568,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
     // step is whole.  Loads of steps >= nk fetch bytes no MFMA uses (in-range
     // bytes of the panel's next rows, or zeros past its last row) into panels
     // no one reads any more.
-    const int shift = __builtin_amdgcn_readfirstlane(p.nk * kRowBytes - ldk);
-    const int va = r8 * ldk + cb_a, vb = r8 * ldk + cb_b;
+    const int shift = __builtin_amdgcn_readfirstlane(p.nk * kRowBytes - kb);
+    const int va = r8 * pa + cb_a, vb = r8 * pb + cb_b;
     const int va_first = cb_a >= shift ? va - shift : kOutOfRange;
     const int vb_first = cb_b >= shift ? vb - shift : kOutOfRange;
     auto soff = [&](int k) { return k == 0 ? 0 : k * kRowBytes - shift; };
@@ -576,10 +588,10 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
     auto b_off2 = [&](int k) { return kBRing + (k & 1) * kPanelBytes; };
     // this wave's 4 of the 8-row groups u = base + w4 + 4 v of a K step's panel
     auto load_a = [&](int k, int off, int base) {
-        dma_panel_part<4>(ra, smem + off, base, w4, k == 0 ? va_first : va, soff(k), ldk);
+        dma_panel_part<4>(ra, smem + off, base, w4, k == 0 ? va_first : va, soff(k), pa);
     };
     auto load_b = [&](int k, int off, int base) {
-        dma_panel_part<4>(rb, smem + off, base, w4, k == 0 ? vb_first : vb, soff(k), ldk);
+        dma_panel_part<4>(rb, smem + off, base, w4, k == 0 ? vb_first : vb, soff(k), pb);
     };
 
     if (kSched == kLockstep) {
@@ -842,10 +854,10 @@ __device__ __forceinline__ void for_slots(F &&f)
 // ring_off and soff_kstep so that the address arithmetic stays at the call).
 __device__ __forceinline__ void dma_rows_at(__amdgpu_buffer_rsrc_t rs, char *smem, int ring_off,
                                             int fixed_off, int u, int voff, int soff_kstep,
-                                            int ldk)
+                                            int pitch)
 {
     const int m = ring_off + fixed_off + u * kDmaBytes;
-    const int so = soff_kstep + u * kDmaRows * ldk;
+    const int so = soff_kstep + u * kDmaRows * pitch;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(smem + m), 16, voff, so, 0, 0);
 }
 
@@ -1113,6 +1125,7 @@ struct QuadCtx {
     int voff_a, voff_b;              // lane's load offsets (swizzled chunk of its row)
     int cb_a, cb_b;                  // byte of that chunk inside a K step
     int shift;                       // K step k covers row bytes [128 k - shift, +128)
+    int pitch_a, pitch_b;            // row pitches of A and B in bytes
     QuadLane l;
     // MXFP8 only: the packed scales (hkg_mx_pack_scales layout) and the byte
     // offsets of this wave's 128-row groups in them at K step 0
@@ -1166,7 +1179,7 @@ struct Ring {
 template <int kDtype, bool kMasked, int kB>
 __device__ __forceinline__ void quad_step(typename Quad<kDtype, kB>::Frags &f,
                                           f32x4 (&acc)[kB][kB], MxScales &sc, const QuadCtx &c,
-                                          int ldk, int t, int lane, Ring &rg, Bases &bs0)
+                                          int t, int lane, Ring &rg, Bases &bs0)
 {
     using Q = Quad<kDtype, kB>;
     constexpr int kP = 32 * kB * kRowBytes;   // panel bytes (32 kB rows)
@@ -1227,7 +1240,7 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype, kB>::Frags &f,
         [&](int v) {
             pb2 = pin_s(pb2);
             so = pin_s(so);
-            dma_rows_at(c.rb, c.smem, pb2, 2 * kP, c.wave + 4 * v, vb, so, ldk);
+            dma_rows_at(c.rb, c.smem, pb2, 2 * kP, c.wave + 4 * v, vb, so, c.pitch_b);
         },
         [&](auto slot) __attribute__((always_inline)) {
             bases_at(bs1, H1{}, slot);
@@ -1246,7 +1259,7 @@ __device__ __forceinline__ void quad_step(typename Quad<kDtype, kB>::Frags &f,
         [&](int v) {
             pa = pin_s(pa);
             so = pin_s(so);
-            dma_rows_at(c.ra, c.smem, pa, 0, c.wave + 4 * v, va, so, ldk);
+            dma_rows_at(c.ra, c.smem, pa, 0, c.wave + 4 * v, va, so, c.pitch_a);
         },
         [&](auto slot) __attribute__((always_inline)) {
             constexpr int n = decltype(slot)::value;
@@ -1309,24 +1322,28 @@ __global__ __launch_bounds__(256, kT == 128 ? 2 : 1) void gemm4_kernel(const Gem
     remap_tile(blockIdx.x, p.Gm, p.Gn, p.W, p.Cc, tm, tn);
 
     constexpr int kElem = kDtype == kBf16 ? 2 : 1;
-    const int ldk = p.K * kElem;
+    const int kb = p.K * kElem;   // bytes of K per operand row
+    c.pitch_a = p.lda * kElem;
+    c.pitch_b = p.ldb * kElem;
     const int rows_a = min(kT, p.M - tm * kT);
     const int rows_b = min(kT, p.N - tn * kT);
-    c.ra = make_rsrc(static_cast<const char *>(p.A) + (int64_t)tm * kT * ldk, rows_a * ldk);
-    c.rb = make_rsrc(static_cast<const char *>(p.B) + (int64_t)tn * kT * ldk, rows_b * ldk);
+    c.ra = make_rsrc(static_cast<const char *>(p.A) + (int64_t)tm * kT * c.pitch_a,
+                     panel_bytes(rows_a, c.pitch_a, kb));
+    c.rb = make_rsrc(static_cast<const char *>(p.B) + (int64_t)tn * kT * c.pitch_b,
+                     panel_bytes(rows_b, c.pitch_b, kb));
 
     // Each wave loads row groups u = wave + 4 v (v < kB) of every panel, so
     // row bits 3,4 equal the wave index for all its loads.
     const int r8 = lane >> 3;
     c.cb_a = ((lane & 7) ^ slot_xor_a(r8 | (c.wave << 3))) << 4;
     c.cb_b = ((lane & 7) ^ slot_xor_b(r8 | (c.wave << 3))) << 4;
-    c.voff_a = r8 * ldk + c.cb_a;
-    c.voff_b = r8 * ldk + c.cb_b;
+    c.voff_a = r8 * c.pitch_a + c.cb_a;
+    c.voff_b = r8 * c.pitch_b + c.cb_b;
     c.l = quad_lane(lane);
     // MXFP8's scales are packed per whole K step, so it keeps a partial step
     // last (masked); the others take it first.
     constexpr bool kMasked = kDtype == kMx;
-    c.shift = kMasked ? 0 : __builtin_amdgcn_readfirstlane(p.nk * kRowBytes - ldk);
+    c.shift = kMasked ? 0 : __builtin_amdgcn_readfirstlane(p.nk * kRowBytes - kb);
     MxScales sc = {{0u, 0u}, {0u, 0u}};
     if constexpr (kDtype == kMx) {
         // Each 128-row group holds nk K steps of 64 lanes x 8 bytes.  256 x 256
@@ -1364,19 +1381,19 @@ __global__ __launch_bounds__(256, kT == 128 ? 2 : 1) void gemm4_kernel(const Gem
         // whole, or absent for nk == 1 (then no MFMA reads its panel).
         int va0, vb0;
         if constexpr (kMasked) {
-            va0 = kstep_voff(c.voff_a, c.cb_a, 0, ldk);
-            vb0 = kstep_voff(c.voff_b, c.cb_b, 0, ldk);
+            va0 = kstep_voff(c.voff_a, c.cb_a, 0, kb);
+            vb0 = kstep_voff(c.voff_b, c.cb_b, 0, kb);
         } else {
             va0 = c.cb_a >= c.shift ? c.voff_a - c.shift : kOutOfRange;
             vb0 = c.cb_b >= c.shift ? c.voff_b - c.shift : kOutOfRange;
         }
-        const int va1 = kMasked ? kstep_voff(c.voff_a, c.cb_a, 1, ldk) : c.voff_a;
-        const int vb1 = kMasked ? kstep_voff(c.voff_b, c.cb_b, 1, ldk) : c.voff_b;
+        const int va1 = kMasked ? kstep_voff(c.voff_a, c.cb_a, 1, kb) : c.voff_a;
+        const int vb1 = kMasked ? kstep_voff(c.voff_b, c.cb_b, 1, kb) : c.voff_b;
         const int so1 = kRowBytes - c.shift;
-        dma_panel_part<kB>(c.ra, smem, 0, c.wave, va0, 0, ldk);
-        dma_panel_part<kB>(c.rb, smem + kRing, 0, c.wave, vb0, 0, ldk);
-        dma_panel_part<kB>(c.ra, smem + kP, 0, c.wave, va1, so1, ldk);
-        dma_panel_part<kB>(c.rb, smem + kRing + kP, 0, c.wave, vb1, so1, ldk);
+        dma_panel_part<kB>(c.ra, smem, 0, c.wave, va0, 0, c.pitch_a);
+        dma_panel_part<kB>(c.rb, smem + kRing, 0, c.wave, vb0, 0, c.pitch_b);
+        dma_panel_part<kB>(c.ra, smem + kP, 0, c.wave, va1, so1, c.pitch_a);
+        dma_panel_part<kB>(c.rb, smem + kRing + kP, 0, c.wave, vb1, so1, c.pitch_b);
         wait_vmcnt<2 * kB>();                      // step 0 landed
         block_barrier();
         typename Q::Frags f;
@@ -1385,8 +1402,8 @@ __global__ __launch_bounds__(256, kT == 128 ? 2 : 1) void gemm4_kernel(const Gem
         if constexpr (kMasked) {
             rg.ma = c.sa_group + 512;
             rg.mb = c.sb_group + 512;
-            rg.rem = ldk - 2 * kRowBytes;
-            rg.vb = kstep_voff(c.voff_b, c.cb_b, 2, ldk);
+            rg.rem = kb - 2 * kRowBytes;
+            rg.vb = kstep_voff(c.voff_b, c.cb_b, 2, kb);
         }
         Bases bs0 = {{0, 0}, {0, 0}};
         Q::template base<0, 0>(bs0, c.l, c.a_rows);
@@ -1394,7 +1411,7 @@ __global__ __launch_bounds__(256, kT == 128 ? 2 : 1) void gemm4_kernel(const Gem
         Q::template base<0, 2>(bs0, c.l, c.b_rows);
         Q::template base<0, 3>(bs0, c.l, c.b_rows);
         for (int t = 0; t < nk; ++t)
-            quad_step<kDtype, kMasked, kB>(f, acc, sc, c, ldk, t, lane, rg, bs0);
+            quad_step<kDtype, kMasked, kB>(f, acc, sc, c, t, lane, rg, bs0);
         wait_vmcnt<0>();
     }
     const Stamp s1 = stamp();

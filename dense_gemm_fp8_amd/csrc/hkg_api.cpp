@@ -117,12 +117,42 @@ void default_remap(int64_t Gm, int64_t Gn, int64_t row_bytes, int32_t *W, int32_
     *C = static_cast<int32_t>(c);
 }
 
-// One 256-row operand panel is addressed through a buffer resource with a
-// 32-bit byte range, and tile counts / element offsets use 32-bit ints.
-bool sizes_fit(int64_t M, int64_t N, int64_t K, int64_t elem)
+// Row pitches of a call in elements (hkg_gemm_opts lda / ldb / ldc; 0 means
+// dense rows: K, K and N).
+struct Layout {
+    int64_t lda, ldb, ldc;
+};
+
+// The layout the options ask for.  HKG_ERR_OPTS for a pitch below its row's
+// extent (or negative), HKG_ERR_ALIGN for an operand pitch whose rows would
+// not start 16-byte aligned.
+int resolve_layout(const hkg_gemm_opts *opts, int64_t N, int64_t K, int64_t elem, Layout *L)
 {
-    return kTile * K * elem < (int64_t(1) << 31) && M < (int64_t(1) << 31) &&
-           N < (int64_t(1) << 31) && ceil_div(M, kTile) * ceil_div(N, kTile) < (int64_t(1) << 30);
+    L->lda = opts && opts->lda ? opts->lda : K;
+    L->ldb = opts && opts->ldb ? opts->ldb : K;
+    L->ldc = opts && opts->ldc ? opts->ldc : N;
+    if (L->lda < K || L->ldb < K || L->ldc < N)
+        return HKG_ERR_OPTS;
+    if ((L->lda * elem) % 16 || (L->ldb * elem) % 16)
+        return HKG_ERR_ALIGN;
+    return HKG_OK;
+}
+
+// Bytes from the first element of a [rows][cols] matrix with row pitch ld to
+// just past its last element (0 when empty).
+int64_t extent(int64_t rows, int64_t cols, int64_t ld, int64_t elem)
+{
+    return rows > 0 && cols > 0 ? ((rows - 1) * ld + cols) * elem : 0;
+}
+
+// One 256-row operand panel is addressed through a buffer resource with a
+// 32-bit byte range, and tile counts / element offsets / pitches use 32-bit
+// ints.
+bool sizes_fit(int64_t M, int64_t N, const Layout &L, int64_t elem)
+{
+    return kTile * L.lda * elem < (int64_t(1) << 31) && kTile * L.ldb * elem < (int64_t(1) << 31) &&
+           L.ldc < (int64_t(1) << 31) && M < (int64_t(1) << 31) && N < (int64_t(1) << 31) &&
+           ceil_div(M, kTile) * ceil_div(N, kTile) < (int64_t(1) << 30);
 }
 
 // Whether byte ranges [p, p + pb) and [q, q + qb) share a byte.
@@ -133,8 +163,9 @@ bool overlaps(const void *p, int64_t pb, const void *q, int64_t qb)
            b < a + static_cast<uintptr_t>(pb);
 }
 
-int validate(int64_t M, int64_t N, int64_t K, int64_t kalign, int64_t elem, const void *A,
-             const void *B, const void *C, const float *C_f32)
+int validate_layout(int64_t M, int64_t N, int64_t K, int64_t kalign, int64_t elem,
+                    const Layout &L, const void *A, const void *B, const void *C,
+                    const float *C_f32)
 {
     if (M < 0 || N < 0 || K < 0)
         return HKG_ERR_SHAPE;
@@ -146,16 +177,24 @@ int validate(int64_t M, int64_t N, int64_t K, int64_t kalign, int64_t elem, cons
         return HKG_ERR_NULL;
     if (!aligned16(A) || !aligned16(B) || !aligned16(C) || (C_f32 && !aligned16(C_f32)))
         return HKG_ERR_ALIGN;
-    if (!sizes_fit(M, N, K, elem))
+    if (!sizes_fit(M, N, L, elem))
         return HKG_ERR_SIZE;
     // Tiles read operand panels while other tiles write C: an output that
     // shares a byte with an input, or the two outputs with each other, would
-    // give a wrong result.  (A and B may alias: both are only read.)
-    const int64_t ab = M * K * elem, bb = N * K * elem, cb = M * N * 2, fb = M * N * 4;
+    // give a wrong result.  (A and B may alias: both are only read.)  With
+    // pitches, each matrix is taken to span its first to its last element.
+    const int64_t ab = extent(M, K, L.lda, elem), bb = extent(N, K, L.ldb, elem),
+                  cb = extent(M, N, L.ldc, 2), fb = extent(M, N, L.ldc, 4);
     if (overlaps(C, cb, A, ab) || overlaps(C, cb, B, bb) || overlaps(C_f32, fb, A, ab) ||
         overlaps(C_f32, fb, B, bb) || overlaps(C_f32, fb, C, cb))
         return HKG_ERR_OVERLAP;
     return HKG_OK;
+}
+
+int validate(int64_t M, int64_t N, int64_t K, int64_t kalign, int64_t elem, const void *A,
+             const void *B, const void *C, const float *C_f32)
+{
+    return validate_layout(M, N, K, kalign, elem, Layout{K, K, N}, A, B, C, C_f32);
 }
 
 // Output tile edge of a schedule's kernel.
@@ -279,7 +318,7 @@ int resolve_opts(hkg::Dtype dt, const hkg_gemm_opts *opts, int64_t M, int64_t N,
 bool opts_in_range(const hkg_gemm_opts *opts)
 {
     return !opts || (opts->remap >= 0 && opts->remap <= 2 && opts->schedule >= 0 &&
-                     opts->schedule <= 5);
+                     opts->schedule <= 5 && opts->lda >= 0 && opts->ldb >= 0 && opts->ldc >= 0);
 }
 
 // Only the 4-wave kernel on 256 x 256 and 128 x 128 tiles has the
@@ -340,9 +379,18 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
     const int64_t kalign =
         dt == hkg::kBf16 ? kKAlignBf16 : (dt == hkg::kFp8 ? kKAlignFp8 : kKAlignMx);
     const int64_t elem = dt == hkg::kBf16 ? 2 : 1;
-    int rc = validate(M, N, K, kalign, elem, A, B, C, C_f32);
+    if (M < 0 || N < 0 || K < 0 || K % kalign)
+        return HKG_ERR_SHAPE;
+    if (!opts_in_range(opts))
+        return HKG_ERR_OPTS;
+    Layout L;
+    int rc = resolve_layout(opts, N, K, elem, &L);
     if (rc != HKG_OK)
         return rc;
+    rc = validate_layout(M, N, K, kalign, elem, L, A, B, C, C_f32);
+    if (rc != HKG_OK)
+        return rc;
+    const int64_t cb = extent(M, N, L.ldc, 2), fb = extent(M, N, L.ldc, 4);
     if (dt == hkg::kMx && M > 0 && N > 0 && K > 0) {
         if (!SA || !SB)
             return HKG_ERR_NULL;
@@ -352,8 +400,8 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
         if (mx_packed_bytes(M, K) >= (int64_t(1) << 31) || mx_packed_bytes(N, K) >= (int64_t(1) << 31))
             return HKG_ERR_SIZE;
         const int64_t sab = mx_packed_bytes(M, K), sbb = mx_packed_bytes(N, K);
-        if (overlaps(C, M * N * 2, SA, sab) || overlaps(C, M * N * 2, SB, sbb) ||
-            overlaps(C_f32, M * N * 4, SA, sab) || overlaps(C_f32, M * N * 4, SB, sbb))
+        if (overlaps(C, cb, SA, sab) || overlaps(C, cb, SB, sbb) || overlaps(C_f32, fb, SA, sab) ||
+            overlaps(C_f32, fb, SB, sbb))
             return HKG_ERR_OVERLAP;
     }
     if (M == 0 || N == 0)
@@ -368,11 +416,11 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
         int64_t wgs = 0;
         for (int i = 0; i < pl.launches; ++i)
             wgs += pl.Gm[i] * pl.Gn[i];
-        const int64_t tb = 64 * wgs, ab = M * K * elem, bb = N * K * elem;
+        const int64_t tb = 64 * wgs, ab = extent(M, K, L.lda, elem), bb = extent(N, K, L.ldb, elem);
         if ((reinterpret_cast<uintptr_t>(trace) & 7u) != 0)
             return HKG_ERR_ALIGN;
-        if (overlaps(trace, tb, A, ab) || overlaps(trace, tb, B, bb) ||
-            overlaps(trace, tb, C, M * N * 2) || overlaps(trace, tb, C_f32, M * N * 4))
+        if (overlaps(trace, tb, A, ab) || overlaps(trace, tb, B, bb) || overlaps(trace, tb, C, cb) ||
+            overlaps(trace, tb, C_f32, fb))
             return HKG_ERR_OVERLAP;
     }
 
@@ -384,6 +432,9 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
     p.B = B;
     p.N = static_cast<int>(N);
     p.K = static_cast<int>(K);
+    p.lda = static_cast<int>(L.lda);
+    p.ldb = static_cast<int>(L.ldb);
+    p.ldc = static_cast<int>(L.ldc);
     p.nk = static_cast<int>(ceil_div(K, kstep));
     // The product of the two per-tensor scales, rounded once to fp32.
     p.scale = dt == hkg::kFp8 ? static_cast<float>(static_cast<double>(sa) * sb) : 1.0f;
@@ -394,7 +445,7 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
         // launch i covers output rows [row, row + rows[i]); row is 0 or a
         // multiple of 256, so the offset pointers keep 16-byte alignment, and
         // A's packed scales start at the group of 128 rows that holds row
-        p.A = static_cast<const char *>(A) + row * K * elem;
+        p.A = static_cast<const char *>(A) + row * L.lda * elem;
         if (dt == hkg::kMx) {
             p.SA = static_cast<const char *>(SA) + mx_packed_bytes(row, K);
             p.sa_bytes = static_cast<int>(mx_packed_bytes(pl.rows[i], K));
@@ -402,8 +453,8 @@ int gemm(hkg::Dtype dt, int64_t M, int64_t N, int64_t K, const void *A, const vo
             p.SA = nullptr;
             p.sa_bytes = 0;
         }
-        p.C = static_cast<uint16_t *>(C) + row * N;
-        p.C_f32 = C_f32 ? C_f32 + row * N : nullptr;
+        p.C = static_cast<uint16_t *>(C) + row * L.ldc;
+        p.C_f32 = C_f32 ? C_f32 + row * L.ldc : nullptr;
         p.M = static_cast<int>(pl.rows[i]);
         p.Gm = static_cast<int>(pl.Gm[i]);
         p.Gn = static_cast<int>(pl.Gn[i]);
@@ -541,9 +592,15 @@ int hkg_launch_plan(int64_t M, int64_t N, int64_t K, int32_t dtype, const hkg_ge
     if (M < 0 || N < 0 || K < 0 || K % kalign)
         return HKG_ERR_SHAPE;
     *plan = hkg_launch_plan_t{};
+    if (!opts_in_range(opts))
+        return HKG_ERR_OPTS;
+    Layout L;
+    const int lrc = resolve_layout(opts, N, K, elem, &L);
+    if (lrc != HKG_OK)
+        return lrc;
     if (M == 0 || N == 0)   // as the entry points: no launch, only the options checked
-        return opts_in_range(opts) && schedule_supported(dt, opts) ? HKG_OK : HKG_ERR_OPTS;
-    if (!sizes_fit(M, N, K, elem))
+        return schedule_supported(dt, opts) ? HKG_OK : HKG_ERR_OPTS;
+    if (!sizes_fit(M, N, L, elem))
         return HKG_ERR_SIZE;
     Plan pl;
     const int rc = plan_gemm(dt, M, N, K, opts, &pl);

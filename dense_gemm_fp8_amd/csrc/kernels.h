@@ -9,11 +9,12 @@ namespace hkg {
 
 // Arguments of one GEMM launch.  All shape checks are done by the caller.
 struct GemmParams {
-    const void *A;      // [M][K] row-major, K contiguous
-    const void *B;      // [N][K] row-major, K contiguous
-    void *C;            // [M][N] bf16 row-major
-    float *C_f32;       // optional [M][N] fp32 pre-rounding copy (nullptr = none)
+    const void *A;      // [M][K] row-major, K contiguous, rows lda elements apart
+    const void *B;      // [N][K] row-major, K contiguous, rows ldb elements apart
+    void *C;            // [M][N] bf16 row-major, rows ldc elements apart
+    float *C_f32;       // optional [M][N] fp32 pre-rounding copy, same ldc (nullptr = none)
     int M, N, K;
+    int lda, ldb, ldc;  // row pitches in elements (>= K, K, N)
     int Gm, Gn;         // tile grid (M/256, N/256)
     int W, Cc;          // remap window height and per-XCD chunk
     int nk;             // number of K steps

@@ -115,7 +115,25 @@ typedef struct {
     int32_t C;         /* consecutive tiles per XCD (HKG_REMAP_XCD)    */
     int32_t schedule;  /* HKG_SCHED_*                                  */
     uint64_t *trace;   /* NULL, or a per-workgroup time record (below) */
+    int64_t lda;       /* row pitches in elements, 0 = dense rows: A (K), */
+    int64_t ldb;       /* B (K) and C / C_f32 (N); see "Row pitches"     */
+    int64_t ldc;
 } hkg_gemm_opts;
+
+/*
+ * Row pitches (hkg_gemm_opts lda, ldb, ldc).  Row m of A starts lda elements
+ * after row m - 1 (likewise B with ldb, and C and C_f32 with ldc), so a caller
+ * can pass a sub-matrix of a wider one, or pad rows: operand rows of m x 8 KiB
+ * with m not a power of two (e.g. bf16 K = 12288 or 28672) make the L2 stall
+ * on tag lookups, which a pitch 128 bytes longer avoids.  Rules: lda, ldb >= K
+ * with lda * element size and ldb * element size multiples of 16
+ * (HKG_ERR_ALIGN); ldc >= N (C rows are then written element by element unless
+ * N and ldc are multiples of 8); 0 selects the dense pitch; a pitch below its
+ * extent or negative is HKG_ERR_OPTS; 256 * pitch * element size must stay
+ * below 2^31 (HKG_ERR_SIZE).  The bytes between rows are neither read into the
+ * result nor written.  Overlap checks take each matrix to span its first to
+ * its last element.
+ */
 
 /*
  * Time record (hkg_gemm_opts.trace): a device buffer, 8-byte aligned, of

@@ -354,7 +354,10 @@ def test_trace_buffer_validated_before_launch():
     assert hkg.hkg_gemm_bf16_ex(M, N, K, FAKE, FB, FC, None, None, o) == hkg.HKG_ERR_OVERLAP
     o = hkg.make_opts(trace=FAKE)                            # over A
     assert hkg.hkg_gemm_fp8_ex(M, N, 128, FAKE, FB, 1.0, 1.0, FC, None, None, o) == hkg.HKG_ERR_OVERLAP
-    assert ctypes.sizeof(hkg.hkg_gemm_opts) == 24
+    assert ctypes.sizeof(hkg.hkg_gemm_opts) == 48
+    assert [hkg.hkg_gemm_opts.__dict__[f].offset for f in ("remap", "W", "C", "schedule", "trace",
+                                                           "lda", "ldb", "ldc")] == \
+        [0, 4, 8, 12, 16, 24, 32, 40]
 
 
 def _table4():
@@ -469,3 +472,37 @@ def test_tune_remap_without_a_gfx950_is_a_device_error():
     rc, ms, tried = hkg.hkg_tune_remap(256, 256, 256, 0, FAKE, FB, FC, 5, best, None)
     assert rc == hkg.HKG_ERR_DEVICE and tried == []
     assert (best.remap, best.W, best.C) == (hkg.HKG_REMAP_XCD, 3, 5)
+
+
+def test_row_pitches_validated_before_launch():
+    """lda / ldb / ldc: 0 = dense; below the row's extent or negative ->
+    HKG_ERR_OPTS; operand rows not 16-byte aligned -> HKG_ERR_ALIGN; panels past
+    the 32-bit range -> HKG_ERR_SIZE; overlap checks span first to last element.
+    Valid layouts reach the device check (HKG_ERR_DEVICE without a gfx950)."""
+    M, N, K = 300, 200, 64
+    G = lambda **kw: hkg.hkg_gemm_bf16_ex(M, N, K, FAKE, FB, FC, None, None, hkg.make_opts(**kw))
+    F = lambda **kw: hkg.hkg_gemm_fp8_ex(M, N, K, FAKE, FB, 1.0, 1.0, FC, None, None,
+                                         hkg.make_opts(**kw))
+    assert G(lda=63) == hkg.HKG_ERR_OPTS and G(ldb=32) == hkg.HKG_ERR_OPTS
+    assert G(ldc=199) == hkg.HKG_ERR_OPTS and G(lda=-64) == hkg.HKG_ERR_OPTS
+    assert G(lda=68) == hkg.HKG_ERR_ALIGN            # 136-byte rows
+    assert F(ldb=72) == hkg.HKG_ERR_ALIGN and F(ldb=80) in (hkg.HKG_OK, hkg.HKG_ERR_DEVICE)
+    assert G(lda=1 << 22) == hkg.HKG_ERR_SIZE          # 256 rows x 8 MiB
+    # a pitched C reaches further: C at FC with ldc 4096 spans 299 * 8 KiB + 400 B
+    far = FC + 299 * 8192
+    assert hkg.hkg_gemm_bf16_ex(M, N, K, FAKE, far, FC, None, None,
+                                hkg.make_opts(ldc=4096)) == hkg.HKG_ERR_OVERLAP
+    assert hkg.hkg_gemm_bf16_ex(M, N, K, FAKE, far + 512, FC, None, None,
+                                hkg.make_opts(ldc=4096)) != hkg.HKG_ERR_OVERLAP
+    try:
+        import torch
+        gpu = torch.cuda.is_available()
+    except ImportError:
+        gpu = False
+    if not gpu:
+        for kw in (dict(lda=64), dict(lda=72, ldb=128, ldc=256), dict(ldc=201)):
+            assert G(**kw) == hkg.HKG_ERR_DEVICE, kw
+    # the plan takes the pitches into its size check too
+    assert hkg.launch_plan(M, N, K, 0, hkg.make_opts(lda=1 << 22))[0] == hkg.HKG_ERR_SIZE
+    assert hkg.launch_plan(M, N, K, 0, hkg.make_opts(lda=63))[0] == hkg.HKG_ERR_OPTS
+    assert hkg.launch_plan(M, N, K, 0, hkg.make_opts(lda=128))[0] == hkg.HKG_OK

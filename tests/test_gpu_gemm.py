@@ -864,3 +864,108 @@ def test_tune_remap_returns_a_timed_order_and_leaves_a_valid_product(dtype, M, N
         ref = oracle.gemm_bf16_pairs(A, B, pm, pn)
         assert np.all(np.abs(bf16_to_f64(want[pm, pn]) - ref) <=
                       1e-3 * np.sqrt(K) + np.abs(ref) * 2.0 ** -8)
+
+
+# ------------------------------------------------------------ row pitches ------------
+
+def _pitched(dense, ld, fill):
+    """A [rows][ld] GPU tensor whose first cols columns are `dense` and the rest
+    `fill`, and the view of those columns (row stride ld)."""
+    rows, cols = dense.shape
+    big = torch.full((rows, ld), fill, dtype=dense.dtype, device="cuda")
+    big[:, :cols] = dense
+    return big, big[:, :cols]
+
+
+PITCH_CASES = [
+    # dtype, M, N, K, pad_a, pad_b, pad_c, schedule
+    ("bf16", 300, 260, 520, 64, 136, 24, hkg.HKG_SCHED_DEFAULT),      # ragged, 128x128 tiles
+    ("bf16", 300, 260, 520, 64, 136, 3, hkg.HKG_SCHED_DEFAULT),       # C rows not 16-byte aligned
+    ("bf16", 1024, 768, 512, 8, 64, 8, hkg.HKG_SCHED_INTERLEAVE),
+    ("bf16", 1024, 768, 512, 8, 64, 8, hkg.HKG_SCHED_PINGPONG),
+    ("bf16", 1024, 768, 512, 8, 64, 8, hkg.HKG_SCHED_LOCKSTEP),
+    ("bf16", 3072, 3072, 128, 64, 64, 64, hkg.HKG_SCHED_DEFAULT),     # 192x192 tiles
+    ("bf16", 4352, 4352, 256, 64, 0, 8, hkg.HKG_SCHED_DEFAULT),       # split default launch
+    ("fp8", 513, 777, 1008, 16, 48, 5, hkg.HKG_SCHED_DEFAULT),
+    ("fp8", 1024, 512, 640, 128, 16, 8, hkg.HKG_SCHED_PINGPONG),
+    ("fp8", 2048, 1536, 512, 32, 32, 16, hkg.HKG_SCHED_INTERLEAVE),
+]
+
+
+@pytest.mark.parametrize("dtype,M,N,K,pa,pb,pc,sched", PITCH_CASES)
+def test_row_pitches_match_dense_layout(dtype, M, N, K, pa, pb, pc, sched):
+    """Operands and output with row pitches (views of wider, NaN-padded
+    matrices; C and C_f32 inside canary-filled rows) give the dense call's output
+    bit for bit, and nothing is written between rows."""
+    _say("pitches %s %dx%dx%d pads %d/%d/%d sched %d" % (dtype, M, N, K, pa, pb, pc, sched))
+    x, y = synth.normal_f32(9801 + M, M, K), synth.normal_f32(9802 + N, N, K)
+    if dtype == "bf16":
+        dA, dB = _dev_bf16(synth.f32_to_bf16_bits(x)), _dev_bf16(synth.f32_to_bf16_bits(y))
+        nan = float("nan")
+        run = lambda a, b, c, f, o: hkg.gemm_bf16(a, b, c, f, opts=o)
+    else:
+        (A, sa), (B, sb) = synth.e4m3_quantize(x), synth.e4m3_quantize(y)
+        dA, dB = _dev_u8(A), _dev_u8(B)
+        nan = 0x7F                                   # an e4m3 NaN code
+        run = lambda a, b, c, f, o: hkg.gemm_fp8(a, b, sa, sb, c, f, opts=o)
+    o = hkg.make_opts(schedule=sched)
+    Cd = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    Fd = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    run(dA, dB, Cd, Fd, o)
+    bigA, vA = _pitched(dA, K + pa, nan)
+    bigB, vB = _pitched(dB, K + pb, nan)
+    canary = -1234.5
+    bigC = torch.full((M, N + pc), canary, dtype=torch.bfloat16, device="cuda")
+    bigF = torch.full((M, N + pc), canary, dtype=torch.float32, device="cuda")
+    vC, vF = bigC[:, :N], bigF[:, :N]
+    if pa == 0 and pb == 0 and pc == 0:
+        pytest.skip("dense")
+    run(vA, vB, vC, vF, o)
+    # the view tensors carry their pitches; the same through explicit options
+    bigC2 = torch.full((M, N + pc), canary, dtype=torch.bfloat16, device="cuda")
+    o2 = hkg.make_opts(schedule=sched, lda=K + pa, ldb=K + pb, ldc=N + pc)
+    M_, K_ = M, K
+    if dtype == "bf16":
+        rc = hkg.hkg_gemm_bf16_ex(M_, N, K_, bigA.data_ptr(), bigB.data_ptr(), bigC2.data_ptr(), None,
+                                  torch.cuda.current_stream().cuda_stream, o2)
+    else:
+        rc = hkg.hkg_gemm_fp8_ex(M_, N, K_, bigA.data_ptr(), bigB.data_ptr(), float(sa), float(sb),
+                                 bigC2.data_ptr(), None, torch.cuda.current_stream().cuda_stream, o2)
+    assert rc == hkg.HKG_OK
+    torch.cuda.synchronize()
+    want = _host_bits(Cd)
+    assert np.array_equal(_host_bits(vC.contiguous()), want)
+    assert np.array_equal(_host_bits(bigC2[:, :N].contiguous()), want)
+    assert np.array_equal(vF.cpu().numpy().view(np.uint32), Fd.cpu().numpy().view(np.uint32))
+    if pc:
+        assert torch.all(bigC[:, N:] == canary) and torch.all(bigC2[:, N:] == canary)
+        assert torch.all(bigF[:, N:] == canary)
+    # the operands' padding was only read
+    assert torch.equal(bigA[:, :K], dA) and torch.equal(bigB[:, :K], dB)
+
+
+def test_row_pitches_mxfp8_and_shared_operand():
+    """MXFP8 with pitched element arrays, and A·Aᵀ from one pitched buffer, equal
+    their dense calls bit for bit."""
+    M, N, K = 520, 300, 544
+    _say("pitches mxfp8 %dx%dx%d" % (M, N, K))
+    ea, sa = synth.mx_quantize(synth.normal_f32(9811, M, K))
+    eb, sb = synth.mx_quantize(synth.normal_f32(9812, N, K))
+    dA, dB = _dev_u8(ea), _dev_u8(eb)
+    pA = hkg.mx_pack_scales(_dev_u8(sa), hkg.HKG_MX_OPERAND_A)
+    pB = hkg.mx_pack_scales(_dev_u8(sb), hkg.HKG_MX_OPERAND_B)
+    Cd = hkg.gemm_mxfp8(dA, dB, pA, pB)
+    bigA, vA = _pitched(dA, K + 48, 0x7F)
+    bigB, vB = _pitched(dB, K + 16, 0x7F)
+    bigC = torch.full((M, N + 8), -7.0, dtype=torch.bfloat16, device="cuda")
+    hkg.gemm_mxfp8(vA, vB, pA, pB, bigC[:, :N])
+    torch.cuda.synchronize()
+    assert np.array_equal(_host_bits(bigC[:, :N].contiguous()), _host_bits(Cd))
+    assert torch.all(bigC[:, N:] == -7.0)
+    # A·Aᵀ: one pitched bf16 buffer as both operands
+    x = _dev_bf16(synth.f32_to_bf16_bits(synth.normal_f32(9813, 700, 264)))
+    big, v = _pitched(x, 264 + 40, float("nan"))
+    C1 = hkg.gemm_bf16(x, x)
+    C2 = hkg.gemm_bf16(v, v)
+    torch.cuda.synchronize()
+    assert np.array_equal(_host_bits(C1), _host_bits(C2))
