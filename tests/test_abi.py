@@ -506,3 +506,21 @@ def test_row_pitches_validated_before_launch():
     assert hkg.launch_plan(M, N, K, 0, hkg.make_opts(lda=1 << 22))[0] == hkg.HKG_ERR_SIZE
     assert hkg.launch_plan(M, N, K, 0, hkg.make_opts(lda=63))[0] == hkg.HKG_ERR_OPTS
     assert hkg.launch_plan(M, N, K, 0, hkg.make_opts(lda=128))[0] == hkg.HKG_OK
+
+
+def test_header_is_c99_and_a_c_caller_links(tmp_path):
+    """include/hkg.h compiles as C99 with -Wall -Wextra -Werror, and a plain C
+    program using it (tests/c/gemm_c_api.c) links against libhkg.so."""
+    import importlib.util
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    spec = importlib.util.spec_from_file_location("c_api_build", os.path.join(ROOT, "tests", "c",
+                                                                               "build.py"))
+    c_api = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(c_api)
+    out = str(tmp_path / "gemm_c_api")
+    res = subprocess.run(c_api.command(out), capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    assert os.path.exists(out)

@@ -819,6 +819,70 @@ def test_concurrent_streams_independent():
     np.testing.assert_array_equal(_host_bits(C2), want2)
 
 
+def test_host_threads_call_concurrently():
+    """Four host threads, each with its own stream and operands, call the C
+    entry points at once (ctypes releases the GIL for the call): every thread
+    gets its own result and status, and a rejected call in one thread does not
+    disturb the others' last HIP error or outputs."""
+    import threading
+    _say("host threads")
+    M, N, K = 1024, 768, 512
+    data = []
+    for t in range(4):
+        A = synth.f32_to_bf16_bits(synth.normal_f32(9920 + t, M, K))
+        B = synth.f32_to_bf16_bits(synth.normal_f32(9930 + t, N, K))
+        want, _ = run_bf16(A, B, want_f32=False)
+        data.append((_dev_bf16(A), _dev_bf16(B), want))
+    outs = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    errors = []
+    torch.cuda.synchronize()
+
+    def work(t):
+        try:
+            dA, dB, _ = data[t]
+            h = streams[t].cuda_stream
+            for i in range(20):
+                rc = hkg.hkg_gemm_bf16(M, N, K, dA.data_ptr(), dB.data_ptr(), outs[t].data_ptr(),
+                                       None, h)
+                if rc != hkg.HKG_OK:
+                    errors.append((t, i, rc))
+                if t == 3:   # one thread also makes calls that fail validation
+                    bad = hkg.hkg_gemm_bf16(M, N, K - 1, dA.data_ptr(), dB.data_ptr(),
+                                            outs[t].data_ptr(), None, h)
+                    if bad != hkg.HKG_ERR_SHAPE:
+                        errors.append((t, i, "bad", bad))
+        except Exception as e:   # pragma: no cover - reported below
+            errors.append((t, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=60)
+    assert not any(th.is_alive() for th in threads)
+    torch.cuda.synchronize()
+    assert errors == []
+    for t in range(4):
+        np.testing.assert_array_equal(_host_bits(outs[t]), data[t][2])
+
+
+def test_plain_c_caller():
+    """tests/c/gemm_c_api: a C99 program using only include/hkg.h and the HIP
+    runtime API runs bf16 (dense and pitched) and e4m3 GEMMs through the C ABI
+    and checks them bit for bit on the host (built by __graft_entry__.build())."""
+    import os
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = os.path.join(root, "tests", "c", "gemm_c_api")
+    if not os.path.exists(exe):
+        pytest.skip("tests/c/gemm_c_api is not built (run __graft_entry__.build())")
+    _say("plain C caller")
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "C API OK" in res.stdout
+
+
 # ------------------------------------------------------------- autotuner ------------
 
 @pytest.mark.parametrize("dtype,M,N,K", [("bf16", 4096, 4096, 512), ("fp8", 3000, 5000, 512),
