@@ -669,6 +669,9 @@ def main(argv=None) -> int:
                     help="with --sizes: also time the vendor library on the same inputs (context)")
     args = ap.parse_args(argv)
 
+    if args.tune and args.pad_k:
+        print("--tune times dense operand rows; it does not combine with --pad-k", file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print("bench.py measures one GPU only: this GEMM path is single-GPU "
               "(--gpus %d is not supported; run with --gpus 1)" % args.gpus, file=sys.stderr)

@@ -17,6 +17,11 @@ def test_more_than_one_gpu_is_refused(capsys):
     assert "one GPU" in capsys.readouterr().err
 
 
+def test_tune_with_padded_rows_is_refused(capsys):
+    assert bench.main(["--tune", "--pad-k", "64"]) == 2
+    assert "--pad-k" in capsys.readouterr().err
+
+
 def test_clock_from_trace_decodes_a_known_record():
     # 2 launches x 16 workgroups; workgroup b on XCD b % 8 at (1500 + 20 x) MHz:
     # shader-clock ticks = MHz / 100 per real-time tick
