@@ -14,10 +14,11 @@
  * shape"): one workgroup per 256 x 256 output tile -- 256 threads (4 waves,
  * the default 4-wave interleave) or 512 threads (8 waves, the ping-pong and
  * lockstep schedules) -- on a flat grid of ceil(M/256) * ceil(N/256)
- * workgroups (HKG_SCHED_INTERLEAVE_128: 128 x 128 tiles, ceil(M/128) *
- * ceil(N/128) workgroups of 256 threads), K consumed 64 (bf16) or 128 (e4m3)
- * at a time; rows past M or N
- * and K past the end read as zeros.  Workgroup ids are remapped to tiles by the
+ * workgroups (HKG_SCHED_INTERLEAVE_128 / _192: 128 x 128 / 192 x 192 tiles,
+ * ceil(M/t) * ceil(N/t) workgroups of 256 threads), K consumed 64 (bf16) or
+ * 128 (e4m3) at a time; rows past M or N and K past the end read as zeros.
+ * Rows of A, B and C may be further apart than their length (row pitches,
+ * hkg_gemm_opts lda / ldb / ldc).  Workgroup ids are remapped to tiles by the
  * chiplet-aware schedule of the same note, section 2 (Pillar 3) / section 7
  * (Algorithm 1), with window height W and per-XCD chunk C.
  *
