@@ -57,10 +57,13 @@ EQ1_LLC_BW_TBS = 5.99
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0}   # MI355X dense MFMA peaks
 # HipKittens 8-wave 0P/8C bf16 GEMM at 8192^3 on MI355X (HipKittens L2 note, Table 2 / Q3)
 PAGES_BF16_8192_TFLOPS = 1610.0
-# the sources that decide what a default launch runs: the kernels and the
-# launch planning (not the cache model or the autotuner, which only advise)
+# the sources that decide what a launch runs: the kernels, the grid remap,
+# and the launch planning and launch code (not the argument checks of the
+# entry points, the cache model or the autotuner, which do not change what a
+# valid call runs)
 KERNEL_SOURCES = ("dense_gemm_fp8_amd/csrc/gemm_kernels.hip", "dense_gemm_fp8_amd/csrc/remap.h",
-                  "dense_gemm_fp8_amd/csrc/kernels.h", "dense_gemm_fp8_amd/csrc/hkg_api.cpp")
+                  "dense_gemm_fp8_amd/csrc/kernels.h", "dense_gemm_fp8_amd/csrc/launch.cpp",
+                  "dense_gemm_fp8_amd/csrc/api_internal.h")
 
 
 def _strip_comments(text: str) -> str:

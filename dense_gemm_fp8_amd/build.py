@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhkg.so")
 SOURCES = [os.path.join(CSRC, "gemm_kernels.hip"), os.path.join(CSRC, "hkg_api.cpp"),
-           os.path.join(CSRC, "remap_model.cpp"), os.path.join(CSRC, "tune.cpp")]
+           os.path.join(CSRC, "launch.cpp"), os.path.join(CSRC, "remap_model.cpp"),
+           os.path.join(CSRC, "tune.cpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

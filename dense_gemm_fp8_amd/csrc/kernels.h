@@ -1,4 +1,4 @@
-// kernels.h -- launch interface between the C ABI (hkg_api.cpp) and the gfx950
+// kernels.h -- launch interface between the C ABI (launch.cpp) and the gfx950
 // kernels (gemm_kernels.hip).  Internal to libhkg.
 #pragma once
 

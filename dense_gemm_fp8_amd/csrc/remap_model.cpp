@@ -49,8 +49,10 @@ RemapModel model_remap(int Gm, int Gn, int W, int C, int64_t panel_bytes, int pe
         }
         llc_requests += fetched;
         llc_hits += fetched - uni;                       // another XCD fetched it this round
-        if (prev_union * panel_bytes <= kLlcBytes)
-            llc_hits += from_prev;                       // still cached from the last round
+        // still cached from the last round (prev_union x panel_bytes <= the
+        // LLC, compared as a quotient so that no panel size can wrap it)
+        if (panel_bytes == 0 || prev_union <= kLlcBytes / panel_bytes)
+            llc_hits += from_prev;
         prev_union = uni;
     }
     RemapModel m;

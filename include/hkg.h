@@ -224,8 +224,10 @@ enum { HKG_MX_OPERAND_A = 0, HKG_MX_OPERAND_B = 1 };
 
 /*
  * Bytes of the packed scales of one MXFP8 operand with `rows` rows:
- * ceil(rows/128) * ceil(K/128) * 512 (host only).  Negative hkg_status
- * (HKG_ERR_SHAPE) if rows < 0, K < 0 or K % 32 != 0.
+ * ceil(rows/128) * ceil(K/128) * 512 (host only).  Negative hkg_status:
+ * HKG_ERR_SHAPE if rows < 0, K < 0 or K % 32 != 0; HKG_ERR_SIZE for sizes
+ * hkg_mx_pack_scales refuses (rows >= 2^31, K >= 2^23, or 2 GiB of packed
+ * scales).
  */
 int64_t hkg_mx_packed_scale_bytes(int64_t rows, int64_t K);
 
@@ -241,7 +243,8 @@ int64_t hkg_mx_packed_scale_bytes(int64_t rows, int64_t K);
  *   operand B: rho = 32 (e >> 1) + 4 (e & 1) + (x & 3) + 8 (x >> 2)
  * Rows past `rows` and blocks past K/32 read 127 (scale 1).  Enqueued on
  * `stream`; weights' scales can be packed once and reused.  HKG_ERR_SIZE if
- * K >= 2^23 (the GEMM's own bound) or the packed size reaches 2 GiB.
+ * rows >= 2^31, K >= 2^23 (the GEMM's own bound) or the packed size reaches
+ * 2 GiB.
  */
 int hkg_mx_pack_scales(int32_t operand, int64_t rows, int64_t K, const void *scales,
                        void *packed, void *stream);

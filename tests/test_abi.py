@@ -182,6 +182,10 @@ def test_mx_packed_scale_bytes():
     assert hkg.hkg_mx_packed_scale_bytes(100, 0) == 0
     for rows, K in ((-1, 64), (10, -32), (10, 48)):
         assert hkg.hkg_mx_packed_scale_bytes(rows, K) == hkg.HKG_ERR_SHAPE
+    # sizes the pack refuses, including ones whose products would wrap 64 bits
+    assert hkg.hkg_mx_packed_scale_bytes(1 << 20, 1 << 15) == 1 << 30   # 2^13 x 2^8 x 512
+    for rows, K in ((1 << 31, 64), (1, 1 << 23), (1 << 62, 1 << 40), (1, (1 << 63) - 32)):
+        assert hkg.hkg_mx_packed_scale_bytes(rows, K) == hkg.HKG_ERR_SIZE, (rows, K)
 
 
 def test_mx_pack_rejects_bad_arguments():
@@ -193,6 +197,10 @@ def test_mx_pack_rejects_bad_arguments():
     assert hkg.hkg_mx_pack_scales(A, 10, 64, FAKE, FAKE + 8, None) == hkg.HKG_ERR_ALIGN
     assert hkg.hkg_mx_pack_scales(A, 0, 64, None, None, None) == hkg.HKG_OK      # nothing to do
     assert hkg.hkg_mx_pack_scales(A, 1, 1 << 23, FAKE, FAKE, None) == hkg.HKG_ERR_SIZE
+    # K near 2^63 would wrap 256 x K and ceil(K / 128) negative: refused, never
+    # launched with truncated sizes
+    for rows, K in ((1, (1 << 63) - 32), (1 << 40, 64), ((1 << 62) + 128, 1 << 40)):
+        assert hkg.hkg_mx_pack_scales(A, rows, K, FAKE, FB, None) == hkg.HKG_ERR_SIZE, (rows, K)
 
 
 def test_mxfp8_validation():
@@ -398,6 +406,17 @@ def test_remap_model_closed_forms():
     rc, l2, llc, bw = hkg.hkg_remap_model(1, 1, 1, 1, 1 << 20)
     assert l2 == 0.0 and llc == 0.0
     assert hkg.hkg_remap_model(0, 4, 1, 1, 1, 32)[0] == hkg.HKG_ERR_SHAPE
+    # grid sides whose product would wrap are refused before it is formed
+    # (2^32 x 2^32 is 2^64, 0 modulo 2^64)
+    for gm, gn in ((1 << 32, 1 << 32), (1 << 40, 2), (1 << 31, 1)):
+        assert hkg.hkg_remap_model(gm, gn, 1, 1, 1 << 20)[0] == hkg.HKG_ERR_SHAPE
+        assert hkg.hkg_remap_tile(gm, gn, 1, 1, 0)[0] == hkg.HKG_ERR_SHAPE
+        assert hkg.hkg_remap_tiles_device(gm, gn, 1, 1, FAKE, None) == hkg.HKG_ERR_SHAPE
+    # a panel size too large for the last-level cache term does not wrap it:
+    # no panel stays cached between rounds, as for any size above the cache
+    rc, l2, llc_big, bw = hkg.hkg_remap_model(32, 32, 8, 32, (1 << 62) + 1)
+    rc2, l2b, llc_huge, bw2 = hkg.hkg_remap_model(32, 32, 8, 32, 1 << 30)
+    assert rc == rc2 == hkg.HKG_OK and llc_big == llc_huge and l2 == l2b
     assert hkg.hkg_remap_model(4, 4, 0, 1, 1, 32)[0] == hkg.HKG_ERR_SHAPE
 
 
@@ -502,6 +521,13 @@ def test_row_pitches_validated_before_launch():
     if not gpu:
         for kw in (dict(lda=64), dict(lda=72, ldb=128, ldc=256), dict(ldc=201)):
             assert G(**kw) == hkg.HKG_ERR_DEVICE, kw
+    # pitches whose byte size would wrap a 64-bit product are refused, not
+    # wrapped into range (256 x 2^56 x 2 bytes is 2^65)
+    for big in (1 << 56, 1 << 60, (1 << 63) - 16):
+        assert G(lda=big) == hkg.HKG_ERR_SIZE and G(ldb=big) == hkg.HKG_ERR_SIZE, big
+        assert G(ldc=big) == hkg.HKG_ERR_SIZE and F(ldb=big) == hkg.HKG_ERR_SIZE, big
+        assert hkg.launch_plan(M, N, K, 0, hkg.make_opts(lda=big))[0] == hkg.HKG_ERR_SIZE
+    assert G(lda=(1 << 63) - 1) == hkg.HKG_ERR_ALIGN
     # the plan takes the pitches into its size check too
     assert hkg.launch_plan(M, N, K, 0, hkg.make_opts(lda=1 << 22))[0] == hkg.HKG_ERR_SIZE
     assert hkg.launch_plan(M, N, K, 0, hkg.make_opts(lda=63))[0] == hkg.HKG_ERR_OPTS
