@@ -672,8 +672,15 @@ def main(argv=None) -> int:
                     help="with --sizes: also time the vendor library on the same inputs (context)")
     args = ap.parse_args(argv)
 
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be at least 1 and --warmup at least 0", file=sys.stderr)
+        return 2
     if args.tune and args.pad_k:
         print("--tune times dense operand rows; it does not combine with --pad-k", file=sys.stderr)
+        return 2
+    if args.tune and (args.remap or args.row_major or args.schedule != "interleave"):
+        print("--tune picks the grid order of the default launch; it does not combine with "
+              "--remap, --row-major or --schedule", file=sys.stderr)
         return 2
     if args.gpus != 1:
         print("bench.py measures one GPU only: this GEMM path is single-GPU "
@@ -715,7 +722,7 @@ def main(argv=None) -> int:
         steps = args.steps
         res = bench_one(w, steps, args.warmup, opts, args.schedule,
                         with_cpu=(not args.no_cpu_baseline), deadline_s=args.deadline,
-                        settle_ms=args.settle_ms, tune=args.tune and opts is None,
+                        settle_ms=args.settle_ms, tune=args.tune,
                         pad_k=args.pad_k)
         print(json.dumps(res), flush=True)
     return 0

@@ -22,6 +22,16 @@ def test_tune_with_padded_rows_is_refused(capsys):
     assert "--pad-k" in capsys.readouterr().err
 
 
+def test_step_counts_and_tune_combinations_are_refused(capsys):
+    for argv in (["--steps", "0"], ["--steps", "-3"], ["--warmup", "-1"]):
+        assert bench.main(argv) == 2, argv
+        assert "--steps" in capsys.readouterr().err
+    for argv in (["--tune", "--remap", "8,32"], ["--tune", "--row-major"],
+                 ["--tune", "--schedule", "pingpong"]):
+        assert bench.main(argv) == 2, argv
+        assert "--tune" in capsys.readouterr().err
+
+
 def test_clock_from_trace_decodes_a_known_record():
     # 2 launches x 16 workgroups; workgroup b on XCD b % 8 at (1500 + 20 x) MHz:
     # shader-clock ticks = MHz / 100 per real-time tick
