@@ -586,12 +586,18 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(const GemmParams p)
     auto a_off = [&](int k) { return (k & 1) * kPanelBytes; };
     auto b_off = [&](int k) { return kBRing + (k % kBPanels) * kPanelBytes; };
     auto b_off2 = [&](int k) { return kBRing + (k & 1) * kPanelBytes; };
-    // this wave's 4 of the 8-row groups u = base + w4 + 4 v of a K step's panel
+    // this wave's 4 of the 8-row groups u = base + w4 + 4 v of a K step's panel.
+    // The K step's scalar offset goes through readfirstlane: it is uniform,
+    // but the compiler otherwise keeps its per-group strength-reduced copies
+    // in vector registers and wraps every e4m3 ping-pong load in a loop over
+    // the distinct lane values (about 9 % more cycles per K step).
     auto load_a = [&](int k, int off, int base) {
-        dma_panel_part<4>(ra, smem + off, base, w4, k == 0 ? va_first : va, soff(k), pa);
+        dma_panel_part<4>(ra, smem + off, base, w4, k == 0 ? va_first : va,
+                          __builtin_amdgcn_readfirstlane(soff(k)), pa);
     };
     auto load_b = [&](int k, int off, int base) {
-        dma_panel_part<4>(rb, smem + off, base, w4, k == 0 ? vb_first : vb, soff(k), pb);
+        dma_panel_part<4>(rb, smem + off, base, w4, k == 0 ? vb_first : vb,
+                          __builtin_amdgcn_readfirstlane(soff(k)), pb);
     };
 
     if (kSched == kLockstep) {
