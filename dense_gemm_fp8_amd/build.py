@@ -53,6 +53,43 @@ def scratch_users(report: str) -> list[tuple[str, str, int]]:
     return bad
 
 
+def waterfall_loops(asm: str) -> list[tuple[str, str]]:
+    """(function, loop label) of every loop in a gfx950 assembly listing that
+    branches back on a non-empty exec mask (s_cbranch_execnz) and issues a
+    buffer load.  The compiler emits such a loop when an operand that must be
+    scalar (a buffer load's soffset or resource) is held in a vector register:
+    it loads once per distinct lane value.  The GEMM kernels pass only uniform
+    values there, so any such loop is a code-generation regression (it once
+    cost the e4m3 ping-pong 9 % of its cycles per K step)."""
+    found, fn, labels, body_start = [], None, {}, {}
+    lines = asm.splitlines()
+    for i, line in enumerate(lines):
+        m = re.match(r"^([A-Za-z_.$][\w.$]*):", line)
+        if m and not m.group(1).startswith(".L"):
+            fn, labels = m.group(1), {}
+            continue
+        m = re.match(r"^(\.LBB\w+):", line)
+        if m:
+            labels[m.group(1)] = i
+            continue
+        m = re.match(r"\s+s_cbranch_execnz\s+(\.LBB\w+)", line)
+        if m and m.group(1) in labels:
+            body = lines[labels[m.group(1)]:i]
+            if any(re.match(r"\s+buffer_load", x) for x in body):
+                found.append((fn, m.group(1)))
+    return found
+
+
+def device_asm(out: str) -> None:
+    """Compile the kernels' source to gfx950 assembly (device code only) with
+    the library's flags, into `out`."""
+    cmd = [hipcc(), *HIPCC_FLAGS, "--cuda-device-only", "-S", "-x", "hip",
+           os.path.join(CSRC, "gemm_kernels.hip"), "-I", os.path.join(ROOT, "include"), "-o", out]
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + res.stderr[-3000:])
+
+
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     """Compile every source into dense_gemm_fp8_amd/libhkg.so (always rebuilds);
     fails if a kernel uses scratch memory or spills registers."""
