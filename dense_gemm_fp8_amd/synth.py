@@ -200,6 +200,41 @@ def small_int_e4m3(seed: int, rows: int, cols: int, lo: int = -4, hi: int = 4) -
     return e4m3_encode(v)
 
 
+def ternary(seed: int, rows: int, cols: int, dtype: str) -> np.ndarray:
+    """Entries in {-1, 0, 1} as bf16 bits (uint16) or e4m3 codes (uint8), one
+    random byte each (bytes 0-84 give -1, 85-169 and 255 give 0, 170-254 give
+    1), so that operands of gigabytes take seconds to make."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    n = rows * cols
+    words = g.integers(0, 1 << 64, size=-(-n // 8), dtype=np.uint64, endpoint=False)
+    raw = words.view(np.uint8)[:n].reshape(rows, cols)
+    code = (np.uint16 if dtype == "bf16" else np.uint8)
+    neg, one = (0xBF80, 0x3F80) if dtype == "bf16" else (0xB8, 0x38)   # -1.0, 1.0
+    table = np.zeros(256, dtype=code)
+    table[:85], table[170:255] = neg, one
+    return table[raw]
+
+
+def ternary_long(seed: int, rows: int, cols: int, dtype: str, chunk: int = 1 << 16) -> np.ndarray:
+    """Rows of gigabytes with entries in {-1, 0, 1}, made in one write pass:
+    each row is a run of `chunk`-element pieces, piece j of row r being row r
+    of one random ternary() block with its sign flipped by a random bit per
+    (r, j) (sign-bit XOR; a flipped 0 is -0).  An offset error of whole pieces
+    therefore meets the opposite sign half the time, and any other offset
+    meets different random entries."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    w = min(chunk, cols)
+    block = ternary(int(g.integers(1 << 62)), rows, w, dtype)
+    pieces = -(-cols // w)
+    bit = 0x8000 if dtype == "bf16" else 0x80
+    masks = g.integers(0, 2, size=(rows, pieces)).astype(block.dtype) * block.dtype.type(bit)
+    out = np.empty((rows, cols), dtype=block.dtype)
+    for j in range(pieces):
+        lo, hi = j * w, min(cols, (j + 1) * w)
+        np.bitwise_xor(block[:, :hi - lo], masks[:, j:j + 1], out=out[:, lo:hi])
+    return out
+
+
 def sample_pairs(seed: int, M: int, N: int, count: int, tile: int = 256) -> tuple[np.ndarray, np.ndarray]:
     """Sampled output coordinates (m, n) that touch every output tile.
 

@@ -656,6 +656,51 @@ def test_long_k_exact(dtype):
         np.testing.assert_array_equal(cb[pm, pn], synth.f32_to_bf16_bits(want.astype(np.float32)))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_max_k_panels_exact(dtype):
+    """The largest K the entry points accept: bf16 K = 2^22 - 8, e4m3 K = 2^23
+    - 16, where one 256-row operand panel spans just under 2 GiB and the
+    loads' buffer offsets reach 97 % of 2^31 (one K granule more is refused).
+    Entries in {-1, 0, 1} keep every partial sum an integer below 2^24, so the
+    fp32 copy is exact in any order; it is compared bit for bit on sampled
+    outputs of the default launch (128 x 128 tiles at this size), 256 x 256
+    4-wave tiles and the ping-pong, which share the operands on the GPU."""
+    import time
+    M = N = 257
+    dt, granule = (0, 8) if dtype == "bf16" else (1, 16)
+    K = (1 << 22) - granule if dtype == "bf16" else (1 << 23) - granule
+    assert hkg.launch_plan(M, N, K + granule, dt)[0] == hkg.HKG_ERR_SIZE
+    assert hkg.launch_plan(M, N, K, dt)[0] == hkg.HKG_OK
+    _say("max K %s %dx%dx%d" % (dtype, M, N, K))
+    t0 = time.time()
+    A = synth.ternary_long(9981, M, K, dtype)
+    B = synth.ternary_long(9982, N, K, dtype)
+    pm, pn = synth.sample_pairs(9983, M, N, 150)
+    if dtype == "bf16":
+        want = oracle.gemm_bf16_pairs(A, B, pm, pn)
+        dA, dB = _dev_bf16(A), _dev_bf16(B)
+    else:
+        want = oracle.gemm_fp8_pairs(A, B, 1.0, 1.0, pm, pn)
+        dA, dB = _dev_u8(A), _dev_u8(B)
+    del A, B
+    assert np.all(want == np.round(want)) and np.abs(want).max() < 1 << 24
+    _say("  inputs and oracle: %.1f s" % (time.time() - t0))
+    wf = want.astype(np.float32)
+    for opts in (None, hkg.make_opts(schedule=hkg.HKG_SCHED_INTERLEAVE),
+                 hkg.make_opts(schedule=hkg.HKG_SCHED_PINGPONG)):
+        C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        Cf = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        if dtype == "bf16":
+            hkg.gemm_bf16(dA, dB, C, Cf, opts=opts)
+        else:
+            hkg.gemm_fp8(dA, dB, 1.0, 1.0, C, Cf, opts=opts)
+        torch.cuda.synchronize()
+        cb, cf = _host_bits(C), Cf.cpu().numpy()
+        np.testing.assert_array_equal(cf[pm, pn], wf)
+        np.testing.assert_array_equal(cb[pm, pn], synth.f32_to_bf16_bits(wf))
+    _say("  done: %.1f s" % (time.time() - t0))
+
+
 # ------------------------------------------------------- split default launch -------
 
 def _split_rows(M, N):
