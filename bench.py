@@ -172,34 +172,48 @@ def clock_from_trace(rec: np.ndarray, launches: int) -> dict:
             "workgroups_per_launch": int(rec.shape[1])}
 
 
-def cpu_baseline(w: synth.Workload, A, B, sa, sb, target_s: float = 12.0) -> dict:
-    """The oracle as it stands, timed on this host on a sample of whole output rows."""
+def cpu_baseline(w: synth.Workload, A, B, sa, sb, target_s: float = 12.0,
+                 gpu_rows=None) -> tuple[dict, dict | None]:
+    """The oracle as it stands, timed on this host on a sample of whole output
+    rows; and, when gpu_rows(rows) gives the GPU's (C_f32, C_bf16 bits) of
+    those rows, the acceptance statistics of the GPU output on them."""
     import oracle
+    from oracle import parity
     threads = oracle.default_threads()
     flops_per_row = 2.0 * w.N * w.K
 
     def run(rows):
-        pm = np.repeat(np.arange(rows, dtype=np.int64) * max(1, w.M // rows), w.N)
+        idx = np.arange(rows, dtype=np.int64) * max(1, w.M // rows)
+        pm = np.repeat(idx, w.N)
         pn = np.tile(np.arange(w.N, dtype=np.int64), rows)
         t0 = time.perf_counter()
         if w.dtype == "bf16":
-            oracle.gemm_bf16_pairs(A, B, pm, pn, threads=threads)
+            ref = oracle.gemm_bf16_pairs(A, B, pm, pn, threads=threads)
         elif w.dtype == "mxfp8":
-            oracle.gemm_mxfp8_pairs(A, B, sa, sb, pm, pn, threads=threads)
+            ref = oracle.gemm_mxfp8_pairs(A, B, sa, sb, pm, pn, threads=threads)
         else:
-            oracle.gemm_fp8_pairs(A, B, sa, sb, pm, pn, threads=threads)
-        return time.perf_counter() - t0
+            ref = oracle.gemm_fp8_pairs(A, B, sa, sb, pm, pn, threads=threads)
+        return time.perf_counter() - t0, idx, ref
 
     probe_rows = max(1, threads // 2)
-    dt = run(probe_rows)
+    dt, _, _ = run(probe_rows)
     rate = probe_rows * flops_per_row / dt
     rows = int(min(w.M, max(probe_rows, round(target_s * rate / flops_per_row))))
-    dt = run(rows)
-    return {"value": rows * flops_per_row / dt / 1e12, "unit": "TFLOPS", "cores": threads,
+    dt, idx, ref = run(rows)
+    sample = "%d full output rows (x %d columns, K=%d) of %s" % (rows, w.N, w.K, w.name)
+    info = {"value": rows * flops_per_row / dt / 1e12, "unit": "TFLOPS", "cores": threads,
             "cores_in_affinity_mask": oracle.affinity_cores(),
             "kind": "oracle",
-            "sample": "%d full output rows (x %d columns, K=%d) of %s, fp64, %.1f s wall"
-                      % (rows, w.N, w.K, w.name, dt)}
+            "sample": "%s, fp64, %.1f s wall" % (sample, dt)}
+    check = None
+    if gpu_rows is not None:
+        c32, cb = gpu_rows(idx)
+        check = parity.stats(ref, c32.reshape(-1), cb.reshape(-1), w.K)
+        check["sample"] = "the CPU baseline's %s, against its fp64 values" % sample
+        check["rule"] = ("(i) |C_f32 - ref| <= tol = 1e-3 sqrt(K); (ii) C_bf16 = RNE(C_f32); "
+                         "(iii) C_bf16 within 1 bf16 ulp of RNE(ref) where that ulp exceeds tol, "
+                         "else within tol + ulp/2 of ref")
+    return info, check
 
 
 def launch_plan(w: synth.Workload, opts) -> list:
@@ -402,12 +416,35 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
         "gpu": torch.cuda.get_device_name(dev),
         "box": gpu_identity(),
     }
-    del dA, dB, C
     if with_cpu:
-        res["cpu_baseline"] = cpu_baseline(w, A, B, sa, sb)
+        # one more (untimed) launch of the same configuration that also writes
+        # the fp32 copy, for the parity of the rows the CPU baseline computes
+        Cf = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+        o = opts
+        if w.dtype == "bf16":
+            hkg.gemm_bf16(dA, dB, C, Cf, opts=o, stream=stream)
+        elif w.dtype == "mxfp8":
+            hkg.gemm_mxfp8(dA, dB, pSA, pSB, C, Cf, opts=o, stream=stream)
+        else:
+            hkg.gemm_fp8(dA, dB, sa, sb, C, Cf, opts=o, stream=stream)
+        done = torch.cuda.Event()
+        done.record(stream)
+        wait_event(done, deadline_s, "parity launch")
+        del dA, dB
+
+        def gpu_rows(idx):
+            rows = torch.from_numpy(idx).to(dev)
+            c32 = Cf.index_select(0, rows).cpu().numpy()
+            cb = C.index_select(0, rows).view(torch.int16).cpu().numpy().view(np.uint16)
+            return c32, cb
+
+        res["cpu_baseline"], res["parity"] = cpu_baseline(w, A, B, sa, sb, gpu_rows=gpu_rows)
         res["vs_cpu_baseline"] = round(tflops / res["cpu_baseline"]["value"], 1)
+        del C, Cf
     else:
+        del dA, dB, C
         res["cpu_baseline"] = None
+        res["parity"] = None
     return res
 
 

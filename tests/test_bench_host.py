@@ -1,5 +1,6 @@
 """Host-side logic of bench.py (no GPU): argument limits, the time-record
-decoder, the counter facts and the Eq. 1 field."""
+decoder, the counter facts, the Eq. 1 field and the CPU-baseline leg's parity
+record."""
 import json
 import os
 import sys
@@ -10,6 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
+from dense_gemm_fp8_amd import synth  # noqa: E402
 
 
 def test_more_than_one_gpu_is_refused(capsys):
@@ -83,3 +85,35 @@ def test_eq1_l2_term():
     assert abs(c["eq1"]["l2_term_tbs"] - 0.8 * bench.EQ1_L2_BW_TBS) < 0.006
     assert c["eq1"]["llc_term_tbs"] is None
     assert bench.cache_fields({})["eq1"]["l2_term_tbs"] is None
+
+
+def test_cpu_baseline_reports_parity_of_the_rows_it_computes():
+    """bench's CPU-baseline leg compares the GPU output of the rows it computes
+    with its fp64 values; fed the oracle's own product (and one flipped code)
+    it reports a pass (and the flip)."""
+    import oracle
+    from oracle import parity
+    w = synth.workload(1)                      # bf16 256^3
+    A, B, sa, sb = synth.make_inputs(w)
+    full = oracle.gemm_bf16(A, B)
+    c32 = full.astype(np.float32)
+    cb = parity.f32_to_bf16_rne(c32)
+    seen = []
+
+    def rows(idx):
+        seen.append(idx)
+        return c32[idx], cb[idx]
+
+    info, check = bench.cpu_baseline(w, A, B, sa, sb, target_s=0.05, gpu_rows=rows)
+    assert info["kind"] == "oracle" and info["value"] > 0
+    assert check["pass"] and check["checked"] == len(seen[-1]) * w.N
+    # fp64 -> fp32 -> bf16 may differ from one rounding of fp64 by a code
+    assert check["ulp_hist"][">=2"] == 0 and check["max_abs_err"] < 1e-4
+    bad = cb.copy()
+    bad[seen[-1][0], 3] ^= 1
+
+    info, check = bench.cpu_baseline(w, A, B, sa, sb, target_s=0.05,
+                                     gpu_rows=lambda idx: (c32[idx], bad[idx]))
+    assert not check["pass"] and check["fail_ii"] == 1
+    info, check = bench.cpu_baseline(w, A, B, sa, sb, target_s=0.05)
+    assert check is None
