@@ -25,6 +25,3 @@ def build(out: str = EXE) -> str:
     subprocess.run(command(out), check=True)
     return out
 
-
-if __name__ == "__main__":
-    print(build())
