@@ -60,9 +60,9 @@
 //   kPingPong  8-wave ping-pong.  Group 0 (waves 0-3, one per SIMD) and group
 //              1 (waves 4-7) run one barrier apart: while one group issues its
 //              MFMA cluster at s_setprio 3 the other issues the next K steps'
-//              HBM->LDS loads and reads the first half of its own next
-//              cluster's fragments from LDS into registers, so a cluster
-//              starts with MFMAs instead of waiting for LDS.  Group 1 starts
+//              HBM->LDS loads and reads all of its own next cluster's
+//              fragments from LDS into registers, so a cluster holds no LDS
+//              instruction and starts with MFMAs.  Group 1 starts
 //              with a memory phase, which staggers it one phase behind group 0:
 //              the conditional extra barrier wait that the pages' GEMM entry
 //              gives one wave group (HipKittens L2 note, section 7 code
