@@ -235,6 +235,18 @@ def ternary_long(seed: int, rows: int, cols: int, dtype: str, chunk: int = 1 << 
     return out
 
 
+def e8m0_near_one(seed: int, rows: int, blocks: int) -> np.ndarray:
+    """E8M0 block scales uniform in {126, 127, 128} (x0.5, x1, x2), one random
+    byte each as in ternary(), for MXFP8 operands of gigabytes."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    n = rows * blocks
+    words = g.integers(0, 1 << 64, size=-(-n // 8), dtype=np.uint64, endpoint=False)
+    raw = words.view(np.uint8)[:n].reshape(rows, blocks)
+    table = np.full(256, 127, dtype=np.uint8)
+    table[:85], table[170:255] = 126, 128
+    return table[raw]
+
+
 def sample_pairs(seed: int, M: int, N: int, count: int, tile: int = 256) -> tuple[np.ndarray, np.ndarray]:
     """Sampled output coordinates (m, n) that touch every output tile.
 

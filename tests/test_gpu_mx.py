@@ -120,6 +120,42 @@ def test_long_k_exact():
         np.testing.assert_array_equal(cb[pm, pn], oracle.bf16_round(want))
 
 
+def test_max_k_exact():
+    """The largest MXFP8 K the entry point accepts, 2^23 - 32 (a 256-row e4m3
+    panel just under 2 GiB; one more block is refused), at 257 x 257.
+    Elements in {-1, 0, 1} with block scales 2^-1, 2^0 or 2^1 make every
+    product one of +-1/4 ... +-4, inside one MFMA's exact window, and every
+    partial sum a multiple of 1/4 far below 2^22: the fp32 copy is exact and
+    is compared bit for bit on sampled outputs of both tile kernels."""
+    import time
+    M = N = 257
+    K = (1 << 23) - 32
+    assert hkg.launch_plan(M, N, K + 32, 2)[0] == hkg.HKG_ERR_SIZE
+    assert hkg.launch_plan(M, N, K, 2)[0] == hkg.HKG_OK
+    _say("mx max K %dx%dx%d" % (M, N, K))
+    t0 = time.time()
+    A, B = synth.ternary_long(9391, M, K, "fp8"), synth.ternary_long(9392, N, K, "fp8")
+    SA, SB = synth.e8m0_near_one(9393, M, K // 32), synth.e8m0_near_one(9394, N, K // 32)
+    pm, pn = synth.sample_pairs(9395, M, N, 150)
+    want = oracle.gemm_mxfp8_pairs(A, B, SA, SB, pm, pn)
+    assert np.all(want * 4 == np.round(want * 4)) and np.abs(want).max() < 1 << 22
+    pa = hkg.mx_pack_scales(_dev(SA), hkg.HKG_MX_OPERAND_A)
+    pb = hkg.mx_pack_scales(_dev(SB), hkg.HKG_MX_OPERAND_B)
+    dA, dB = _dev(A), _dev(B)
+    del A, B
+    _say("  inputs and oracle: %.1f s" % (time.time() - t0))
+    for opts in (None, hkg.make_opts(schedule=hkg.HKG_SCHED_INTERLEAVE)):
+        C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        Cf = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        hkg.gemm_mxfp8(dA, dB, pa, pb, C, Cf, opts=opts)
+        torch.cuda.synchronize()
+        cb = C.view(torch.int16).cpu().numpy().view(np.uint16)
+        cf = Cf.cpu().numpy()
+        np.testing.assert_array_equal(cf[pm, pn].astype(np.float64), want)
+        np.testing.assert_array_equal(cb[pm, pn], oracle.bf16_round(want))
+    _say("  done: %.1f s" % (time.time() - t0))
+
+
 def test_unit_scales_equal_per_tensor_fp8():
     _say("mx unit scales vs fp8")
     M, N, K = 512, 512, 512
