@@ -517,6 +517,49 @@ def test_full_size_workload_every_entry(idx):
         _say("full-size %s %s: every entry within tol %.4g: %s" % (w.name, name, w.tol, acc))
 
 
+@pytest.mark.parametrize("idx", [2, 3, 4, 5])
+def test_full_size_every_kernel_bit_identical_to_default(idx):
+    """Every other kernel at every full-size workload: lockstep, 4-wave on
+    128 x 128 and 192 x 192 tiles, and 4-wave on 256 x 256 tiles in row-major
+    order.  Each sums every 16 x 16 block's K steps in the same order, so C
+    and C_f32 must equal the default launch's bit for bit (compared on the
+    device); with the every-entry oracle comparison of the default launch
+    above, every kernel meets the oracle on every entry."""
+    w = synth.workload(idx)
+    _say("full-size %s: every kernel vs default" % w.name)
+    A, B, sa, sb = synth.make_inputs(w)
+    if w.dtype == "bf16":
+        dA, dB = _dev_bf16(A), _dev_bf16(B)
+    else:
+        dA, dB = _dev_u8(A), _dev_u8(B)
+    del A, B
+
+    def launch(opts):
+        C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+        Cf = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        if w.dtype == "bf16":
+            hkg.gemm_bf16(dA, dB, C, Cf, opts=opts)
+        else:
+            hkg.gemm_fp8(dA, dB, sa, sb, C, Cf, opts=opts)
+        torch.cuda.synchronize()
+        return C.view(torch.int16), Cf.view(torch.int32)
+
+    ref_c, ref_f = launch(None)
+    others = [("lockstep", hkg.make_opts(schedule=hkg.HKG_SCHED_LOCKSTEP)),
+              ("interleave128", hkg.make_opts(schedule=hkg.HKG_SCHED_INTERLEAVE_128)),
+              ("interleave192", hkg.make_opts(schedule=hkg.HKG_SCHED_INTERLEAVE_192)),
+              ("interleave row-major", hkg.make_opts(remap=hkg.HKG_REMAP_ROW_MAJOR,
+                                                     schedule=hkg.HKG_SCHED_INTERLEAVE))]
+    for name, opts in others:
+        _say("full-size %s: %s" % (w.name, name))
+        c, f = launch(opts)
+        assert torch.equal(c, ref_c), "%s %s: bf16 output differs from the default launch" % (w.name, name)
+        assert torch.equal(f, ref_f), "%s %s: fp32 output differs from the default launch" % (w.name, name)
+        del c, f
+    del dA, dB, ref_c, ref_f
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- ragged shapes ----
 
 RAGGED_BF16 = [(1, 1, 8), (17, 33, 72), (255, 257, 200), (300, 520, 136), (513, 777, 1000)]
