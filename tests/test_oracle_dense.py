@@ -134,3 +134,49 @@ def test_rejects_bad_inputs():
         dense.DenseReference("fp8", np.zeros((2, 4), np.uint8), np.zeros((2, 5), np.uint8))
     with pytest.raises(ValueError):
         dense.DenseReference("fp16", np.zeros((2, 4), np.uint16), np.zeros((2, 4), np.uint16))
+
+
+# ---- MXFP8 (e4m3 elements, one E8M0 scale per 32 along K) -------------------
+
+def test_mxfp8_decoder_matches_torch_and_ldexp():
+    torch = pytest.importorskip("torch")
+    codes = np.tile(np.arange(256, dtype=np.uint8), 4).reshape(8, 128)      # every code, 4 blocks a row
+    scales = np.array([[0, 100, 127, 254], [1, 126, 128, 255]] * 4, dtype=np.uint8)
+    got = dense.decode_mxfp8(codes, scales)
+    e4 = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    want = np.ldexp(e4, np.repeat(scales.astype(np.int64) - 127, 32, axis=1))
+    want[np.repeat(scales == 255, 32, axis=1)] = np.nan                      # E8M0 0xFF is NaN
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (3, 5, 64), (4, 2, 96)])
+def test_mxfp8_brute_force_exact(M, N, K):
+    A, SA = synth.mx_quantize(synth.normal_f32(9081 + M, M, K))
+    B, SB = synth.mx_quantize(synth.normal_f32(9082 + N, N, K))
+    got = dense.gemm_mxfp8(A, B, SA, SB)
+    tab = oracle.e4m3_table()
+    for m in range(M):
+        for n in range(N):
+            ex = sum((Fraction(float(tab[A[m, k]])) * Fraction(2) ** (int(SA[m, k // 32]) - 127) *
+                      Fraction(float(tab[B[n, k]])) * Fraction(2) ** (int(SB[n, k // 32]) - 127)
+                      for k in range(K)), Fraction(0))
+            assert Fraction(float(got[m, n])) == ex        # exact: K small, power-of-two scales
+
+
+def test_mxfp8_matches_plain_oracle():
+    M, N, K = 200, 150, 1024
+    A, SA = synth.mx_quantize(synth.normal_f32(9091, M, K))
+    B, SB = synth.mx_quantize(synth.normal_f32(9092, N, K))
+    got, want = dense.gemm_mxfp8(A, B, SA, SB), oracle.gemm_mxfp8(A, B, SA, SB)
+    av, bv = np.abs(dense.decode_mxfp8(A, SA)), np.abs(dense.decode_mxfp8(B, SB))
+    assert np.all(np.abs(got - want) <= av @ bv.T * (2 * K * 2.0 ** -53))
+    ref = dense.DenseReference("mxfp8", A, B, SA, SB)
+    np.testing.assert_array_equal(np.concatenate([ref.rows(a, b) for a, b in
+                                                  ref.row_blocks(max_flops=2.0 * N * K * 64)]), got)
+
+
+def test_mxfp8_rejects_mismatched_scales():
+    with pytest.raises(ValueError):
+        dense.DenseReference("mxfp8", np.zeros((2, 64), np.uint8), np.zeros((3, 64), np.uint8),
+                             np.zeros((2, 2), np.uint8), np.zeros((3, 1), np.uint8))
