@@ -856,12 +856,31 @@ def test_graph_capture_replays_match_eager():
     replay, with other eager work and synchronisations in between, gives the
     eager result bit for bit (the default split launch included)."""
     _say("graph capture")
-    shapes = [(2048, 2048, 512, "bf16"), (4352, 4352, 256, "bf16"), (1024, 768, 256, "fp8")]
+    shapes = [(2048, 2048, 512, "bf16"), (4352, 4352, 256, "bf16"), (1024, 768, 256, "fp8"),
+              (1024, 512, 256, "mxfp8"), (700, 520, 264, "bf16 pitched")]
     for M, N, K, dtype in shapes:
         if dtype == "bf16":
             A = _dev_bf16(synth.f32_to_bf16_bits(synth.normal_f32(9900 + M, M, K)))
             B = _dev_bf16(synth.f32_to_bf16_bits(synth.normal_f32(9901 + N, N, K)))
             call = lambda C, s: hkg.gemm_bf16(A, B, C, stream=s)
+        elif dtype == "bf16 pitched":
+            # operand and output rows further apart than their length (views)
+            A = _dev_bf16(synth.f32_to_bf16_bits(synth.normal_f32(9904, M, K + 72)))[:, 8:8 + K]
+            B = _dev_bf16(synth.f32_to_bf16_bits(synth.normal_f32(9905, N, K + 64)))[:, :K]
+            wide = torch.zeros((M, N + 24), dtype=torch.bfloat16, device="cuda")
+            call = lambda C, s: (hkg.gemm_bf16(A, B, wide[:, :N], stream=s), C.copy_(wide[:, :N]))
+        elif dtype == "mxfp8":
+            # the whole MXFP8 step: both scale packs, then the GEMM
+            a, sa_ = synth.mx_quantize(synth.normal_f32(9906, M, K))
+            b, sb_ = synth.mx_quantize(synth.normal_f32(9907, N, K))
+            A, B, SA, SB = _dev_u8(a), _dev_u8(b), _dev_u8(sa_), _dev_u8(sb_)
+            pa = torch.empty((hkg.hkg_mx_packed_scale_bytes(M, K),), dtype=torch.uint8, device="cuda")
+            pb = torch.empty((hkg.hkg_mx_packed_scale_bytes(N, K),), dtype=torch.uint8, device="cuda")
+
+            def call(C, s):
+                hkg.mx_pack_scales(SA, hkg.HKG_MX_OPERAND_A, pa, stream=s)
+                hkg.mx_pack_scales(SB, hkg.HKG_MX_OPERAND_B, pb, stream=s)
+                hkg.gemm_mxfp8(A, B, pa, pb, C, stream=s)
         else:
             a, sa = synth.e4m3_quantize(synth.normal_f32(9902, M, K))
             b, sb = synth.e4m3_quantize(synth.normal_f32(9903, N, K))
@@ -877,6 +896,11 @@ def test_graph_capture_replays_match_eager():
             call(C, s)
         for rep in range(3):
             C.fill_(0.0)
+            if dtype == "mxfp8":
+                pa.fill_(0)
+                pb.fill_(0)
+            elif dtype == "bf16 pitched":
+                wide.fill_(0.0)
             x = torch.randn(512, 512, device="cuda")      # unrelated eager work
             (x @ x).sum().item()
             g.replay()
