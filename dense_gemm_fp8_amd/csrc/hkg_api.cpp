@@ -472,7 +472,9 @@ const char *hkg_status_string(int status)
     case HKG_ERR_SHAPE:
         return "unsupported shape (negative, or K not a multiple of 8 bf16 / 16 e4m3 / 32 MXFP8)";
     case HKG_ERR_ALIGN: return "pointer not 16-byte aligned";
-    case HKG_ERR_SIZE: return "operand panel exceeds the 32-bit buffer range";
+    case HKG_ERR_SIZE:
+        return "size beyond the 32-bit limits (a 2 GiB operand panel, M, N or ldc of 2^31, "
+               "2^30 tiles, or 2 GiB of packed MXFP8 scales)";
     case HKG_ERR_OPTS: return "invalid hkg_gemm_opts";
     case HKG_ERR_DEVICE: return "the stream's device is not a gfx950, or could not be queried";
     case HKG_ERR_LAUNCH: return "kernel launch failed";

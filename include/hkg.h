@@ -57,7 +57,10 @@ typedef enum {
     HKG_ERR_SHAPE = -2,   /* M, N, K negative, or K not a multiple of 8 (bf16) / 16 (e4m3)
                              / 32 (MXFP8)                                            */
     HKG_ERR_ALIGN = -3,   /* a pointer is not 16-byte aligned                        */
-    HKG_ERR_SIZE = -4,    /* a per-tile operand panel exceeds the 32-bit buffer range */
+    HKG_ERR_SIZE = -4,    /* beyond the 32-bit limits: a 256-row operand panel of
+                             2 GiB or more (256 * pitch * element size), M, N or
+                             ldc of 2^31 or more, 2^30 tiles, or 2 GiB of packed
+                             MXFP8 scales                                         */
     HKG_ERR_OPTS = -5,    /* invalid hkg_gemm_opts                                   */
     HKG_ERR_DEVICE = -6,  /* the device of `stream` (NULL: the current device) is not
                              a gfx950, or could not be queried; nothing launched  */
@@ -131,7 +134,8 @@ typedef struct {
  * (HKG_ERR_ALIGN); ldc >= N (C rows are then written element by element unless
  * N and ldc are multiples of 8); 0 selects the dense pitch; a pitch below its
  * extent or negative is HKG_ERR_OPTS; 256 * pitch * element size must stay
- * below 2^31 (HKG_ERR_SIZE).  The bytes between rows are neither read into the
+ * below 2^31 and ldc below 2^31 (HKG_ERR_SIZE; any larger value, up to
+ * INT64_MAX, is refused without being multiplied).  The bytes between rows are neither read into the
  * result nor written.  Overlap checks take each matrix to span its first to
  * its last element.
  */
