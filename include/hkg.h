@@ -187,7 +187,7 @@ int hkg_gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
  *                                + steps * 2^-24 * sum_k |a_k b_k| ),
  * and sums whose products all lie within that window (e.g. small integers)
  * are exact.  For per-tensor-quantised N(0,1) data the error is far smaller
- * (8192^3: max 0.006 against 1e-3 * sqrt(K) = 0.09).
+ * (8192^3, every entry: max 0.009 against 1e-3 * sqrt(K) = 0.09).
  */
 int hkg_gemm_fp8(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
                  float scale_a, float scale_b, void *C, float *C_f32, void *stream);
@@ -255,8 +255,8 @@ int hkg_mx_pack_scales(int32_t operand, int64_t rows, int64_t K, const void *sca
 
 /*
  * The (W, C) the library uses for HKG_REMAP_DEFAULT on a shape (host only, no
- * HIP call).  dtype: 0 = bf16, 1 = fp8, 2 = MXFP8.  Returns HKG_ERR_NULL/SHAPE
- * on bad input.  The grid is that of the default call's first launch
+ * HIP call).  dtype: 0 = bf16, 1 = fp8, 2 = MXFP8.  Returns HKG_ERR_NULL,
+ * HKG_ERR_SHAPE or HKG_ERR_SIZE as hkg_launch_plan does on bad input.  The grid is that of the default call's first launch
  * (hkg_launch_plan: W[0], C[0]; tiles of 256, or of 128 / 192 where
  * HKG_SCHED_DEFAULT picks them).  Rule (the L2 and LLC terms of the
  * HipKittens L2 note's section 4 equation): (8, 32) while an operand row
@@ -378,7 +378,9 @@ int hkg_tune_remap(int64_t M, int64_t N, int64_t K, int32_t dtype, const void *A
  * The grid remap itself (HipKittens L2 note, section 7 Algorithm 1 reading): flat
  * workgroup id b of a Gm x Gn tile grid -> output tile (tile_m, tile_n) for
  * window height W and chunk C.  Host function, no HIP call.  Returns
- * HKG_ERR_SHAPE if b is outside [0, Gm*Gn) or W, C < 1.
+ * HKG_ERR_NULL for a NULL output, HKG_ERR_SHAPE if Gm or Gn is below 1, either
+ * side or Gm*Gn reaches 2^30, W or C is below 1, or b is outside [0, Gm*Gn).
+ * W and C are clamped to the grid as hkg_remap_model describes.
  */
 int hkg_remap_tile(int64_t Gm, int64_t Gn, int32_t W, int32_t C, int64_t b,
                    int64_t *tile_m, int64_t *tile_n);
@@ -386,7 +388,10 @@ int hkg_remap_tile(int64_t Gm, int64_t Gn, int32_t W, int32_t C, int64_t b,
 /*
  * The same remap evaluated by the device code the GEMM kernels use: writes
  * out[2*b] = tile_m, out[2*b+1] = tile_n for every b in [0, Gm*Gn).
- *   out: device int32 array of 2*Gm*Gn elements, caller-owned.
+ *   out: device int32 array of 2*Gm*Gn elements, caller-owned, 4-byte aligned
+ *        (HKG_ERR_ALIGN).
+ * Grid checks as hkg_remap_tile (HKG_ERR_NULL, HKG_ERR_SHAPE), then the device
+ * check of every launching entry point.
  */
 int hkg_remap_tiles_device(int64_t Gm, int64_t Gn, int32_t W, int32_t C, int32_t *out,
                            void *stream);
