@@ -3,8 +3,6 @@
 The acceptance rule (i)-(iii) and its statistics live in oracle/parity.py;
 check() asserts that an output meets it.
 """
-import numpy as np
-
 from oracle.parity import bf16_to_f64, bf16_ulp, f32_to_bf16_rne, stats   # noqa: F401
 
 

@@ -1,7 +1,6 @@
 """Pins of the grid remap reading and of the Eq. 1 fit against the pages."""
 import itertools
 
-import numpy as np
 import pytest
 
 from oracle import eq1, remap
