@@ -14,9 +14,12 @@ then after --settle-ms (200) of untimed steps back to back ("value").  An idle
 MI355X under its power cap takes ~50-100 ms of load before its clock settles
 (it starts near 1.5 GHz, dips, then rises to its steady clock), and a short
 timed region right after an idle gap measures that ramp, not the kernel.
+Then K more launches run with cold caches, each after a 1 GiB buffer fill
+outside its events ("cold_cache", context only).
 
   python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload 2]
-                  [--settle-ms 200] [--all] [--remap W,C | --row-major | --tune]
+                  [--settle-ms 200] [--cold-mib 1024] [--all]
+                  [--remap W,C | --row-major | --tune]
                   [--schedule interleave|pingpong|lockstep|interleave128|interleave192]
                   [--no-cpu-baseline]
   python bench.py --clock-ramp 800 [--workload N | --all]
@@ -229,7 +232,7 @@ def launch_plan(w: synth.Workload, opts) -> list:
 
 def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
               with_cpu: bool, deadline_s: float = 120.0, settle_ms: float = 200.0,
-              tune: bool = False, pad_k: int = 0) -> dict:
+              tune: bool = False, pad_k: int = 0, cold_bytes: int = 1 << 30) -> dict:
     import torch
     import dense_gemm_fp8_amd as hkg
 
@@ -359,6 +362,29 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
                                "clock, not on the clock ramp that follows an idle GPU; from_idle "
                                "is the same W + K measurement without it" % settle_ms}
         per_launch_ms, region_ms, wall, clock_info = warm_then_time()
+    cold = None
+    if cold_bytes > 0:
+        # 3. context for `value`, which runs with warm caches: the same launches,
+        #    each after a fill of a cold_bytes buffer (outside its events) that
+        #    evicts the operands from every L2 and the last-level cache
+        scratch = torch.empty(cold_bytes // 4, dtype=torch.float32, device=dev)
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for i, (s, e) in enumerate(cev):
+            scratch.fill_(float(i))
+            step(s, e)
+        mark = torch.cuda.Event()
+        mark.record(stream)
+        wait_event(mark, deadline_s, "cold-cache launches")
+        torch.cuda.synchronize()
+        cold_ms = np.array([s.elapsed_time(e) for s, e in cev])
+        cold = {"flush_bytes": cold_bytes,
+                "kernel_ms_mean": round(float(cold_ms.mean()), 5),
+                "kernel_ms_median": round(float(np.median(cold_ms)), 5),
+                "TFLOPS": round(w.flops / (float(cold_ms.mean()) * 1e-3) / 1e12, 2),
+                "rule": "each of K launches after writing a %d MiB buffer; HIP events bracket the "
+                        "launch only" % (cold_bytes >> 20)}
+        del scratch
     ms_per_step = region_ms / steps
     tflops = w.flops / (ms_per_step * 1e-3) / 1e12
     kern_ms = float(per_launch_ms.mean())
@@ -411,6 +437,7 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
         "clock": clock_info,
         "settle": settle_info,
         "from_idle": from_idle,
+        "cold_cache": cold,
         "wall_s_timed_region": round(wall, 4),
         "kernel_source_hash": kernel_source_hash(),
         "gpu": torch.cuda.get_device_name(dev),
@@ -700,6 +727,9 @@ def main(argv=None) -> int:
     ap.add_argument("--deadline", type=float, default=120.0,
                     help="seconds to wait for the GPU to finish the warm-up or the timed "
                          "region before reporting a hang (exit status 3)")
+    ap.add_argument("--cold-mib", type=int, default=1024,
+                    help="after the timed region, time K more launches, each after writing a "
+                         "buffer of this many MiB (cold caches; reported as cold_cache, 0 skips)")
     ap.add_argument("--shape", type=str, default=None, help="M,N,K (custom size)")
     ap.add_argument("--dtype", choices=["bf16", "fp8", "mxfp8"], default="bf16")
     ap.add_argument("--sweep", type=str, default=None, help='"W,C W,C ..." grid orders to time')
@@ -709,6 +739,9 @@ def main(argv=None) -> int:
                     help="with --sizes: also time the vendor library on the same inputs (context)")
     args = ap.parse_args(argv)
 
+    if args.cold_mib < 0:
+        print("--cold-mib must be at least 0", file=sys.stderr)
+        return 2
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be at least 1 and --warmup at least 0", file=sys.stderr)
         return 2
@@ -760,7 +793,7 @@ def main(argv=None) -> int:
         res = bench_one(w, steps, args.warmup, opts, args.schedule,
                         with_cpu=(not args.no_cpu_baseline), deadline_s=args.deadline,
                         settle_ms=args.settle_ms, tune=args.tune,
-                        pad_k=args.pad_k)
+                        pad_k=args.pad_k, cold_bytes=args.cold_mib << 20)
         print(json.dumps(res), flush=True)
     return 0
 

@@ -32,6 +32,8 @@ def test_step_counts_and_tune_combinations_are_refused(capsys):
                  ["--tune", "--schedule", "pingpong"]):
         assert bench.main(argv) == 2, argv
         assert "--tune" in capsys.readouterr().err
+    assert bench.main(["--cold-mib", "-1"]) == 2
+    assert "--cold-mib" in capsys.readouterr().err
 
 
 def test_clock_from_trace_decodes_a_known_record():
