@@ -135,9 +135,9 @@ typedef struct {
  * N and ldc are multiples of 8); 0 selects the dense pitch; a pitch below its
  * extent or negative is HKG_ERR_OPTS; 256 * pitch * element size must stay
  * below 2^31 and ldc below 2^31 (HKG_ERR_SIZE; any larger value, up to
- * INT64_MAX, is refused without being multiplied).  The bytes between rows are neither read into the
- * result nor written.  Overlap checks take each matrix to span its first to
- * its last element.
+ * INT64_MAX, is refused without being multiplied).  The bytes between rows
+ * are neither read into the result nor written.  Overlap checks take each
+ * matrix to span its first to its last element.
  */
 
 /*
@@ -256,10 +256,11 @@ int hkg_mx_pack_scales(int32_t operand, int64_t rows, int64_t K, const void *sca
 /*
  * The (W, C) the library uses for HKG_REMAP_DEFAULT on a shape (host only, no
  * HIP call).  dtype: 0 = bf16, 1 = fp8, 2 = MXFP8.  Returns HKG_ERR_NULL,
- * HKG_ERR_SHAPE or HKG_ERR_SIZE as hkg_launch_plan does on bad input.  The grid is that of the default call's first launch
- * (hkg_launch_plan: W[0], C[0]; tiles of 256, or of 128 / 192 where
- * HKG_SCHED_DEFAULT picks them).  Rule (the L2 and LLC terms of the
- * HipKittens L2 note's section 4 equation): (8, 32) while an operand row
+ * HKG_ERR_SHAPE or HKG_ERR_SIZE as hkg_launch_plan does on bad input.  The
+ * grid is that of the default call's first launch (hkg_launch_plan: W[0],
+ * C[0]; tiles of 256, or of 128 / 192 where HKG_SCHED_DEFAULT picks them).
+ * Rule (the L2 and LLC terms of the HipKittens L2 note's section 4
+ * equation): (8, 32) while an operand row
  * holds at most 18944 bytes (K x element size), else (16, 4).  Both keep each
  * XCD's 32 concurrent tiles on 12 operand panels (the same L2 hit rate); the
  * second's 256 concurrent tiles share fewer panels (32 instead of 40), which
