@@ -175,6 +175,99 @@ def clock_from_trace(rec: np.ndarray, launches: int) -> dict:
             "workgroups_per_launch": int(rec.shape[1])}
 
 
+def metrics_reader():
+    """A callable returning GPU 0's gpu_metrics accumulators from amdsmi as
+    (mem_activity_acc, gfx_activity_acc, accumulation_counter,
+    vram_max_bandwidth in GB/s), or None where amdsmi or these fields are
+    unavailable.  The accumulators advance by the activity in percent per
+    tick of accumulation_counter and are refreshed about once a second."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+        keys = ("mem_activity_acc", "gfx_activity_acc", "accumulation_counter", "vram_max_bandwidth")
+
+        def read():
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            return tuple(m[k] for k in keys)
+        if not all(isinstance(v, int) for v in read()):
+            return None
+        return read
+    except Exception:  # pragma: no cover - no amdsmi / no device
+        return None
+
+
+def hbm_from_accumulators(a, b, launches_per_s: float) -> dict | None:
+    """HBM traffic from two gpu_metrics samples a, b (see metrics_reader) taken
+    at refreshes while the GPU ran one kind of launch back to back at
+    launches_per_s: activity in percent of vram_max_bandwidth, and bytes per
+    launch."""
+    ticks = b[2] - a[2]
+    if ticks <= 0 or launches_per_s <= 0:
+        return None
+    mem = (b[0] - a[0]) / ticks
+    bw = b[3] * 1e9
+    return {"mem_activity_pct": round(mem, 3), "gfx_activity_pct": round((b[1] - a[1]) / ticks, 2),
+            "bytes_per_s": round(mem / 100.0 * bw), "bytes_per_launch": round(mem / 100.0 * bw / launches_per_s),
+            "ticks": ticks, "vram_max_bandwidth_gbs": b[3]}
+
+
+def hbm_window(step, stream, window_s: float, deadline_s: float, read=None) -> dict | None:
+    """Launch `step` back to back (8 to 24 in flight) for about window_s + 2 s
+    and read the memory controllers' activity between two accumulator refreshes
+    inside that time: the first after 1.1 s of launches, the last at least
+    window_s later.  None without amdsmi."""
+    import torch
+    read = read or metrics_reader()
+    if read is None:
+        return None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks, n, a, b, first = [], 0, None, None, None
+    e0.record(stream)
+    t0 = time.perf_counter()
+    while b is None:
+        for _ in range(8):
+            step()
+        n += 8
+        e = torch.cuda.Event()
+        e.record(stream)
+        marks.append(e)
+        if len(marks) > 2:
+            wait_event(marks.pop(0), deadline_s, "HBM window")
+        now = time.perf_counter() - t0
+        if now < 1.1:
+            continue
+        cur = read()
+        if first is None:
+            first = cur
+        elif a is None:
+            if cur[2] != first[2]:
+                a, t_a = cur, now
+        elif now - t_a >= window_s and cur[2] != a[2] and cur[2] - a[2] >= 1000 * window_s:
+            b = cur
+        if now > window_s + 6.0:
+            break
+    e1.record(stream)
+    wait_event(e1, deadline_s, "HBM window")
+    torch.cuda.synchronize()
+    if a is None or b is None:
+        return None
+    out = hbm_from_accumulators(a, b, n / (e0.elapsed_time(e1) * 1e-3))
+    if out is not None:
+        out["launches"] = n
+        out["ms_per_launch"] = round(e0.elapsed_time(e1) / n, 5)
+    return out
+
+
+def llc_estimate(hbm_bytes_per_launch, past_l2_bytes_per_launch) -> float | None:
+    """Share of the bytes moving between the L2s and memory (FETCH_SIZE plus
+    WRITE_SIZE, reads and writes together) that never reach HBM, in percent:
+    the last-level cache's hit rate by bytes."""
+    if not hbm_bytes_per_launch or not past_l2_bytes_per_launch:
+        return None
+    return round(100.0 * max(0.0, 1.0 - hbm_bytes_per_launch / past_l2_bytes_per_launch), 1)
+
+
 def cpu_baseline(w: synth.Workload, A, B, sa, sb, target_s: float = 12.0,
                  gpu_rows=None) -> tuple[dict, dict | None]:
     """The oracle as it stands, timed on this host on a sample of whole output
@@ -232,7 +325,8 @@ def launch_plan(w: synth.Workload, opts) -> list:
 
 def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
               with_cpu: bool, deadline_s: float = 120.0, settle_ms: float = 200.0,
-              tune: bool = False, pad_k: int = 0, cold_bytes: int = 1 << 30) -> dict:
+              tune: bool = False, pad_k: int = 0, cold_bytes: int = 1 << 30,
+              hbm_window_s: float = 2.0) -> dict:
     import torch
     import dense_gemm_fp8_amd as hkg
 
@@ -362,9 +456,14 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
                                "clock, not on the clock ramp that follows an idle GPU; from_idle "
                                "is the same W + K measurement without it" % settle_ms}
         per_launch_ms, region_ms, wall, clock_info = warm_then_time()
+    hbm = None
+    if hbm_window_s > 0:
+        # 3. HBM traffic per launch from the memory controllers' activity, with
+        #    the launches back to back at the same steady clock
+        hbm = hbm_window(step, stream, hbm_window_s, deadline_s)
     cold = None
     if cold_bytes > 0:
-        # 3. context for `value`, which runs with warm caches: the same launches,
+        # 4. context for `value`, which runs with warm caches: the same launches,
         #    each after a fill of a cold_bytes buffer (outside its events) that
         #    evicts the operands from every L2 and the last-level cache
         scratch = torch.empty(cold_bytes // 4, dtype=torch.float32, device=dev)
@@ -432,7 +531,8 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
             "kernel_ms_min": round(float(per_launch_ms.min()), 5),
             "kernel_ms_median": round(float(np.median(per_launch_ms)), 5),
         },
-        "cache": cache_fields(facts),
+        "cache": cache_fields(facts, hbm),
+        "hbm": hbm,
         "counters": counter_fields(facts),
         "clock": clock_info,
         "settle": settle_info,
@@ -475,16 +575,22 @@ def bench_one(w: synth.Workload, steps: int, warmup: int, opts, sched_name: str,
     return res
 
 
-def cache_fields(facts: dict) -> dict:
-    """L2 / LLC hit rates from the committed counter run of this kernel source,
-    and the L2 term of the pages' Eq. 1 that the measured L2 hit rate implies.
-    The LLC term needs an LLC hit rate, which this ROCm does not expose."""
+def cache_fields(facts: dict, hbm: dict | None = None) -> dict:
+    """L2 / LLC hit rates and the two terms of the pages' Eq. 1 they imply.  The
+    L2 hit rate is from the committed counter run of this kernel source.  This
+    ROCm has no last-level-cache counter; the LLC hit rate is estimated by bytes
+    from this run's HBM traffic (hbm_window) against the bytes past the L2s in
+    the same counter run (llc_estimate), when both exist."""
     l2 = facts.get("l2_hit_pct")
-    out = {"l2_hit_pct": l2, "llc_hit_pct": facts.get("llc_hit_pct"),
-           "llc_note": facts.get("llc_note"), "source": facts.get("source")}
+    llc = llc_estimate((hbm or {}).get("bytes_per_launch"), facts.get("hbm_bytes_per_launch"))
+    out = {"l2_hit_pct": l2, "llc_hit_pct": llc,
+           "llc_note": ("estimated: 1 - HBM bytes per launch (memory-controller activity, this run) / "
+                        "bytes past the L2s per launch (FETCH_SIZE + WRITE_SIZE, %s)" % facts.get("source")
+                        if llc is not None else facts.get("llc_note")),
+           "source": facts.get("source")}
     out["eq1"] = {"l2_bw_tbs": EQ1_L2_BW_TBS, "llc_bw_tbs": EQ1_LLC_BW_TBS,
                   "l2_term_tbs": None if l2 is None else round(EQ1_L2_BW_TBS * l2 / 100.0, 2),
-                  "llc_term_tbs": None}
+                  "llc_term_tbs": None if llc is None else round(EQ1_LLC_BW_TBS * llc / 100.0, 2)}
     return out
 
 
@@ -700,6 +806,29 @@ def size_sweep(sizes, dtype: str, warmup: int, vendor: bool = False) -> None:
         torch.cuda.empty_cache()
 
 
+def hbm_calibrate(window_s: float, deadline_s: float) -> None:
+    """The memory controllers' activity (hbm_window) under device kernels whose
+    HBM traffic is known: a 1 GiB copy (reads and writes), a 4 GiB fill (writes)
+    and a 4 GiB sum (reads), each far larger than the last-level cache."""
+    import torch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    x = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    big = torch.ones(1 << 30, dtype=torch.float32, device=dev)
+    for name, fn, nbytes in (("copy 1 GiB", lambda: y.copy_(x), 2 << 30),
+                             ("fill 4 GiB", lambda: big.fill_(2.0), 4 << 30),
+                             ("sum 4 GiB", lambda: torch.sum(big), 4 << 30)):
+        r = hbm_window(fn, stream, window_s, deadline_s)
+        if r is None:
+            print(json.dumps({"calibration": name, "hbm": None, "note": "amdsmi unavailable"}), flush=True)
+            continue
+        known = nbytes / (r["ms_per_launch"] * 1e-3)
+        print(json.dumps({"calibration": name, "known_bytes_per_s": round(known),
+                          "activity_bytes_per_s": r["bytes_per_s"],
+                          "ratio": round(r["bytes_per_s"] / known, 4), "hbm": r}), flush=True)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -730,6 +859,12 @@ def main(argv=None) -> int:
     ap.add_argument("--cold-mib", type=int, default=1024,
                     help="after the timed region, time K more launches, each after writing a "
                          "buffer of this many MiB (cold caches; reported as cold_cache, 0 skips)")
+    ap.add_argument("--hbm-window", type=float, default=2.0,
+                    help="seconds of launches back to back over which the HBM controllers' activity "
+                         "is read (amdsmi), for the line's hbm and LLC estimate (0 skips)")
+    ap.add_argument("--hbm-calibrate", action="store_true",
+                    help="read the HBM controllers' activity under a copy, a fill and a sum of known "
+                         "byte counts and print one JSON line each")
     ap.add_argument("--shape", type=str, default=None, help="M,N,K (custom size)")
     ap.add_argument("--dtype", choices=["bf16", "fp8", "mxfp8"], default="bf16")
     ap.add_argument("--sweep", type=str, default=None, help='"W,C W,C ..." grid orders to time')
@@ -739,8 +874,8 @@ def main(argv=None) -> int:
                     help="with --sizes: also time the vendor library on the same inputs (context)")
     args = ap.parse_args(argv)
 
-    if args.cold_mib < 0:
-        print("--cold-mib must be at least 0", file=sys.stderr)
+    if args.cold_mib < 0 or args.hbm_window < 0:
+        print("--cold-mib and --hbm-window must be at least 0", file=sys.stderr)
         return 2
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be at least 1 and --warmup at least 0", file=sys.stderr)
@@ -775,6 +910,9 @@ def main(argv=None) -> int:
     if args.sizes:
         size_sweep(args.sizes.split(), args.dtype, args.warmup, args.vendor)
         return 0
+    if args.hbm_calibrate:
+        hbm_calibrate(args.hbm_window or 2.0, args.deadline)
+        return 0
     if args.clock_ramp:
         for i in ([2, 5] if args.all else [args.workload]):
             clock_ramp(synth.workload(i), args.clock_ramp, 2.0)
@@ -793,7 +931,8 @@ def main(argv=None) -> int:
         res = bench_one(w, steps, args.warmup, opts, args.schedule,
                         with_cpu=(not args.no_cpu_baseline), deadline_s=args.deadline,
                         settle_ms=args.settle_ms, tune=args.tune,
-                        pad_k=args.pad_k, cold_bytes=args.cold_mib << 20)
+                        pad_k=args.pad_k, cold_bytes=args.cold_mib << 20,
+                        hbm_window_s=args.hbm_window)
         print(json.dumps(res), flush=True)
     return 0
 

@@ -32,8 +32,9 @@ def test_step_counts_and_tune_combinations_are_refused(capsys):
                  ["--tune", "--schedule", "pingpong"]):
         assert bench.main(argv) == 2, argv
         assert "--tune" in capsys.readouterr().err
-    assert bench.main(["--cold-mib", "-1"]) == 2
-    assert "--cold-mib" in capsys.readouterr().err
+    for argv in (["--cold-mib", "-1"], ["--hbm-window", "-0.5"]):
+        assert bench.main(argv) == 2, argv
+        assert "--cold-mib and --hbm-window" in capsys.readouterr().err
 
 
 def test_clock_from_trace_decodes_a_known_record():
@@ -87,6 +88,30 @@ def test_eq1_l2_term():
     assert abs(c["eq1"]["l2_term_tbs"] - 0.8 * bench.EQ1_L2_BW_TBS) < 0.006
     assert c["eq1"]["llc_term_tbs"] is None
     assert bench.cache_fields({})["eq1"]["l2_term_tbs"] is None
+
+
+def test_hbm_traffic_from_activity_accumulators():
+    # 2 s of ticks (1 ms each) at 25 % memory and 100 % gfx activity of an
+    # 8192 GB/s part: 2.048e12 B/s; at 1000 launches per second, 2.048e9 B each
+    a = (1_000_000, 5_000_000, 40_000, 8192)
+    b = (a[0] + 25 * 2000, a[1] + 100 * 2000, a[2] + 2000, 8192)
+    r = bench.hbm_from_accumulators(a, b, 1000.0)
+    assert r["mem_activity_pct"] == 25.0 and r["gfx_activity_pct"] == 100.0
+    assert r["bytes_per_s"] == 2_048_000_000_000 and r["bytes_per_launch"] == 2_048_000_000
+    assert bench.hbm_from_accumulators(a, a, 1000.0) is None      # no refresh in between
+
+
+def test_llc_estimate_and_eq1_llc_term():
+    # 0.25 GB of HBM traffic per launch against 1.75 GB past the L2s: 6/7 served
+    # by the last-level cache
+    assert bench.llc_estimate(0.25e9, 1.75e9) == 85.7
+    assert bench.llc_estimate(None, 1.75e9) is None and bench.llc_estimate(0.25e9, None) is None
+    assert bench.llc_estimate(3e9, 1e9) == 0.0
+    c = bench.cache_fields({"l2_hit_pct": 80.0, "hbm_bytes_per_launch": 1.75e9, "source": "x"},
+                           {"bytes_per_launch": 0.25e9})
+    assert c["llc_hit_pct"] == 85.7 and c["llc_note"].startswith("estimated")
+    assert abs(c["eq1"]["llc_term_tbs"] - 0.857 * bench.EQ1_LLC_BW_TBS) < 0.006
+    assert bench.cache_fields({"l2_hit_pct": 80.0}, None)["llc_hit_pct"] is None
 
 
 def test_cpu_baseline_reports_parity_of_the_rows_it_computes():
