@@ -14,14 +14,19 @@ then after --settle-ms (200) of untimed steps back to back ("value").  An idle
 MI355X under its power cap takes ~50-100 ms of load before its clock settles
 (it starts near 1.5 GHz, dips, then rises to its steady clock), and a short
 timed region right after an idle gap measures that ramp, not the kernel.
-Then K more launches run with cold caches, each after a 1 GiB buffer fill
-outside its events ("cold_cache", context only).
+Then the launches run back to back for --hbm-window seconds while amdsmi's
+accumulator of the HBM controllers' activity gives the HBM bytes per launch
+("hbm"; with the committed L2 counters, the last-level cache's hit rate by
+bytes), and K more launches run with cold caches, each after a 1 GiB buffer
+fill outside its events ("cold_cache", context only).
 
   python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--workload 2]
-                  [--settle-ms 200] [--cold-mib 1024] [--all]
+                  [--settle-ms 200] [--hbm-window 2] [--cold-mib 1024] [--all]
                   [--remap W,C | --row-major | --tune]
                   [--schedule interleave|pingpong|lockstep|interleave128|interleave192]
                   [--no-cpu-baseline]
+  python bench.py --hbm-calibrate
+        the HBM activity reading against a copy, a fill and a sum of known bytes
   python bench.py --clock-ramp 800 [--workload N | --all]
         the clock after 2 s of idle, per window of launches (time record)
   python bench.py --sizes "1024 2048 ..." [--dtype bf16|fp8|mxfp8] [--vendor]
