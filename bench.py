@@ -615,8 +615,10 @@ def custom_workload(shape: str, dtype: str) -> synth.Workload:
     return synth.Workload("%s_%dx%dx%d" % (dtype, M, N, K), dtype, M, N, K, 7101, 7102)
 
 
-def sweep(w: synth.Workload, pairs, steps: int, warmup: int) -> None:
-    """Time each grid order (W, C) on the same inputs; one JSON line each."""
+def sweep(w: synth.Workload, pairs, steps: int, warmup: int, hbm_window_s: float = 0.0,
+          deadline_s: float = 120.0) -> None:
+    """Time each grid order (W, C) on the same inputs, and with hbm_window_s > 0
+    read its HBM bytes per launch (hbm_window); one JSON line each."""
     import torch
     import dense_gemm_fp8_amd as hkg
 
@@ -666,6 +668,8 @@ def sweep(w: synth.Workload, pairs, steps: int, warmup: int) -> None:
             e1.record(stream)
             torch.cuda.synchronize()
             times[key].append(e0.elapsed_time(e1) / steps)
+    hbm = {key: (hbm_window(lambda: run(*key[:2], 1, *key[2:]), stream, hbm_window_s, deadline_s)
+                 if hbm_window_s > 0 else None) for key in pairs}
     for key in pairs:
         W, Cc = key[:2]
         ms = float(np.mean(times[key]))
@@ -673,7 +677,7 @@ def sweep(w: synth.Workload, pairs, steps: int, warmup: int) -> None:
                           "W": W, "C": Cc, "schedule": key[2] if len(key) > 2 else "i",
                           "default": W == "default" or [W, Cc] == [dW, dC],
                           "ms": round(ms, 5), "ms_runs": [round(t, 5) for t in times[key]],
-                          "TFLOPS": round(w.flops / (ms * 1e-3) / 1e12, 2)}), flush=True)
+                          "TFLOPS": round(w.flops / (ms * 1e-3) / 1e12, 2), "hbm": hbm[key]}), flush=True)
 
 
 def clock_ramp(w: synth.Workload, launches: int, idle_s: float) -> None:
@@ -927,7 +931,7 @@ def main(argv=None) -> int:
         pairs = [("default", 0) if item == "default" else
                  tuple(int(v) if v.isdigit() else v for v in item.split(","))
                  for item in args.sweep.split()]
-        sweep(w, pairs, args.steps, args.warmup)
+        sweep(w, pairs, args.steps, args.warmup, args.hbm_window, args.deadline)
         return 0
     ids = [1, 2, 3, 4, 5] if args.all else [args.workload]
     for i in ids:
