@@ -41,8 +41,9 @@ def test_bench_line_fields_small_workload():
     assert line["config"]["workload"] == "bf16_256"
     r = line["roofline"]
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and 0 < r["frac"] < 1
+    # achieved is printed to 0.01 TFLOP/s and the mean launch time to 10 ns
     assert r["achieved"] == pytest.approx(synth.workload(1).flops / (r["kernel_ms_mean"] * 1e-3) / 1e12,
-                                          rel=1e-3)
+                                          rel=2e-3, abs=0.006)
     assert 50 < line["clock"]["mhz_mean"] < 3000
     assert line["cold_cache"]["kernel_ms_mean"] > 0
     assert line["cpu_baseline"]["kind"] == "oracle" and line["cpu_baseline"]["cores"] >= 1
