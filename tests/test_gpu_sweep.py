@@ -1,10 +1,11 @@
 """Seeded random sweep of every launch option against the oracle (needs a gfx950
 GPU): shapes with ragged edges, every schedule a dtype accepts, default /
 row-major / explicit grid orders, row pitches on A, B and C, A and B in one
-buffer, K = 0.  Operands are small integers (block scales powers of two), so
-the oracle's fp64 product is exact in fp32: C_f32 must equal it bit for bit,
-C must be its round-to-nearest-even bf16, and the bytes between C's rows must
-keep their canary."""
+buffer, K = 0.  With small-integer operands (block scales powers of two) the
+oracle's fp64 product is exact in fp32: C_f32 must equal it bit for bit, C
+must be its round-to-nearest-even bf16, and the bytes between C's rows must
+keep their canary.  With N(0,1) operands (quantised per tensor or per block
+for e4m3) every entry must meet the acceptance rule (i)-(iii)."""
 import sys
 
 import numpy as np
@@ -13,6 +14,8 @@ import pytest
 from dense_gemm_fp8_amd import synth
 from oracle import dense
 from oracle.parity import f32_to_bf16_rne
+
+from _parity import check
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -127,3 +130,54 @@ def test_random_launch_options_exact(dt):
         np.testing.assert_array_equal(got, f32_to_bf16_rne(w32))
         if pc:
             assert torch.all(bigC[:, N:] == canary) and torch.all(bigF[:, N:] == canary)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8", "mxfp8"])
+def test_random_launch_options_normal_inputs(dt):
+    rng = np.random.default_rng({"bf16": 8201, "fp8": 8202, "mxfp8": 8203}[dt])
+    for i in range(20):
+        M, N, K, o, pa, pb, pc, alias, s = _case(rng, dt)
+        M, N, K = min(M, 1500), (M if alias else min(N, 1500)), max(K_ALIGN[dt], min(K, 1024))
+        _say("sweep N(0,1) %s %d: %dx%dx%d opts %s pads %d/%d/%d alias %s" % (
+            dt, i, M, N, K, o, pa, pb, pc, alias))
+        opts = hkg.make_opts(**o)
+        x = synth.normal_f32(s, M, K)
+        y = x if alias else synth.normal_f32(s + 1, N, K)
+        if dt == "bf16":
+            A, B = synth.f32_to_bf16_bits(x), synth.f32_to_bf16_bits(y)
+            ref = dense.gemm_bf16(A, B)
+            dA = torch.from_numpy(A.view(np.int16)).view(torch.bfloat16).cuda()
+            dB = None if alias else torch.from_numpy(B.view(np.int16)).view(torch.bfloat16).cuda()
+            fill = float("nan")
+        elif dt == "fp8":
+            (A, sa), (B, sb) = synth.e4m3_quantize(x), synth.e4m3_quantize(y)
+            sa, sb = float(sa), float(sb)
+            ref = dense.gemm_fp8(A, B, sa, sb)
+            dA = torch.from_numpy(A).cuda()
+            dB = None if alias else torch.from_numpy(B).cuda()
+            fill = 0x7F
+        else:
+            (A, SA), (B, SB) = synth.mx_quantize(x), synth.mx_quantize(y)
+            ref = dense.gemm_mxfp8(A, B, SA, SB)
+            dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+            pA = hkg.mx_pack_scales(torch.from_numpy(SA).cuda(), hkg.HKG_MX_OPERAND_A)
+            pB = hkg.mx_pack_scales(torch.from_numpy(SB).cuda(), hkg.HKG_MX_OPERAND_B)
+            fill = 0x7F
+        if pa:
+            dA = _pitched(dA, K + pa, fill)
+        if alias:
+            dB = dA
+        elif pb:
+            dB = _pitched(dB, K + pb, fill)
+        C = torch.empty((M, N + pc), dtype=torch.bfloat16, device="cuda")[:, :N]
+        F = torch.empty((M, N + pc), dtype=torch.float32, device="cuda")[:, :N]
+        if dt == "bf16":
+            hkg.gemm_bf16(dA, dB, C, F, opts=opts)
+        elif dt == "fp8":
+            hkg.gemm_fp8(dA, dB, sa, sb, C, F, opts=opts)
+        else:
+            hkg.gemm_mxfp8(dA, dB, pA, pB, C, F, opts=opts)
+        torch.cuda.synchronize()
+        check(ref, F.contiguous().cpu().numpy(),
+              C.contiguous().view(torch.int16).cpu().numpy().view(np.uint16), K,
+              "%s case %d" % (dt, i))
