@@ -34,7 +34,7 @@ fill outside its events ("cold_cache", context only).
         size, one JSON line each
   python bench.py --sweep "default 1,1 8,32 5,25 8,32,i192 ..." [--workload N | --shape M,N,K --dtype bf16|fp8]
         grid-order sweep: one JSON line per (W, C) on the same resident inputs ("default" = the
-        library's default launch, split included)
+        library's default launch, split included), with its HBM bytes per launch (--hbm-window)
         ("1,1" is row-major order; a third field picks the kernel: i = 4-wave on
         256x256 tiles (default), i128 / i192 = on 128x128 / 192x192 tiles, p =
         ping-pong, l = lockstep); used to choose the library's default (W, C)
