@@ -193,11 +193,13 @@ def metrics_reader():
         keys = ("mem_activity_acc", "gfx_activity_acc", "accumulation_counter", "vram_max_bandwidth")
 
         def read():
-            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
-            return tuple(m[k] for k in keys)
-        if not all(isinstance(v, int) for v in read()):
-            return None
-        return read
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                v = tuple(m[k] for k in keys)
+            except Exception:  # pragma: no cover - a failed query mid-run
+                return None
+            return v if all(isinstance(x, int) for x in v) else None
+        return read if read() is not None else None
     except Exception:  # pragma: no cover - no amdsmi / no device
         return None
 
@@ -243,6 +245,8 @@ def hbm_window(step, stream, window_s: float, deadline_s: float, read=None) -> d
         if now < 1.1:
             continue
         cur = read()
+        if cur is None:
+            break
         if first is None:
             first = cur
         elif a is None:
