@@ -139,10 +139,16 @@ def wait_event(ev, deadline_s: float, what: str) -> None:
 
 
 def gpu_identity() -> dict:
-    """Which box and GPU a line was measured on: host name, and the GPU's serial
-    number and power cap as amdsmi reports them (null where unavailable)."""
+    """Which box and GPU a line was measured on: host name, the device's
+    architecture and compute-unit count, the HIP runtime version, and the GPU's
+    serial number and power cap as amdsmi reports them (null where
+    unavailable)."""
     import socket
-    out = {"host": socket.gethostname(), "gpu_serial": None, "power_cap_w": None}
+    import torch
+    prop = torch.cuda.get_device_properties(0)
+    out = {"host": socket.gethostname(), "arch": getattr(prop, "gcnArchName", None),
+           "compute_units": prop.multi_processor_count, "hip_version": torch.version.hip,
+           "gpu_serial": None, "power_cap_w": None}
     try:
         import amdsmi
         amdsmi.amdsmi_init()

@@ -45,6 +45,7 @@ def test_bench_line_fields_small_workload():
     assert r["achieved"] == pytest.approx(synth.workload(1).flops / (r["kernel_ms_mean"] * 1e-3) / 1e12,
                                           rel=2e-3, abs=0.006)
     assert 50 < line["clock"]["mhz_mean"] < 3000
+    assert line["box"]["arch"].startswith("gfx950") and line["box"]["compute_units"] == 256
     assert line["cold_cache"]["kernel_ms_mean"] > 0
     assert line["cpu_baseline"]["kind"] == "oracle" and line["cpu_baseline"]["cores"] >= 1
     assert line["parity"]["pass"] and line["parity"]["checked"] > 0
